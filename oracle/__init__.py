@@ -1,0 +1,220 @@
+"""CPU oracle of the batch-invariant LM head (float64 / exact int64).
+
+TEST INFRASTRUCTURE, NOT PRODUCT.  Only ``tests/``, ``__graft_entry__.smoke()``
+and ``bench.py``'s cpu_baseline leg may import this package.  The HIP library
+(``invariant_lm_head_amd``) never imports it, and the two share no code; only
+the seeded input generators in ``synth`` feed both.
+
+The arithmetic lives in ``oracle.c`` (plain loops, one sequential float64 or
+int64 accumulator per logit); this module compiles it with gcc (no FMA
+contraction, no fast-math, no vectorisation) and wraps it with ctypes.  The
+sources of each definition are cited in ``oracle.c``.
+
+``Oracle(path)`` loads any build of the source (the tests load copies with a
+planted mistake to show that the pins catch it); the module-level functions
+use the default build ``liblmhead_oracle.so``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_DIR = Path(__file__).resolve().parent
+SOURCE = _DIR / "oracle.c"
+LIBRARY = _DIR / "liblmhead_oracle.so"
+
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+          "-ffp-contract=off", "-fno-fast-math", "-fno-tree-vectorize"]
+
+
+def compile_source(src: Path, out: Path) -> Path:
+    tmp = out.with_name(out.name + ".tmp%d" % os.getpid())
+    subprocess.run(["gcc", *CFLAGS, str(src), "-o", str(tmp), "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> Path:
+    """Compile oracle.c into liblmhead_oracle.so (always when force)."""
+    global _default
+    if force or not LIBRARY.exists() or LIBRARY.stat().st_mtime < SOURCE.stat().st_mtime:
+        compile_source(SOURCE, LIBRARY)
+        _default = None
+    return LIBRARY
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _shape(x, w):
+    B, H = x.shape
+    V, H2 = w.shape
+    assert H == H2, "hidden width of x and w differ"
+    return B, H, V
+
+
+class Oracle:
+    """ctypes wrapper of one build of oracle.c."""
+
+    def __init__(self, path: Path):
+        lib = ctypes.CDLL(str(path))
+        i64, i32, P, D = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_double
+        sig = {
+            "oracle_logits_bf16": ([P, P, i64, i64, i64, P, i32], ctypes.c_int),
+            "oracle_logits_i8": ([P, P, i64, i64, i64, P, i32], ctypes.c_int),
+            "oracle_greedy_bf16": ([P, P, i64, i64, i64, i32, P, P, P, i32], ctypes.c_int),
+            "oracle_greedy_i8": ([P, P, i64, i64, i64, P, P, P, P, P, i32], ctypes.c_int),
+            "oracle_logprob_bf16": ([P, P, i64, i64, i64, P, P, i32], ctypes.c_int),
+            "oracle_logprob_i8": ([P, P, i64, i64, i64, P, P, P, i32], ctypes.c_int),
+            "oracle_top2_f64": ([P, i64, P, P], None),
+            "oracle_top2_i64": ([P, i64, P, P], None),
+            "oracle_logsoftmax_f64": ([P, i64, P], None),
+            "oracle_logprob_i64_row": ([P, i64, D, i64], D),
+            "oracle_round_bf16": ([D], D),
+            "oracle_threads": ([i32], ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes, fn.restype = args, res
+        self.lib = lib
+
+    def threads(self, n: int = 0) -> int:
+        """Worker threads used for n (0 = all online CPUs)."""
+        return self.lib.oracle_threads(n)
+
+    # -------------------------------------------------------- logits
+    def logits_bf16(self, x, w, nthreads: int = 0) -> np.ndarray:
+        """z[r, v] = sum_k x[r, k] * w[v, k] in float64, k ascending (bf16 bits in)."""
+        x, w = _c(x, np.uint16), _c(w, np.uint16)
+        B, H, V = _shape(x, w)
+        z = np.empty((B, V), np.float64)
+        assert self.lib.oracle_logits_bf16(_ptr(x), _ptr(w), B, H, V, _ptr(z), nthreads) == 0
+        return z
+
+    def logits_i8(self, x, w, nthreads: int = 0) -> np.ndarray:
+        """z[r, v] = sum_k x[r, k] * w[v, k] exactly in int64."""
+        x, w = _c(x, np.int8), _c(w, np.int8)
+        B, H, V = _shape(x, w)
+        z = np.empty((B, V), np.int64)
+        assert self.lib.oracle_logits_i8(_ptr(x), _ptr(w), B, H, V, _ptr(z), nthreads) == 0
+        return z
+
+    # -------------------------------------------------------- greedy
+    def greedy_bf16(self, x, w, round_bf16: bool = False, nthreads: int = 0):
+        """Top-2 ids, values and margin of each row's float64 logits.
+
+        Ties go to the lowest id.  With ``round_bf16`` the logits are first
+        rounded to bf16 (nearest-even): the ordinary 16-bit head's output.
+        Returns (ids[B,2] int32, vals[B,2] float64, margin[B] float64).
+        """
+        x, w = _c(x, np.uint16), _c(w, np.uint16)
+        B, H, V = _shape(x, w)
+        ids = np.empty((B, 2), np.int32)
+        vals = np.empty((B, 2), np.float64)
+        margin = np.empty(B, np.float64)
+        rc = self.lib.oracle_greedy_bf16(_ptr(x), _ptr(w), B, H, V, int(round_bf16),
+                                         _ptr(ids), _ptr(vals), _ptr(margin), nthreads)
+        assert rc == 0
+        return ids, vals, margin
+
+    def greedy_i8(self, x, w, scale=None, nthreads: int = 0):
+        """Top-2 on exact int64 logits, then the per-row scale.
+
+        Returns (ids[B,2] int32, raw[B,2] int64, vals[B,2] float32, margin[B]
+        float32) with vals = float32(raw * scale), margin = float32((raw1 -
+        raw2) * scale): one rounding of an exact float64 product each (NaN
+        when the scale is not a positive finite number).
+        """
+        x, w = _c(x, np.int8), _c(w, np.int8)
+        B, H, V = _shape(x, w)
+        s = None if scale is None else _c(scale, np.float32)
+        ids = np.empty((B, 2), np.int32)
+        raw = np.empty((B, 2), np.int64)
+        vals = np.empty((B, 2), np.float32)
+        margin = np.empty(B, np.float32)
+        rc = self.lib.oracle_greedy_i8(_ptr(x), _ptr(w), B, H, V,
+                                       None if s is None else _ptr(s),
+                                       _ptr(ids), _ptr(raw), _ptr(vals), _ptr(margin), nthreads)
+        assert rc == 0
+        return ids, raw, vals, margin
+
+    # ------------------------------------------------------ log-prob
+    def logprob_bf16(self, x, w, target, nthreads: int = 0) -> np.ndarray:
+        """log p(target[r]) under softmax of row r's float64 logits (NaN if out of range)."""
+        x, w = _c(x, np.uint16), _c(w, np.uint16)
+        B, H, V = _shape(x, w)
+        t = _c(target, np.int32)
+        out = np.empty(B, np.float64)
+        assert self.lib.oracle_logprob_bf16(_ptr(x), _ptr(w), B, H, V, _ptr(t), _ptr(out),
+                                            nthreads) == 0
+        return out
+
+    def logprob_i8(self, x, w, target, scale=None, nthreads: int = 0) -> np.ndarray:
+        """log p(target[r]) under softmax of scale[r] * z (exact int differences)."""
+        x, w = _c(x, np.int8), _c(w, np.int8)
+        B, H, V = _shape(x, w)
+        t = _c(target, np.int32)
+        s = None if scale is None else _c(scale, np.float32)
+        out = np.empty(B, np.float64)
+        assert self.lib.oracle_logprob_i8(_ptr(x), _ptr(w), B, H, V,
+                                          None if s is None else _ptr(s), _ptr(t), _ptr(out),
+                                          nthreads) == 0
+        return out
+
+    # ------------------------------------------- per-row definitions
+    def top2_f64(self, z):
+        """(ids[2], vals[2]) of one float64 logit row; ties to the lowest id."""
+        z = _c(z, np.float64)
+        ids = np.empty(2, np.int32)
+        vals = np.empty(2, np.float64)
+        self.lib.oracle_top2_f64(_ptr(z), z.size, _ptr(ids), _ptr(vals))
+        return ids, vals
+
+    def top2_i64(self, z):
+        z = _c(z, np.int64)
+        ids = np.empty(2, np.int32)
+        vals = np.empty(2, np.int64)
+        self.lib.oracle_top2_i64(_ptr(z), z.size, _ptr(ids), _ptr(vals))
+        return ids, vals
+
+    def logsoftmax_f64(self, z) -> np.ndarray:
+        """Full log-softmax vector of one float64 logit row."""
+        z = _c(z, np.float64)
+        out = np.empty_like(z)
+        self.lib.oracle_logsoftmax_f64(_ptr(z), z.size, _ptr(out))
+        return out
+
+    def logprob_i64_row(self, z, scale: float, t: int) -> float:
+        z = _c(z, np.int64)
+        return self.lib.oracle_logprob_i64_row(_ptr(z), z.size, float(scale), int(t))
+
+    def round_bf16(self, v: float) -> float:
+        """Nearest bf16 value (ties to even) of a float64, as float64."""
+        return self.lib.oracle_round_bf16(float(v))
+
+
+_default: Oracle | None = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        build(force=False)
+        _default = Oracle(LIBRARY)
+    return _default
+
+
+def __getattr__(name):
+    # module-level access to the default build: oracle.logits_bf16(...), ...
+    if not name.startswith("_") and hasattr(Oracle, name):
+        return getattr(default(), name)
+    raise AttributeError(name)

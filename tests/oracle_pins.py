@@ -1,0 +1,449 @@
+"""Pins of the CPU oracle against what mathematics and the pages fix.
+
+Every pin takes an ``oracle.Oracle`` and raises AssertionError when it
+disagrees.  None of them re-types the oracle's formula or re-calls its code:
+they compare with exact rational arithmetic (``fractions``), 50-digit
+``decimal`` arithmetic, an independent BLAS (numpy float64 / int64 matmul),
+brute-force sorting, closed forms and invariants.  ``FAST`` pins also run
+against copies of the oracle with a planted mistake (test_oracle_mutants.py).
+"""
+from __future__ import annotations
+
+import json
+import math
+from decimal import Decimal, getcontext
+from fractions import Fraction
+from pathlib import Path
+
+import numpy as np
+
+import synth
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+# ------------------------------------------------------------- helpers
+def rand_bf16(rng, shape, emin=-8, emax=3):
+    """Random bf16 bit patterns: random sign, exponent in [emin, emax], mantissa."""
+    sign = rng.integers(0, 2, shape).astype(np.uint32) << 15
+    expo = rng.integers(127 + emin, 127 + emax + 1, shape).astype(np.uint32) << 7
+    mant = rng.integers(0, 128, shape).astype(np.uint32)
+    return (sign | expo | mant).astype(np.uint16)
+
+
+def bf16_const(v: float, shape):
+    return np.full(shape, synth.bf16_from_f32(np.float32(v)).item(), dtype=np.uint16)
+
+
+def fracs(a):
+    return [[Fraction(float(v)) for v in row] for row in a]
+
+
+def dec(fr: Fraction) -> Decimal:
+    return Decimal(fr.numerator) / Decimal(fr.denominator)
+
+
+def float32_rne(fr: Fraction) -> float:
+    """Nearest float32 (ties to even) of an exact rational (normal range)."""
+    if fr == 0:
+        return 0.0
+    sgn = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = math.floor(math.log2(a))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = a / Fraction(2) ** (e - 23)          # in [2^23, 2^24)
+    n = math.floor(q)
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sgn * float(Fraction(n) * Fraction(2) ** (e - 23))
+
+
+# ------------------------------------------------------------ logits
+def pin_logits_bruteforce(o):
+    """Float64 logits equal the exact rational dot products within the
+    sequential-summation bound H * 2^-52 * sum|terms|."""
+    rng = np.random.default_rng(11)
+    for _ in range(40):
+        B, H, V = int(rng.integers(1, 5)), int(rng.integers(1, 9)), int(rng.integers(2, 17))
+        x, w = rand_bf16(rng, (B, H)), rand_bf16(rng, (V, H))
+        z = o.logits_bf16(x, w)
+        xf, wf = fracs(synth.bf16_to_f64(x)), fracs(synth.bf16_to_f64(w))
+        for r in range(B):
+            for v in range(V):
+                terms = [xf[r][k] * wf[v][k] for k in range(H)]
+                exact = sum(terms)
+                bound = Fraction(H) * Fraction(2) ** -52 * sum(abs(t) for t in terms)
+                assert abs(Fraction(float(z[r, v])) - exact) <= bound, (r, v)
+
+
+def pin_logits_one_hot(o):
+    """x = e_k picks column k of W: z[k, v] == W[v, k] exactly (V != H, so a
+    transposed or mis-strided operand cannot pass)."""
+    rng = np.random.default_rng(12)
+    H, V = 24, 37
+    x = np.zeros((H, H), np.uint16)
+    x[np.arange(H), np.arange(H)] = bf16_const(1.0, ()).item()
+    w = rand_bf16(rng, (V, H))
+    z = o.logits_bf16(x, w)
+    assert np.array_equal(z, synth.bf16_to_f64(w).T)
+    xi = np.eye(H, dtype=np.int8)
+    wi = rng.integers(-128, 128, (V, H)).astype(np.int8)
+    assert np.array_equal(o.logits_i8(xi, wi), wi.astype(np.int64).T)
+
+
+def pin_logits_closed_forms(o):
+    """W = 0 gives z = 0; constant rows give z = H * c * d exactly."""
+    H, V = 64, 9
+    rng = np.random.default_rng(13)
+    x = rand_bf16(rng, (3, H))
+    assert np.all(o.logits_bf16(x, np.zeros((V, H), np.uint16)) == 0.0)
+    c, ds = 0.375, [-1.25, 0.5, 3.0, -0.0078125, 2.0, 1.5, -6.0, 0.25, 1.0]
+    xc = bf16_const(c, (2, H))
+    wd = np.stack([bf16_const(d, (H,)) for d in ds])
+    z = o.logits_bf16(xc, wd)
+    assert np.array_equal(z[0], np.array([H * c * d for d in ds]))
+    xi = np.full((2, H), -7, np.int8)
+    wi = np.stack([np.full(H, d, np.int8) for d in (5, -128, 127, 0)])
+    assert np.array_equal(o.logits_i8(xi, wi)[1], np.array([H * -7 * d for d in (5, -128, 127, 0)]))
+
+
+def pin_int_logits_bruteforce(o):
+    """int8 logits equal Python's arbitrary-precision integer dot products."""
+    rng = np.random.default_rng(14)
+    for _ in range(20):
+        B, H, V = int(rng.integers(1, 5)), int(rng.integers(1, 40)), int(rng.integers(2, 17))
+        x = rng.integers(-128, 128, (B, H)).astype(np.int8)
+        w = rng.integers(-128, 128, (V, H)).astype(np.int8)
+        z = o.logits_i8(x, w)
+        for r in range(B):
+            for v in range(V):
+                assert int(z[r, v]) == sum(int(x[r, k]) * int(w[v, k]) for k in range(H))
+
+
+def pin_int_overflow_bound(o):
+    """An all-127 row against an all-127 W row at H = 4096 hits the stated bound
+    4096 * 127^2 = 66,064,384 < 2^31 exactly; -128 squared at H = 131,071 stays
+    below 2^31 too."""
+    x = np.full((1, 4096), 127, np.int8)
+    w = np.stack([np.full(4096, 127, np.int8), np.full(4096, -127, np.int8)])
+    assert o.logits_i8(x, w).tolist() == [[66064384, -66064384]]
+    H = 131071
+    z = o.logits_i8(np.full((1, H), -128, np.int8), np.full((1, H), -128, np.int8))
+    assert int(z[0, 0]) == H * 128 * 128 < 2 ** 31
+
+
+def pin_logits_vs_blas(o):
+    """float64 logits agree with an independent BLAS (numpy float64 matmul)
+    within 1e-9 on the tiny workload and eight rows of the 2048 x 32000 head."""
+    d = synth.make_inputs("tiny")
+    ref = synth.bf16_to_f64(d["x"]) @ synth.bf16_to_f64(d["w"]).T
+    assert np.max(np.abs(o.logits_bf16(d["x"], d["w"]) - ref)) <= 1e-9
+    d = synth.make_inputs("tinyllama", rows=8)
+    ref = synth.bf16_to_f64(d["x"]) @ synth.bf16_to_f64(d["w"]).T
+    assert np.max(np.abs(o.logits_bf16(d["x"], d["w"]) - ref)) <= 1e-9
+
+
+def pin_int_logits_vs_numpy(o):
+    """int8-workload rows: int64 logits equal numpy's exact int64 matmul on a
+    slice of 8,192 vocabulary rows."""
+    d = synth.make_inputs("int8", rows=4)
+    w = d["w"][-8192:]
+    ref = d["x"].astype(np.int64) @ w.astype(np.int64).T
+    assert np.array_equal(o.logits_i8(d["x"], w), ref)
+
+
+# ------------------------------------------------------------- greedy
+def _brute_top2(z):
+    order = sorted(range(len(z)), key=lambda v: (-z[v], v))
+    return order[:2]
+
+
+def pin_top2_bruteforce(o):
+    """Top-2 ids equal brute-force sorting by (value desc, id asc), with many
+    exact ties (values from a small set)."""
+    rng = np.random.default_rng(21)
+    for _ in range(300):
+        V = int(rng.integers(2, 13))
+        zi = rng.integers(-3, 4, V)
+        ids, vals = o.top2_f64(zi.astype(np.float64))
+        assert list(ids) == _brute_top2(list(zi)), zi
+        assert list(vals) == [float(zi[i]) for i in _brute_top2(list(zi))]
+        ids, vals = o.top2_i64(zi.astype(np.int64))
+        assert list(ids) == _brute_top2(list(zi)), zi
+
+
+def pin_top2_hand_ties(o):
+    """The maximum at ids 5, 2 and 9: top-1 = 2 and top-2 = 5, margin 0
+    (lowest-id tie rule)."""
+    z = np.zeros(12)
+    z[[5, 2, 9]] = 4.0
+    z[7] = 3.9
+    ids, vals = o.top2_f64(z)
+    assert list(ids) == [2, 5] and vals[0] - vals[1] == 0.0
+    ids, _ = o.top2_i64(z.astype(np.int64) * 0 + np.where(z == 4.0, 7, 1))
+    assert list(ids) == [2, 5]
+
+
+def pin_greedy_identical_rows(o):
+    """Two identical dominant W rows (ids 3 and 7) tie exactly: top-1 = 3,
+    top-2 = 7, margin 0, whatever their order in memory."""
+    rng = np.random.default_rng(22)
+    H, V = 64, 16
+    x = rand_bf16(rng, (2, H), emin=-2, emax=1)
+    w = rand_bf16(rng, (V, H), emin=-12, emax=-9)
+    w[3] = w[7] = synth.bf16_from_f32(synth.bf16_to_f32(x[0]) * np.float32(0.5))
+    ids, vals, margin = o.greedy_bf16(x[:1], w)
+    assert list(ids[0]) == [3, 7] and margin[0] == 0.0
+    xi = rng.integers(-127, 128, (1, H)).astype(np.int8)
+    wi = rng.integers(-3, 4, (V, H)).astype(np.int8)
+    wi[3] = wi[7] = xi[0]
+    ids, raw, vals, margin = o.greedy_i8(xi, wi)
+    assert list(ids[0]) == [3, 7] and raw[0, 0] == raw[0, 1] and margin[0] == 0.0
+
+
+def pin_greedy_permutation(o):
+    """Permuting W's rows permutes the chosen ids (tie-free data)."""
+    d = synth.make_inputs("tiny")
+    rng = np.random.default_rng(23)
+    perm = rng.permutation(d["V"])
+    ids, vals, _ = o.greedy_bf16(d["x"], d["w"])
+    ids_p, vals_p, _ = o.greedy_bf16(d["x"], d["w"][perm])
+    assert np.array_equal(perm[ids_p], ids) and np.array_equal(vals, vals_p)
+
+
+def pin_greedy_near_ties(o):
+    """Hand-built gaps from exact bf16 edits: 0, one float64 ulp of 6.0, 2^-17,
+    2^-14 (< 1e-4), 2^-13 (> 1e-4) and one bf16 ulp of 6.0 (1/32).  Rows a (id
+    9) and b (id 4) share the logit 6.0; a's last coordinate adds the gap.  The
+    float64 head resolves every gap exactly (winner 9, margin == gap; tie ->
+    id 4); the bf16-output head ties every gap below half a bf16 ulp."""
+    H, V = 64, 12
+    gaps = [0.0, 2.0 ** -50, 2.0 ** -17, 2.0 ** -14, 2.0 ** -13, 2.0 ** -5]
+    rng = np.random.default_rng(24)
+    for g in gaps:
+        x = bf16_const(1.0, (1, H))
+        w = rand_bf16(rng, (V, H), emin=-14, emax=-12)
+        w[4] = w[9] = 0
+        w[4, 0] = w[9, 0] = bf16_const(6.0, ()).item()
+        w[9, H - 1] = synth.bf16_from_f32(np.float32(g)).item()
+        assert float(synth.bf16_to_f64(w[9, H - 1:])[0]) == g
+        ids, vals, margin = o.greedy_bf16(x, w)
+        if g == 0.0:
+            assert list(ids[0]) == [4, 9] and margin[0] == 0.0
+        else:
+            assert list(ids[0]) == [9, 4] and margin[0] == g
+        exempt = margin[0] < 1e-4                 # the 1e-4 argmax exemption rule
+        assert exempt == (g < 1e-4)
+        ids16, vals16, margin16 = o.greedy_bf16(x, w, round_bf16=True)
+        if g < 2.0 ** -6:
+            assert list(ids16[0]) == [4, 9] and margin16[0] == 0.0 and vals16[0, 0] == 6.0
+        else:
+            assert list(ids16[0]) == [9, 4] and margin16[0] == g
+
+
+def pin_int_scaled_values(o):
+    """int8 top-2 values and margin are the nearest float32 of the exact
+    rational raw * scale; a non-positive scale gives NaN values but valid ids."""
+    d = synth.make_inputs("int8", rows=6, with_weights=False)
+    rng = np.random.default_rng(25)
+    w = rng.integers(-127, 128, (257, d["H"])).astype(np.int8)
+    scale = d["scale"].copy()
+    scale[5] = -1.0
+    ids, raw, vals, margin = o.greedy_i8(d["x"], w, scale)
+    z = d["x"].astype(np.int64) @ w.astype(np.int64).T
+    for r in range(6):
+        assert list(ids[r]) == _brute_top2(list(z[r]))
+        assert list(raw[r]) == [int(z[r, i]) for i in ids[r]]
+        if r == 5:
+            assert np.isnan(vals[r]).all() and np.isnan(margin[r])
+            continue
+        s = Fraction(float(scale[r]))
+        assert [float(v) for v in vals[r]] == [float32_rne(int(q) * s) for q in raw[r]]
+        assert float(margin[r]) == float32_rne(int(raw[r, 0] - raw[r, 1]) * s)
+    # logits above 2^24 (not float32-representable): the scaled value must still
+    # be one rounding of the exact product
+    H = d["H"]
+    xb = np.full((1, H), 127, np.int8)
+    for r in range(48):
+        wb = rng.integers(100, 128, (2, H)).astype(np.int8)
+        sb = np.array([2.0 ** -18 * rng.uniform(0.5, 2.0)], np.float32)
+        ids, raw, vals, margin = o.greedy_i8(xb, wb, sb)
+        s = Fraction(float(sb[0]))
+        assert raw[0, 0] > 2 ** 24
+        assert [float(v) for v in vals[0]] == [float32_rne(int(q) * s) for q in raw[0]]
+
+
+# ----------------------------------------------------------- log-prob
+def pin_logsoftmax_sums_to_one(o):
+    """sum_v exp(log p_v) = 1 within 1e-6 (logsumexp identity), and the
+    per-target log-prob is that vector's entry."""
+    d = synth.make_inputs("tiny")
+    z = o.logits_bf16(d["x"], d["w"])
+    lp = o.logprob_bf16(d["x"], d["w"], d["target"])
+    for r in range(d["B"]):
+        lsm = o.logsoftmax_f64(z[r])
+        assert abs(math.fsum(np.exp(lsm).tolist()) - 1.0) <= 1e-6
+        assert abs(lsm[d["target"][r]] - lp[r]) <= 1e-12
+    rng = np.random.default_rng(31)
+    zz = rng.normal(0, 20, 5000)
+    assert abs(math.fsum(np.exp(o.logsoftmax_f64(zz)).tolist()) - 1.0) <= 1e-6
+
+
+def pin_logprob_closed_forms(o):
+    """W = 0: log p = -ln V for every target.  V = 2: log p_0 = -log1p(exp(z1 - z0))."""
+    rng = np.random.default_rng(32)
+    H, V = 64, 50
+    x = rand_bf16(rng, (3, H))
+    lp = o.logprob_bf16(x, np.zeros((V, H), np.uint16), np.array([0, 17, 49], np.int32))
+    assert np.allclose(lp, -math.log(V), rtol=0, atol=1e-14)
+    x = rand_bf16(rng, (4, H), emin=-3, emax=0)
+    w = rand_bf16(rng, (2, H), emin=-3, emax=0)
+    xf, wf = fracs(synth.bf16_to_f64(x)), fracs(synth.bf16_to_f64(w))
+    for t in (0, 1):
+        lp = o.logprob_bf16(x, w, np.full(4, t, np.int32))
+        for r in range(4):
+            z = [float(sum(a * b for a, b in zip(xf[r], wf[v]))) for v in (0, 1)]
+            assert abs(lp[r] + math.log1p(math.exp(z[1 - t] - z[t]))) <= 1e-12
+
+
+def pin_logprob_shift_invariance(o):
+    """Appending a coordinate x_H = 1 with W[:, H] = c adds c to every logit
+    and leaves every log-prob unchanged (1e-12); in int8 mode exactly."""
+    d = synth.make_inputs("tiny")
+    x2 = np.concatenate([d["x"], bf16_const(1.0, (d["B"], 1))], axis=1)
+    w2 = np.concatenate([d["w"], bf16_const(3.5, (d["V"], 1))], axis=1)
+    a = o.logprob_bf16(d["x"], d["w"], d["target"])
+    b = o.logprob_bf16(x2, w2, d["target"])
+    assert np.max(np.abs(a - b)) <= 1e-12
+    rng = np.random.default_rng(33)
+    x = rng.integers(-127, 128, (3, 64)).astype(np.int8)
+    w = rng.integers(-127, 128, (300, 64)).astype(np.int8)
+    t = np.array([0, 150, 299], np.int32)
+    s = np.full(3, 2.0 ** -12, np.float32)
+    a = o.logprob_i8(x, w, t, s)
+    b = o.logprob_i8(np.concatenate([x, np.ones((3, 1), np.int8)], 1),
+                     np.concatenate([w, np.full((300, 1), 99, np.int8)], 1), t, s)
+    assert np.array_equal(a, b)
+
+
+def pin_logprob_decimal(o):
+    """50-digit decimal log-softmax of the exact rational logits agrees within
+    1e-12 (bf16 mode) and for the scaled int8 logits."""
+    getcontext().prec = 50
+    rng = np.random.default_rng(34)
+    H, V = 16, 23
+    x = rand_bf16(rng, (3, H), emin=-2, emax=1)
+    w = rand_bf16(rng, (V, H), emin=-3, emax=0)
+    t = np.array([0, 11, 22], np.int32)
+    lp = o.logprob_bf16(x, w, t)
+    xf, wf = fracs(synth.bf16_to_f64(x)), fracs(synth.bf16_to_f64(w))
+    for r in range(3):
+        z = [dec(sum(a * b for a, b in zip(xf[r], wf[v]))) for v in range(V)]
+        ref = z[t[r]] - sum(zv.exp() for zv in z).ln()
+        assert abs(Decimal(float(lp[r])) - ref) <= Decimal("1e-12")
+    xi = rng.integers(-127, 128, (3, 64)).astype(np.int8)
+    wi = rng.integers(-127, 128, (40, 64)).astype(np.int8)
+    s = np.array([2.0 ** -10, 3.0e-4, 1.0e-3], np.float32)
+    lp = o.logprob_i8(xi, wi, t % 40, s)
+    for r in range(3):
+        zr = [sum(int(a) * int(b) for a, b in zip(xi[r], wi[v])) for v in range(40)]
+        sr = dec(Fraction(float(s[r])))
+        y = [sr * zv for zv in zr]
+        ref = y[t[r] % 40] - sum(yv.exp() for yv in y).ln()
+        assert abs(Decimal(float(lp[r])) - ref) <= Decimal("1e-12")
+
+
+def pin_logprob_out_of_range(o):
+    """A target outside [0, V) gives NaN (and only for that row)."""
+    d = synth.make_inputs("tiny")
+    t = np.array([-1, 3, d["V"], 999], np.int32)
+    lp = o.logprob_bf16(d["x"], d["w"], t)
+    assert np.isnan(lp[0]) and np.isnan(lp[2]) and np.isfinite(lp[1]) and np.isfinite(lp[3])
+    xi = np.ones((2, 64), np.int8)
+    wi = np.ones((5, 64), np.int8)
+    lp = o.logprob_i8(xi, wi, np.array([5, 4], np.int32), np.ones(2, np.float32))
+    assert np.isnan(lp[0]) and abs(lp[1] + math.log(5)) < 1e-14
+
+
+# ------------------------------------------------------ bf16 rounding
+def pin_round_bf16(o):
+    """Rounding float64 -> bf16 is nearest-even: it matches the bit-level RNE
+    of float32 inputs, exact halfway cases go to the even neighbour, and random
+    doubles match an exact rational rounding."""
+    rng = np.random.default_rng(41)
+    f32 = (rng.standard_normal(2000) * np.exp2(rng.integers(-20, 20, 2000))).astype(np.float32)
+    ref = synth.bf16_to_f32(synth.bf16_from_f32(f32)).astype(np.float64)
+    got = np.array([o.round_bf16(float(v)) for v in f32])
+    assert np.array_equal(got, ref)
+    assert o.round_bf16(1.0 + 2.0 ** -8) == 1.0
+    assert o.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert o.round_bf16(-(1.0 + 2.0 ** -8)) == -1.0
+    assert o.round_bf16(6.0 + 2.0 ** -6) == 6.0 and o.round_bf16(6.0 + 3 * 2.0 ** -6) == 6.0 + 2.0 ** -4
+    for v in rng.standard_normal(500) * 50:
+        a = Fraction(float(v))
+        e = math.floor(math.log2(abs(a)))
+        q = a / Fraction(2) ** (e - 7)
+        n = math.floor(q)
+        rem = q - n
+        if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2):
+            n += 1
+        assert o.round_bf16(float(v)) == float(n * Fraction(2) ** (e - 7))
+
+
+# --------------------------------------------- the pages' own numbers
+def pin_pages_float_examples(o):
+    """The printed float examples (golden file) hold in IEEE arithmetic, and a
+    crafted row shows the two summation orders a split-K kernel can pick give
+    different float32 results while the oracle's float64 logit is exact."""
+    g = json.loads((GOLDEN / "pages_float_examples.json").read_text())
+    for case in g["cases"]:
+        t = {"float64": np.float64, "float32": np.float32}[case["dtype"]]
+        a, b, c = (t(case[k]) for k in ("a", "b", "c"))
+        got = t(t(a + b) + c) if case["order"] == "(a+b)+c" else t(a + t(b + c))
+        assert float(got) == float(case["value"]), case
+    H = 8
+    x = bf16_const(1.0, (1, H))
+    vals = [2.0 ** 24, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0]
+    w = synth.bf16_from_f32(np.array([vals], np.float32))
+    seq = np.float32(0)
+    for v in vals:
+        seq = np.float32(seq + np.float32(v))
+    halves = np.float32(0)
+    for part in (vals[:4], vals[4:]):
+        acc = np.float32(0)
+        for v in part:
+            acc = np.float32(acc + np.float32(v))
+        halves = np.float32(halves + acc)
+    assert seq == 2.0 ** 24 and halves == 2.0 ** 24 + 4
+    assert o.logits_bf16(x, w)[0, 0] == 2.0 ** 24 + 7
+
+
+# --------------------------------------------------- near-tie workload
+def pin_neartie_builder(o, rows=48):
+    """On the planted near-tie rows the oracle's top-2 is the planted pair, the
+    winner is the planted winner (lowest id on an exact tie) and its margin
+    equals the builder's exact gap within 1e-9."""
+    d = synth.make_inputs("neartie", rows=rows)
+    ids, vals, margin = o.greedy_bf16(d["x"], d["w"])
+    t = d["tie"]
+    for r in range(rows):
+        win, lose, gap = int(t["win"][r]), int(t["lose"][r]), float(t["gap"][r])
+        assert set(ids[r]) == {win, lose}, r
+        assert ids[r, 0] == (min(win, lose) if gap == 0.0 else win), r
+        assert abs(margin[r] - gap) <= 1e-9, r
+
+
+FAST = [
+    pin_logits_bruteforce, pin_logits_one_hot, pin_logits_closed_forms,
+    pin_int_logits_bruteforce, pin_int_overflow_bound, pin_top2_bruteforce,
+    pin_top2_hand_ties, pin_greedy_identical_rows, pin_greedy_permutation,
+    pin_greedy_near_ties, pin_int_scaled_values, pin_logsoftmax_sums_to_one,
+    pin_logprob_closed_forms, pin_logprob_shift_invariance, pin_logprob_decimal,
+    pin_logprob_out_of_range, pin_round_bf16, pin_pages_float_examples,
+]
+SLOW = [pin_logits_vs_blas, pin_int_logits_vs_numpy, pin_neartie_builder]
+ALL = FAST + SLOW
