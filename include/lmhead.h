@@ -1,0 +1,139 @@
+/*
+ * lmhead.h - batch-invariant LM head for AMD Instinct MI355X (gfx950).
+ *
+ * The output projection of final hidden states against the vocabulary matrix,
+ * followed by greedy top-2 (with the top-2 logit margin) or by the log-softmax
+ * probability of a given token, in two arithmetic modes:
+ *
+ *   LMHEAD_MODE_BF16  bf16 hidden x bf16 vocab matrix, products accumulated in
+ *                     float32 in one fixed order, float32 logits.
+ *                     ("Greedy Decoding Has a Precision Clause", section
+ *                     "Correct the vulnerable token decisions, not every
+ *                     calculation": the final output projection recomputed in
+ *                     FP32; "12 Exactness", section 12.2: the head returns
+ *                     fp32 logits.)
+ *   LMHEAD_MODE_INT8  int8 hidden x int8 vocab matrix, exact int32 logits.
+ *                     ("Eliminating Nondeterminism in LLM Inference with
+ *                     Integer-Only Arithmetic", sections "What if we don't use
+ *                     floats at all?" and "DetLLM": int8 x int8 -> int32
+ *                     matmul; integer sums are exact in any order.)
+ *
+ * Batch invariance.  Every logit is reduced over k in one order fixed by H
+ * alone (one MFMA shape, k ascending, one accumulator), never by the number of
+ * rows or a row's position in the batch; the softmax partial sums are fixed by
+ * V alone.  A row's outputs are therefore bitwise identical at every batch
+ * size.  ("12 Exactness", section 12.2: every matrix-product kernel fixes its
+ * reduction order by the weight's shape and never by the row count;
+ * "Integer-Only Arithmetic", section "Why kernels don't always add in the same
+ * order": split reductions chosen by batch size break batch invariance.)
+ *
+ * Layout.  x is [B, H] row-major, w is [V, H] row-major (each vocabulary row
+ * contiguous in k).  bf16 tensors are raw 16-bit patterns.  x, w and the
+ * workspace must be 16-byte aligned, every other array aligned to its element
+ * size.  All data pointers are DEVICE pointers owned by the caller; the
+ * library never allocates, frees or synchronises, and keeps no pointer after a
+ * call returns.  Every call is
+ * asynchronous on `stream` (a hipStream_t; NULL = the default stream).
+ *
+ * Errors.  Arguments are validated on the host, synchronously, before any work
+ * is queued; on any error nothing is queued and the status says why.  A failed
+ * launch returns LMHEAD_E_HIP (lmhead_last_error() has the HIP message).  No
+ * exception or abort crosses this interface.  Inputs are assumed finite.
+ */
+#ifndef LMHEAD_H_
+#define LMHEAD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LMHEAD_OK = 0,
+  LMHEAD_E_NULL = 1,      /* a required pointer is NULL */
+  LMHEAD_E_SHAPE = 2,     /* B < 1, V < 2, H not a positive multiple of 64, or too large */
+  LMHEAD_E_ALIGN = 3,     /* x, w or workspace not 16-byte aligned, or another array
+                             not aligned to its element size */
+  LMHEAD_E_MODE = 4,      /* unknown mode / rounding, or rounding not valid for the mode */
+  LMHEAD_E_OVERFLOW = 5,  /* int8: H * 128^2 could exceed int32 (H > 131071) */
+  LMHEAD_E_WORKSPACE = 6, /* workspace NULL or smaller than lmhead_workspace_bytes() */
+  LMHEAD_E_HIP = 7        /* the HIP runtime refused the launch */
+} lmhead_status;
+
+typedef enum { LMHEAD_MODE_BF16 = 0, LMHEAD_MODE_INT8 = 1 } lmhead_mode;
+
+/* Rounding of the logits before they are stored or ranked.  LMHEAD_ROUND_BF16
+ * is the ordinary 16-bit head (float32 accumulation, then round-to-nearest-even
+ * to bf16), kept to compare decisions against the float32 head; it is valid
+ * only in LMHEAD_MODE_BF16.  ("Greedy Decoding Has a Precision Clause":
+ * BF16-output head versus the FP32-recomputed head.) */
+typedef enum { LMHEAD_ROUND_F32 = 0, LMHEAD_ROUND_BF16 = 1 } lmhead_round;
+
+/* Bytes of device workspace lmhead_greedy_top2 / lmhead_logprob need for this
+ * shape (0 if the shape is invalid).  The workspace must be zero-filled ONCE by
+ * the caller before its first use; every call leaves it zero-filled again.  One
+ * workspace must not be shared by two calls that can run at the same time. */
+size_t lmhead_workspace_bytes(int mode, int64_t B, int64_t H, int64_t V);
+
+/* Full logits.  logits[b, v] = sum_k x[b, k] * w[v, k], stored row-major [B, V]
+ * as float32 (MODE_BF16, ROUND_F32), bf16 bits (MODE_BF16, ROUND_BF16) or int32
+ * (MODE_INT8, exact).  ("Greedy Decoding Has a Precision Clause", section
+ * "Token-ranking margins explain why numerical error sometimes matters": the
+ * lm_head turns the final representation into one score per token.) */
+lmhead_status lmhead_logits(int mode, int round, const void *x, const void *w, int64_t B,
+                            int64_t H, int64_t V, void *logits, void *stream);
+
+/* Greedy decision per row, logits never written to memory.
+ *   top_id[b, 0..1]  ids of the best and second-best logit; ties go to the
+ *                    lowest token id ("Integer-Only Arithmetic", section
+ *                    "DetLLM": argmax breaks ties toward the lowest token id);
+ *                    an exactly tied maximum makes top_id[b,1] the next tied id.
+ *   top_val[b, 0..1] their values: float32 logits (ROUND_BF16: the bf16-rounded
+ *                    logits); MODE_INT8: float32(raw * row_scale[b]), one
+ *                    rounding of the exact product.
+ *   margin[b]        top-2 logit margin z(1) - z(2) >= 0 ("Greedy Decoding Has
+ *                    a Precision Clause", section "Token-ranking margins": the
+ *                    top-two logit margin); MODE_INT8: float32((raw1 - raw2) *
+ *                    row_scale[b]).
+ *   top_raw[b, 0..1] MODE_INT8 only, optional (NULL to skip): exact int32 logits.
+ *   row_scale[b]     MODE_INT8 only, optional (NULL = 1): per-row positive
+ *                    float32 scale applied after the integer argmax; a
+ *                    non-positive or non-finite scale makes that row's values
+ *                    and margin NaN (ids and raw values stay exact).
+ * ws / ws_bytes: device workspace, see lmhead_workspace_bytes. */
+lmhead_status lmhead_greedy_top2(int mode, int round, const void *x, const void *w, int64_t B,
+                                 int64_t H, int64_t V, const float *row_scale, int32_t *top_id,
+                                 float *top_val, float *margin, int32_t *top_raw, void *ws,
+                                 size_t ws_bytes, void *stream);
+
+/* log p(target[b]) under the softmax (temperature 1) of row b's logits, float32,
+ * logits never written to memory ("batch-logprob-gap": the log probability a
+ * model gives a token; "Inference and Decoding", section 3, temperature
+ * softmax).  MODE_INT8 uses the scaled logits row_scale[b] * z (NULL = 1).  A
+ * target outside [0, V) or an invalid scale gives NaN for that row. */
+lmhead_status lmhead_logprob(int mode, const void *x, const void *w, int64_t B, int64_t H,
+                             int64_t V, const float *row_scale, const int32_t *target,
+                             float *logprob, void *ws, size_t ws_bytes, void *stream);
+
+/* Device self-check of the row property ("12 Exactness", section 12.8: a
+ * load-time self-check proves on the device that every row gets the same bits
+ * whatever the number of rows).  Computes the logits of x[0..B) as one batch,
+ * of every row alone, and of the rows in reverse order, and adds the number of
+ * logits whose bits differ to *mismatches (a device uint64 the caller zeroes).
+ * scratch: device memory of lmhead_self_check_bytes() bytes, 16-byte aligned;
+ * it is overwritten. */
+size_t lmhead_self_check_bytes(int mode, int64_t B, int64_t H, int64_t V);
+lmhead_status lmhead_self_check(int mode, const void *x, const void *w, int64_t B, int64_t H,
+                                int64_t V, void *scratch, size_t scratch_bytes,
+                                uint64_t *mismatches, void *stream);
+
+/* Text of a status code, and of the last HIP error seen by this thread. */
+const char *lmhead_status_string(int status);
+const char *lmhead_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LMHEAD_H_ */

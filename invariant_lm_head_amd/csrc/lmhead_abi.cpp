@@ -1,0 +1,222 @@
+// C-ABI of the batch-invariant LM head (declared in include/lmhead.h).
+//
+// Everything here runs on the host: argument validation (synchronous, before
+// anything is queued), workspace layout, choice of the grid tiling and the
+// kernel launch on the caller's stream.  No allocation, no synchronisation.
+#include "lmhead.h"
+
+#include <hip/hip_runtime_api.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "lmhead_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "no HIP error";
+
+constexpr int64_t kMaxRows = (int64_t)1 << 24;   // B bound (int indexing of rows)
+constexpr int64_t kMaxVocab = (int64_t)1 << 30;  // V bound
+constexpr int64_t kMaxHidden = (int64_t)1 << 20; // H bound
+constexpr int64_t kInt8MaxHidden = 131071;       // H * 128^2 < 2^31
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+lmhead_status check_common(int mode, int round, const void *x, const void *w, int64_t B,
+                           int64_t H, int64_t V) {
+  if (mode != LMHEAD_MODE_BF16 && mode != LMHEAD_MODE_INT8) return LMHEAD_E_MODE;
+  if (round != LMHEAD_ROUND_F32 && round != LMHEAD_ROUND_BF16) return LMHEAD_E_MODE;
+  if (mode == LMHEAD_MODE_INT8 && round != LMHEAD_ROUND_F32) return LMHEAD_E_MODE;
+  if (!x || !w) return LMHEAD_E_NULL;
+  if (B < 1 || B > kMaxRows || V < 2 || V > kMaxVocab || H < 64 || H % 64 != 0 ||
+      H > kMaxHidden)
+    return LMHEAD_E_SHAPE;
+  if (mode == LMHEAD_MODE_INT8 && H > kInt8MaxHidden) return LMHEAD_E_OVERFLOW;
+  if (!aligned16(x) || !aligned16(w)) return LMHEAD_E_ALIGN;
+  return LMHEAD_OK;
+}
+
+lmhead_status launched(hipError_t e) {
+  if (e == hipSuccess) return LMHEAD_OK;
+  snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+  return LMHEAD_E_HIP;
+}
+
+lmh::Params base_params(int mode, const void *x, const void *w, int64_t B, int64_t H, int64_t V,
+                        const lmh::Plan &plan) {
+  lmh::Params p;
+  memset(&p, 0, sizeof p);
+  p.x = (const char *)x;
+  p.w = (const char *)w;
+  p.rowbytes = mode == LMHEAD_MODE_BF16 ? 2 * H : H;
+  p.B = (int)B;
+  p.V = (int)V;
+  p.nblocks = (int)((V + lmh::kBlockCols - 1) / lmh::kBlockCols);
+  p.grid_m = plan.grid_m;
+  p.grid_n = plan.grid_n;
+  return p;
+}
+
+int64_t row_bytes(int mode, int64_t H) { return mode == LMHEAD_MODE_BF16 ? 2 * H : H; }
+
+}  // namespace
+
+namespace lmh {
+size_t workspace_layout(int64_t B, int64_t V, size_t *off_zt, size_t *off_records) {
+  auto up = [](size_t n) { return (n + 255) & ~(size_t)255; };
+  const size_t tickets = up(sizeof(unsigned) * (size_t)((B + 15) / 16));
+  const size_t zt = up(sizeof(int32_t) * (size_t)B);
+  const size_t nblocks = (size_t)((V + kBlockCols - 1) / kBlockCols);
+  const size_t records = 16 * (size_t)B * nblocks;
+  if (off_zt) *off_zt = tickets;
+  if (off_records) *off_records = tickets + zt;
+  return tickets + zt + records;
+}
+}  // namespace lmh
+
+extern "C" {
+
+size_t lmhead_workspace_bytes(int mode, int64_t B, int64_t H, int64_t V) {
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  if (check_common(mode, LMHEAD_ROUND_F32, dummy, dummy, B, H, V) != LMHEAD_OK) return 0;
+  return lmh::workspace_layout(B, V, nullptr, nullptr);
+}
+
+lmhead_status lmhead_logits(int mode, int round, const void *x, const void *w, int64_t B,
+                            int64_t H, int64_t V, void *logits, void *stream) {
+  lmhead_status st = check_common(mode, round, x, w, B, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (!logits) return LMHEAD_E_NULL;
+  if (((uintptr_t)logits & (round == LMHEAD_ROUND_BF16 ? 1u : 3u)) != 0) return LMHEAD_E_ALIGN;
+  const lmh::Plan plan = lmh::plan_for(B, row_bytes(mode, H), V);
+  lmh::Params p = base_params(mode, x, w, B, H, V, plan);
+  p.round_bf16 = round == LMHEAD_ROUND_BF16;
+  p.logits = logits;
+  return launched(lmh::launch(mode, lmh::kStore, plan, p, (hipStream_t)stream));
+}
+
+static lmhead_status bind_workspace(lmh::Params &p, void *ws, size_t ws_bytes, int64_t B,
+                                    int64_t V) {
+  size_t off_zt, off_rec;
+  const size_t need = lmh::workspace_layout(B, V, &off_zt, &off_rec);
+  if (!ws || ws_bytes < need) return LMHEAD_E_WORKSPACE;
+  if (!aligned16(ws)) return LMHEAD_E_ALIGN;
+  p.tickets = (unsigned *)ws;
+  p.zt = (int32_t *)((char *)ws + off_zt);
+  p.records = (uint4 *)((char *)ws + off_rec);
+  return LMHEAD_OK;
+}
+
+lmhead_status lmhead_greedy_top2(int mode, int round, const void *x, const void *w, int64_t B,
+                                 int64_t H, int64_t V, const float *row_scale, int32_t *top_id,
+                                 float *top_val, float *margin, int32_t *top_raw, void *ws,
+                                 size_t ws_bytes, void *stream) {
+  lmhead_status st = check_common(mode, round, x, w, B, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (!top_id || !top_val || !margin) return LMHEAD_E_NULL;
+  if (!aligned4(top_id) || !aligned4(top_val) || !aligned4(margin) ||
+      (top_raw && !aligned4(top_raw)) || (row_scale && !aligned4(row_scale)))
+    return LMHEAD_E_ALIGN;
+  const lmh::Plan plan = lmh::plan_for(B, row_bytes(mode, H), V);
+  lmh::Params p = base_params(mode, x, w, B, H, V, plan);
+  st = bind_workspace(p, ws, ws_bytes, B, V);
+  if (st != LMHEAD_OK) return st;
+  p.round_bf16 = round == LMHEAD_ROUND_BF16;
+  p.scale = mode == LMHEAD_MODE_INT8 ? row_scale : nullptr;
+  p.top_id = top_id;
+  p.top_val = top_val;
+  p.margin = margin;
+  p.top_raw = mode == LMHEAD_MODE_INT8 ? top_raw : nullptr;
+  return launched(lmh::launch(mode, lmh::kTop2, plan, p, (hipStream_t)stream));
+}
+
+lmhead_status lmhead_logprob(int mode, const void *x, const void *w, int64_t B, int64_t H,
+                             int64_t V, const float *row_scale, const int32_t *target,
+                             float *logprob, void *ws, size_t ws_bytes, void *stream) {
+  lmhead_status st = check_common(mode, LMHEAD_ROUND_F32, x, w, B, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (!target || !logprob) return LMHEAD_E_NULL;
+  if (!aligned4(target) || !aligned4(logprob) || (row_scale && !aligned4(row_scale)))
+    return LMHEAD_E_ALIGN;
+  const lmh::Plan plan = lmh::plan_for(B, row_bytes(mode, H), V);
+  lmh::Params p = base_params(mode, x, w, B, H, V, plan);
+  st = bind_workspace(p, ws, ws_bytes, B, V);
+  if (st != LMHEAD_OK) return st;
+  p.scale = mode == LMHEAD_MODE_INT8 ? row_scale : nullptr;
+  p.target = target;
+  p.logprob = logprob;
+  return launched(lmh::launch(mode, lmh::kLse, plan, p, (hipStream_t)stream));
+}
+
+// scratch: [B, V] batch logits | [V] one-row logits | [B, V] reversed-batch logits |
+//          [B, H] reversed rows; every region 256-byte aligned
+static size_t self_check_layout(int mode, int64_t B, int64_t H, int64_t V, size_t off[4]) {
+  auto up = [](size_t n) { return (n + 255) & ~(size_t)255; };
+  const size_t lb = up(4 * (size_t)B * (size_t)V), l1 = up(4 * (size_t)V);
+  off[0] = 0;
+  off[1] = lb;
+  off[2] = lb + l1;
+  off[3] = lb + l1 + lb;
+  return off[3] + up((size_t)B * (size_t)row_bytes(mode, H));
+}
+
+size_t lmhead_self_check_bytes(int mode, int64_t B, int64_t H, int64_t V) {
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  if (check_common(mode, LMHEAD_ROUND_F32, dummy, dummy, B, H, V) != LMHEAD_OK) return 0;
+  size_t off[4];
+  return self_check_layout(mode, B, H, V, off);
+}
+
+lmhead_status lmhead_self_check(int mode, const void *x, const void *w, int64_t B, int64_t H,
+                                int64_t V, void *scratch, size_t scratch_bytes,
+                                uint64_t *mismatches, void *stream) {
+  lmhead_status st = check_common(mode, LMHEAD_ROUND_F32, x, w, B, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (!scratch || !mismatches) return LMHEAD_E_NULL;
+  size_t off[4];
+  if (scratch_bytes < self_check_layout(mode, B, H, V, off)) return LMHEAD_E_WORKSPACE;
+  if (!aligned16(scratch) || !aligned4(mismatches)) return LMHEAD_E_ALIGN;
+  char *sc = (char *)scratch;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t rb = row_bytes(mode, H);
+  unsigned long long *mm = (unsigned long long *)mismatches;
+  // the whole batch
+  if ((st = lmhead_logits(mode, LMHEAD_ROUND_F32, x, w, B, H, V, sc + off[0], stream)))
+    return st;
+  // every row alone, compared with its row of the batch
+  for (int64_t r = 0; r < B; ++r) {
+    if ((st = lmhead_logits(mode, LMHEAD_ROUND_F32, (const char *)x + r * rb, w, 1, H, V,
+                            sc + off[1], stream)))
+      return st;
+    if ((st = launched(lmh::launch_compare(sc + off[0] + 4 * r * V, sc + off[1], V, mm, s))))
+      return st;
+  }
+  // the rows in reverse order (every row at another position, other neighbours)
+  if ((st = launched(lmh::launch_reverse_rows(x, sc + off[3], B, rb, s)))) return st;
+  if ((st = lmhead_logits(mode, LMHEAD_ROUND_F32, sc + off[3], w, B, H, V, sc + off[2], stream)))
+    return st;
+  for (int64_t r = 0; r < B; ++r)
+    if ((st = launched(lmh::launch_compare(sc + off[0] + 4 * r * V,
+                                           sc + off[2] + 4 * (B - 1 - r) * V, V, mm, s))))
+      return st;
+  return LMHEAD_OK;
+}
+
+const char *lmhead_status_string(int status) {
+  switch (status) {
+    case LMHEAD_OK: return "ok";
+    case LMHEAD_E_NULL: return "a required pointer is NULL";
+    case LMHEAD_E_SHAPE: return "invalid shape (need B >= 1, V >= 2, H a positive multiple of 64)";
+    case LMHEAD_E_ALIGN: return "a pointer is not 16-byte aligned";
+    case LMHEAD_E_MODE: return "unknown mode or rounding, or rounding not valid for the mode";
+    case LMHEAD_E_OVERFLOW: return "int8 head: H too large for exact int32 accumulation";
+    case LMHEAD_E_WORKSPACE: return "workspace missing or too small";
+    case LMHEAD_E_HIP: return "HIP launch failed (see lmhead_last_error)";
+    default: return "unknown status";
+  }
+}
+
+const char *lmhead_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal interface between the C-ABI layer (lmhead_abi.cpp) and the gfx950
+// kernels (lmhead_kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lmh {
+
+enum Epilogue { kStore = 0, kTop2 = 1, kLse = 2 };
+
+// Softmax partial sums and top-2 partial records are kept per block of 128
+// vocabulary columns; the block grid depends on V only.
+constexpr int kBlockCols = 128;
+
+struct Params {
+  const char *x;      // [B, H] row-major (bf16 bits or int8)
+  const char *w;      // [V, H] row-major
+  int64_t rowbytes;   // H * element size
+  int B, V, nblocks;  // nblocks = ceil(V / kBlockCols)
+  int grid_m, grid_n; // workgroup tiles over rows and vocabulary columns
+  int round_bf16;     // 1: round logits to bf16 before storing / ranking
+  void *logits;       // kStore output [B, V]
+  const float *scale;     // int8 per-row scale (may be null)
+  const int32_t *target;  // kLse targets [B]
+  int32_t *top_id;        // [B, 2]
+  float *top_val;         // [B, 2]
+  float *margin;          // [B]
+  int32_t *top_raw;       // [B, 2] int8 only (may be null)
+  float *logprob;         // [B]
+  unsigned *tickets;      // [ceil(B/16)] zero on entry and on exit
+  int32_t *zt;            // [B] target logit bits (float32 or int32)
+  uint4 *records;         // [B][nblocks] per-block partials
+};
+
+// One tiling of the grid: which kernel instance runs and its grid shape.
+struct Plan {
+  int variant;  // tile shape index (see lmhead_kernels.hip)
+  int bkb;      // bytes of every row staged per pipeline stage
+  int bm, bn;   // rows and vocabulary columns per workgroup
+  int grid_m, grid_n;
+};
+
+Plan plan_for(int64_t B, int64_t rowbytes, int64_t V);
+
+// Byte offsets of the workspace regions; returns the total size.
+size_t workspace_layout(int64_t B, int64_t V, size_t *off_zt, size_t *off_records);
+
+hipError_t launch(int mode, int epilogue, const Plan &plan, const Params &p, hipStream_t s);
+
+hipError_t launch_compare(const void *a, const void *b, int64_t nwords,
+                          unsigned long long *mismatches, hipStream_t s);
+hipError_t launch_reverse_rows(const void *src, void *dst, int64_t rows, int64_t rowbytes,
+                               hipStream_t s);
+
+}  // namespace lmh

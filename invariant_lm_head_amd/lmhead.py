@@ -1,0 +1,184 @@
+"""Python binding of liblmhead.so (the C-ABI in include/lmhead.h).
+
+Argument marshalling only: every step of the head runs in the HIP kernels.
+PyTorch provides device memory and the current stream.  There is no CPU or
+PyTorch fallback: if the library cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import threading
+
+import torch
+
+from . import _build
+
+MODE_BF16, MODE_INT8 = 0, 1
+ROUND_F32, ROUND_BF16 = 0, 1
+
+_STATUS = {0: "LMHEAD_OK", 1: "LMHEAD_E_NULL", 2: "LMHEAD_E_SHAPE", 3: "LMHEAD_E_ALIGN",
+           4: "LMHEAD_E_MODE", 5: "LMHEAD_E_OVERFLOW", 6: "LMHEAD_E_WORKSPACE",
+           7: "LMHEAD_E_HIP"}
+
+# every function the header declares, with its C signature
+_P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "lmhead_workspace_bytes": ([_I, _I64, _I64, _I64], _SZ),
+    "lmhead_logits": ([_I, _I, _P, _P, _I64, _I64, _I64, _P, _P], _I),
+    "lmhead_greedy_top2": ([_I, _I, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "lmhead_logprob": ([_I, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _I),
+    "lmhead_self_check_bytes": ([_I, _I64, _I64, _I64], _SZ),
+    "lmhead_self_check": ([_I, _P, _P, _I64, _I64, _I64, _P, _SZ, _P, _P], _I),
+    "lmhead_status_string": ([_I], ctypes.c_char_p),
+    "lmhead_last_error": ([], ctypes.c_char_p),
+}
+
+
+class LMHeadError(RuntimeError):
+    def __init__(self, fn: str, status: int, lib):
+        msg = lib.lmhead_status_string(status).decode()
+        if status == 7:
+            msg += " (" + lib.lmhead_last_error().decode() + ")"
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def library():
+    """Load liblmhead.so (building it first only if it does not exist)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not _build.LIBRARY.exists():
+                _build.build()
+            lib = ctypes.CDLL(str(_build.LIBRARY))
+            for name, (args, res) in SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.argtypes, fn.restype = args, res
+            _lib = lib
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise LMHeadError(fn, status, library())
+
+
+def _mode_of(x: torch.Tensor, w: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16 and w.dtype == torch.bfloat16:
+        return MODE_BF16
+    if x.dtype == torch.int8 and w.dtype == torch.int8:
+        return MODE_INT8
+    raise TypeError(f"x and w must both be bfloat16 or both int8, got {x.dtype}, {w.dtype}")
+
+
+def _dims(x: torch.Tensor, w: torch.Tensor):
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError(f"x must be [B, H] and w [V, H], got {tuple(x.shape)}, {tuple(w.shape)}")
+    if not (x.is_cuda and w.is_cuda and x.is_contiguous() and w.is_contiguous()):
+        raise ValueError("x and w must be contiguous device tensors")
+    return x.shape[0], x.shape[1], w.shape[0]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+# ---------------------------------------------------------------- workspace
+_ws_cache: dict = {}
+
+
+def workspace_bytes(mode: int, B: int, H: int, V: int) -> int:
+    return int(library().lmhead_workspace_bytes(mode, B, H, V))
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled workspace of at least nbytes for the current stream.
+
+    The library leaves it zeroed after every call, so it is reused by all calls
+    ordered on that stream (calls on one stream never overlap)."""
+    dev = torch.device(device)
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = ws
+    return ws
+
+
+# ---------------------------------------------------------------- calls
+def logits(x: torch.Tensor, w: torch.Tensor, round_bf16: bool = False,
+           out: torch.Tensor | None = None) -> torch.Tensor:
+    """Z = x @ w.T as float32 (bf16 mode), bf16 (round_bf16) or int32 (int8 mode)."""
+    mode = _mode_of(x, w)
+    B, H, V = _dims(x, w)
+    dt = torch.int32 if mode == MODE_INT8 else (torch.bfloat16 if round_bf16 else torch.float32)
+    if out is None:
+        out = torch.empty((B, V), dtype=dt, device=x.device)
+    st = library().lmhead_logits(mode, ROUND_BF16 if round_bf16 else ROUND_F32, _ptr(x), _ptr(w),
+                                 B, H, V, _ptr(out), _stream(x.device))
+    _check("lmhead_logits", st)
+    return out
+
+
+def greedy_top2(x: torch.Tensor, w: torch.Tensor, row_scale: torch.Tensor | None = None,
+                round_bf16: bool = False, ws: torch.Tensor | None = None):
+    """Per-row top-2 ids [B,2] int32, values [B,2] float32, margin [B] float32 and,
+    in int8 mode, the exact int32 logits of the two [B,2] (None in bf16 mode)."""
+    mode = _mode_of(x, w)
+    B, H, V = _dims(x, w)
+    dev = x.device
+    ids = torch.empty((B, 2), dtype=torch.int32, device=dev)
+    vals = torch.empty((B, 2), dtype=torch.float32, device=dev)
+    margin = torch.empty((B,), dtype=torch.float32, device=dev)
+    raw = torch.empty((B, 2), dtype=torch.int32, device=dev) if mode == MODE_INT8 else None
+    need = workspace_bytes(mode, B, H, V)
+    if ws is None:
+        ws = workspace(need, dev)
+    st = library().lmhead_greedy_top2(mode, ROUND_BF16 if round_bf16 else ROUND_F32,
+                                      _ptr(x), _ptr(w), B, H, V, _ptr(row_scale), _ptr(ids),
+                                      _ptr(vals), _ptr(margin), _ptr(raw), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(dev))
+    _check("lmhead_greedy_top2", st)
+    return ids, vals, margin, raw
+
+
+def logprob(x: torch.Tensor, w: torch.Tensor, target: torch.Tensor,
+            row_scale: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """log p(target[b]) [B] float32 under the softmax of row b's logits."""
+    mode = _mode_of(x, w)
+    B, H, V = _dims(x, w)
+    dev = x.device
+    if target.dtype != torch.int32 or target.numel() != B or not target.is_cuda:
+        raise ValueError("target must be a device int32 tensor of B ids")
+    out = torch.empty((B,), dtype=torch.float32, device=dev)
+    need = workspace_bytes(mode, B, H, V)
+    if ws is None:
+        ws = workspace(need, dev)
+    st = library().lmhead_logprob(mode, _ptr(x), _ptr(w), B, H, V, _ptr(row_scale),
+                                  _ptr(target.contiguous()), _ptr(out), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(dev))
+    _check("lmhead_logprob", st)
+    return out
+
+
+def self_check(x: torch.Tensor, w: torch.Tensor) -> int:
+    """Number of logits whose bits differ between batch, single-row and reversed
+    runs of x (0 proves the row property on this device for these rows)."""
+    mode = _mode_of(x, w)
+    B, H, V = _dims(x, w)
+    dev = x.device
+    nbytes = int(library().lmhead_self_check_bytes(mode, B, H, V))
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    count = torch.zeros(1, dtype=torch.int64, device=dev)
+    st = library().lmhead_self_check(mode, _ptr(x), _ptr(w), B, H, V, _ptr(scratch), nbytes,
+                                     _ptr(count), _stream(dev))
+    _check("lmhead_self_check", st)
+    return int(count.item())

@@ -1,0 +1,145 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and its host-side validation returns the documented status
+codes before queueing anything (no pointer is dereferenced, no HIP call made)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from invariant_lm_head_amd import _build, lmhead
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "lmhead.h"
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_MODE, E_OVERFLOW, E_WORKSPACE, E_HIP = range(8)
+A = ctypes.c_void_p(0x10000)      # aligned, never dereferenced
+A2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)    # 8-byte aligned only
+ODD = ctypes.c_void_p(0x10002)    # 2-byte aligned only
+S = ctypes.c_void_p(0)            # default stream (never reached)
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(lmhead_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return lmhead.library()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) == 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(lmhead.SIGNATURES)
+
+
+def test_library_is_gfx950_only():
+    out = _build.FLAGS
+    assert "--offload-arch=gfx950" in out and "-ffp-contract=off" in out
+
+
+def test_status_strings(lib):
+    for st in range(8):
+        assert lib.lmhead_status_string(st)
+    assert b"unknown" in lib.lmhead_status_string(99)
+    assert lib.lmhead_last_error()
+
+
+def test_workspace_bytes_layout(lib):
+    # tickets (ceil(B/16) x 4 B) | target logits (B x 4 B) | B x ceil(V/128) 16-byte records,
+    # every region rounded up to 256 bytes
+    def up(n):
+        return (n + 255) // 256 * 256
+
+    for (B, H, V) in [(1, 2048, 32000), (512, 2048, 32000), (4, 64, 1000), (16384, 4096, 151936)]:
+        want = up(4 * ((B + 15) // 16)) + up(4 * B) + 16 * B * ((V + 127) // 128)
+        assert lib.lmhead_workspace_bytes(0, B, H, V) == want
+        assert lib.lmhead_workspace_bytes(1, B, H, V) == want
+    assert lib.lmhead_workspace_bytes(0, 0, 2048, 32000) == 0
+    assert lib.lmhead_workspace_bytes(0, 1, 100, 32000) == 0
+    assert lib.lmhead_workspace_bytes(2, 1, 2048, 32000) == 0
+
+
+def logits_status(lib, mode=0, rnd=0, x=A, w=A, B=4, H=64, V=1000, out=A2):
+    return lib.lmhead_logits(mode, rnd, x, w, B, H, V, out, S)
+
+
+def test_logits_validation(lib):
+    assert logits_status(lib, mode=2) == E_MODE
+    assert logits_status(lib, rnd=2) == E_MODE
+    assert logits_status(lib, mode=1, rnd=1) == E_MODE          # bf16 rounding needs bf16 mode
+    assert logits_status(lib, x=None) == E_NULL
+    assert logits_status(lib, w=None) == E_NULL
+    assert logits_status(lib, out=None) == E_NULL
+    for B, H, V in [(0, 64, 1000), (4, 0, 1000), (4, 96, 1000), (4, 64, 1), (4, 64, 0),
+                    (-1, 64, 10), ((1 << 24) + 1, 64, 10)]:
+        assert logits_status(lib, B=B, H=H, V=V) == E_SHAPE, (B, H, V)
+    assert logits_status(lib, mode=1, H=131072) == E_OVERFLOW
+    assert logits_status(lib, mode=1, H=131008) != E_OVERFLOW
+    assert logits_status(lib, x=MIS) == E_ALIGN
+    assert logits_status(lib, w=MIS) == E_ALIGN
+    assert logits_status(lib, out=ODD) == E_ALIGN
+
+
+def test_greedy_validation(lib):
+    ws_need = lib.lmhead_workspace_bytes(0, 4, 64, 1000)
+
+    def call(mode=0, rnd=0, x=A, w=A, B=4, H=64, V=1000, scale=None, ids=A, vals=A, margin=A,
+             raw=None, ws=A2, nws=ws_need):
+        return lib.lmhead_greedy_top2(mode, rnd, x, w, B, H, V, scale, ids, vals, margin, raw,
+                                      ws, nws, S)
+
+    assert call(mode=7) == E_MODE
+    assert call(mode=1, rnd=1) == E_MODE
+    assert call(ids=None) == E_NULL
+    assert call(vals=None) == E_NULL
+    assert call(margin=None) == E_NULL
+    assert call(V=1) == E_SHAPE
+    assert call(H=65) == E_SHAPE
+    assert call(ids=ODD) == E_ALIGN
+    assert call(vals=ODD) == E_ALIGN
+    assert call(mode=1, raw=ODD) == E_ALIGN
+    assert call(mode=1, scale=ODD) == E_ALIGN
+    assert call(x=MIS) == E_ALIGN
+    assert call(ws=None) == E_WORKSPACE
+    assert call(nws=ws_need - 1) == E_WORKSPACE
+    assert call(ws=MIS) == E_ALIGN
+    assert call(mode=1, H=1 << 17) == E_OVERFLOW
+
+
+def test_logprob_validation(lib):
+    ws_need = lib.lmhead_workspace_bytes(0, 4, 64, 1000)
+
+    def call(mode=0, x=A, w=A, B=4, H=64, V=1000, scale=None, tgt=A, out=A, ws=A2, nws=ws_need):
+        return lib.lmhead_logprob(mode, x, w, B, H, V, scale, tgt, out, ws, nws, S)
+
+    assert call(mode=5) == E_MODE
+    assert call(tgt=None) == E_NULL
+    assert call(out=None) == E_NULL
+    assert call(B=0) == E_SHAPE
+    assert call(tgt=ODD) == E_ALIGN
+    assert call(out=ODD) == E_ALIGN
+    assert call(w=MIS) == E_ALIGN
+    assert call(nws=16) == E_WORKSPACE
+    assert call(mode=1, H=1 << 18) == E_OVERFLOW
+
+
+def test_self_check_validation(lib):
+    need = lib.lmhead_self_check_bytes(0, 4, 64, 1000)
+    # batch logits + one-row logits + reversed logits + reversed rows, 256-byte aligned regions
+    up = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    assert need == 2 * up(4 * 4 * 1000) + up(4 * 1000) + up(4 * 64 * 2)
+    assert lib.lmhead_self_check(0, A, A, 4, 64, 1000, None, need, A2, S) == E_NULL
+    assert lib.lmhead_self_check(0, A, A, 4, 64, 1000, A2, need, None, S) == E_NULL
+    assert lib.lmhead_self_check(0, A, A, 4, 64, 1000, A2, need - 1, A, S) == E_WORKSPACE
+    assert lib.lmhead_self_check(0, A, A, 4, 64, 1000, MIS, need, A, S) == E_ALIGN
+
+
+def test_binding_refuses_mixed_dtypes():
+    import torch
+    with pytest.raises(TypeError):
+        lmhead._mode_of(torch.zeros(1, 64, dtype=torch.bfloat16), torch.zeros(2, 64, dtype=torch.int8))

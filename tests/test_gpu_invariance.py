@@ -1,0 +1,95 @@
+"""Bitwise batch invariance of the HIP path: a row's logits, top-2 and log-prob
+bits do not depend on the batch size, the row's position or its neighbours.
+("12 Exactness", section 12.2; "batch-logprob-gap", table T1: fp32 gives 0.00%
+of importance ratios outside [0.9, 1.1] between batch 1 and batch 8, and its
+rerun control is bit-exact.)"""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+from invariant_lm_head_amd import lmhead
+from tests.gpu_util import bits, gpu, host, i8, o, tl  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+# every tile variant and its boundaries: 1..16 | 17..64 | 65..256 | 257..512
+SIZES = [1, 2, 3, 7, 15, 16, 17, 31, 33, 63, 64, 65, 100, 128, 129, 255, 256, 257, 300, 511]
+
+
+def test_logits_bits_equal_for_every_batch_size(tl):
+    full = lmhead.logits(tl["gx"], tl["gw"])
+    for B in SIZES:
+        z = lmhead.logits(tl["gx"][:B].contiguous(), tl["gw"])
+        assert torch.equal(bits(z), bits(full[:B])), B
+
+
+def test_greedy_and_logprob_bits_equal_for_every_batch_size(tl):
+    t = gpu(tl["target"])
+    g512 = lmhead.greedy_top2(tl["gx"], tl["gw"])
+    l512 = lmhead.logprob(tl["gx"], tl["gw"], t)
+    for B in SIZES:
+        x = tl["gx"][:B].contiguous()
+        g = lmhead.greedy_top2(x, tl["gw"])
+        for a, b in zip(g[:3], g512[:3]):
+            assert torch.equal(bits(a), bits(b[:B])), B
+        lp = lmhead.logprob(x, tl["gw"], t[:B].contiguous())
+        assert torch.equal(bits(lp), bits(l512[:B])), B
+
+
+def test_row_position_and_neighbours_do_not_matter(tl):
+    """A permuted batch (every row at another position with other neighbours)
+    and one row repeated B times give the same bits per row."""
+    x, w = tl["gx"], tl["gw"]
+    t = gpu(tl["target"])
+    z = lmhead.logits(x, w)
+    g = lmhead.greedy_top2(x, w)
+    lp = lmhead.logprob(x, w, t)
+    perm = torch.randperm(512, generator=torch.Generator().manual_seed(0)).to(x.device)
+    assert torch.equal(bits(lmhead.logits(x[perm].contiguous(), w)), bits(z[perm]))
+    gp = lmhead.greedy_top2(x[perm].contiguous(), w)
+    for a, b in zip(gp[:3], g[:3]):
+        assert torch.equal(bits(a), bits(b[perm]))
+    assert torch.equal(bits(lmhead.logprob(x[perm].contiguous(), w, t[perm].contiguous())),
+                       bits(lp[perm]))
+    for r, B in [(0, 16), (5, 64), (300, 257), (511, 512)]:
+        rep = x[r:r + 1].repeat(B, 1).contiguous()
+        zr = lmhead.logits(rep, w)
+        assert torch.equal(bits(zr), bits(z[r:r + 1]).expand(B, -1)), (r, B)
+        lr = lmhead.logprob(rep, w, t[r:r + 1].repeat(B).contiguous())
+        assert torch.equal(bits(lr), bits(lp[r:r + 1]).expand(B)), (r, B)
+
+
+def test_reruns_are_bit_exact(tl):
+    t = gpu(tl["target"])
+    for B in (1, 64, 512):
+        x = tl["gx"][:B].contiguous()
+        a = [lmhead.logprob(x, tl["gw"], t[:B].contiguous()) for _ in range(3)]
+        assert all(torch.equal(bits(a[0]), bits(b)) for b in a[1:])
+
+
+def test_importance_ratio_out_of_band_is_zero(tl):
+    """exp(logp at batch B - logp at batch 1) stays exactly 1 for every row."""
+    t = gpu(tl["target"])
+    lp1 = torch.cat([lmhead.logprob(tl["gx"][r:r + 1].contiguous(), tl["gw"], t[r:r + 1].contiguous())
+                     for r in range(32)])
+    for B in (8, 32):
+        lpb = lmhead.logprob(tl["gx"][:B].contiguous(), tl["gw"], t[:B].contiguous())
+        ratio = torch.exp(lpb.double() - lp1[:B].double())
+        out_of_band = ((ratio < 0.9) | (ratio > 1.1)).float().mean().item()
+        assert out_of_band == 0.0 and torch.equal(ratio, torch.ones_like(ratio))
+
+
+def test_int8_logit_hash_identical_across_batches(i8):
+    """A per-row digest of the int32 logits (SHA-256, 12 hex digits) is the same
+    at batch 1, 8 and 64 and in a reversed batch."""
+    x, w = i8["gx"], i8["gw"]
+
+    def digests(z):
+        return [hashlib.sha256(host(r).astype("<i4").tobytes()).hexdigest()[:12] for r in z]
+
+    ref = digests(lmhead.logits(x[:8].contiguous(), w))
+    assert digests(lmhead.logits(x[:1].contiguous(), w)) == ref[:1]
+    assert digests(lmhead.logits(x[:64].contiguous(), w))[:8] == ref
+    assert digests(lmhead.logits(x[:8].flip(0).contiguous(), w))[::-1] == ref

@@ -1,0 +1,256 @@
+"""HIP path against the CPU oracle, element by element, on the seeded workloads,
+plus the edge cases of the method (all through the C-ABI)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from invariant_lm_head_amd import lmhead
+from tests.gpu_util import (DEV, GAP_EXEMPT, TOL, check_greedy_bf16, gpu, gpu_bf16, host,  # noqa: F401
+                            i8, o, tl)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ tiny
+def test_tiny_all_calls(o):
+    d = synth.make_inputs("tiny")
+    x, w = gpu_bf16(d["x"]), gpu_bf16(d["w"])
+    z = o.logits_bf16(d["x"], d["w"])
+    zg = host(lmhead.logits(x, w)).astype(np.float64)
+    assert np.max(np.abs(zg - z)) <= TOL
+    # bf16-output head: within half a bf16 ulp (+ the float32 error) of the exact logit
+    z16 = host(lmhead.logits(x, w, round_bf16=True).float()).astype(np.float64)
+    ulp = np.exp2(np.floor(np.log2(np.abs(z))) - 7)
+    assert np.all(np.abs(z16 - z) <= 0.5 * ulp + TOL)
+    ids, vals, margin, raw = lmhead.greedy_top2(x, w)
+    assert raw is None
+    check_greedy_bf16(ids, vals, margin, *o.greedy_bf16(d["x"], d["w"]))
+    lp = host(lmhead.logprob(x, w, gpu(d["target"])))
+    assert np.max(np.abs(lp - o.logprob_bf16(d["x"], d["w"], d["target"]))) <= TOL
+
+
+# ------------------------------------------------------------ tinyllama
+@pytest.mark.parametrize("B", [1, 8, 64, 256, 512])
+def test_tinyllama_greedy(tl, B):
+    ids, vals, margin, _ = lmhead.greedy_top2(tl["gx"][:B].contiguous(), tl["gw"])
+    o_ids, o_vals, o_margin = (a[:B] for a in tl["o_greedy"])
+    exempt = check_greedy_bf16(ids, vals, margin, o_ids, o_vals, o_margin)
+    print(f"B={B}: {exempt} rows with oracle top-2 gap < {GAP_EXEMPT}", flush=True)
+
+
+@pytest.mark.parametrize("B", [3, 16, 17, 65, 129, 300])
+def test_tinyllama_logits(tl, o, B):
+    """Full float32 logits of ragged batches (every tile variant) vs the oracle."""
+    zg = host(lmhead.logits(tl["gx"][:B].contiguous(), tl["gw"]))
+    rows = sorted({0, B // 2, B - 1})
+    z = o.logits_bf16(tl["x"][rows], tl["w"])
+    assert np.max(np.abs(zg[rows].astype(np.float64) - z)) <= TOL
+
+
+def test_tinyllama_logprob(tl, o):
+    B = 512
+    t = tl["target"][:B]
+    lp = host(lmhead.logprob(tl["gx"], tl["gw"], gpu(t)))
+    rows = np.arange(0, B, 7)
+    ref = o.logprob_bf16(tl["x"][rows], tl["w"], t[rows])
+    assert np.max(np.abs(lp[rows] - ref)) <= TOL
+
+
+# --------------------------------------------------------------- near tie
+def test_neartie_fp32_vs_bf16_head(o):
+    """Planted top-2 near ties (0 to 4 bf16 ulps): the float32 head picks the
+    planted winner on every row whose gap is >= 1e-4 (all 4,096 rows, winner
+    pinned to the oracle on CPU; 512 rows also against the oracle here); the
+    bf16-output head is counted, binned by the gap in bf16 ulps."""
+    d = synth.make_inputs("neartie")
+    x, w = gpu_bf16(d["x"]), gpu_bf16(d["w"])
+    t = d["tie"]
+    ids, vals, margin, _ = lmhead.greedy_top2(x, w)
+    ids16, vals16, margin16, _ = lmhead.greedy_top2(x, w, round_bf16=True)
+    ids, ids16 = host(ids), host(ids16)
+    n = 512
+    check_greedy_bf16(lmhead.greedy_top2(x[:n].contiguous(), w)[0], vals[:n], margin[:n],
+                      *o.greedy_bf16(d["x"][:n], d["w"]))
+    want = np.where(t["gap"] == 0.0, np.minimum(t["win"], t["lose"]), t["win"])
+    clear = t["gap"] >= GAP_EXEMPT
+    assert np.array_equal(ids[clear, 0], want[clear])
+    assert np.all(np.isin(ids[~clear, 0], np.stack([t["win"], t["lose"]])[:, ~clear]))
+    ulps = t["gap"] / t["ulp"]
+    print("gap (bf16 ulp)   rows   fp32-head agree   bf16-head agree", flush=True)
+    for lo, hi in [(0, 0), (0, 0.5), (0.5, 1), (1, 2), (2, 4.01)]:
+        sel = (ulps == 0) if hi == 0 else (ulps > lo) & (ulps <= hi)
+        print(f"  ({lo}, {hi}]  {sel.sum():6d}  {np.mean(ids[sel, 0] == want[sel]):.4f}"
+              f"  {np.mean(ids16[sel, 0] == want[sel]):.4f}", flush=True)
+    assert np.mean(ids[:, 0] == want) >= np.mean(ids16[:, 0] == want)
+    # the bf16 head ties every pair whose gap is below half an ulp -> lowest id
+    half = (ulps > 0) & (ulps < 0.45)
+    assert np.mean(ids16[half, 0] == np.minimum(t["win"], t["lose"])[half]) > 0.95
+
+
+# ------------------------------------------------------- logprob scoring
+def test_logprob_full_size(o):
+    """16,384 x 151,936 x 4,096 scoring batch (fused log-softmax, logits never
+    stored), checked against the oracle on sampled rows."""
+    d = synth.make_inputs("logprob")
+    x, w, t = gpu_bf16(d["x"]), gpu_bf16(d["w"]), gpu(d["target"])
+    lp = host(lmhead.logprob(x, w, t))
+    rows = np.array([0, 1, 255, 256, 4095, 8191, 12000, 16383])
+    ref = o.logprob_bf16(d["x"][rows], d["w"], d["target"][rows])
+    assert np.all(np.isfinite(lp))
+    assert np.max(np.abs(lp[rows] - ref)) <= TOL
+    # batch invariance at full size: prefixes give the same bits
+    for B in (1, 17, 512):
+        lpb = host(lmhead.logprob(x[:B].contiguous(), w, t[:B].contiguous()))
+        assert np.array_equal(lpb.view(np.int32), lp[:B].view(np.int32)), B
+
+
+# ------------------------------------------------------------------ int8
+@pytest.mark.parametrize("B", [1, 8, 64, 256, 512])
+def test_int8_greedy_bit_exact(i8, B):
+    ids, vals, margin, raw = lmhead.greedy_top2(i8["gx"][:B].contiguous(), i8["gw"],
+                                                row_scale=i8["gs"][:B].contiguous())
+    rows = i8["rows"][i8["rows"] < B]
+    o_ids, o_raw, o_vals, o_margin = (a[: len(rows)] for a in i8["o_greedy"])
+    assert np.array_equal(host(ids)[rows], o_ids)
+    assert np.array_equal(host(raw)[rows].astype(np.int64), o_raw)
+    assert np.array_equal(host(vals)[rows].view(np.int32), o_vals.view(np.int32))
+    assert np.array_equal(host(margin)[rows].view(np.int32), o_margin.view(np.int32))
+
+
+def test_int8_logits_exact(i8, o):
+    zg = host(lmhead.logits(i8["gx"][:4].contiguous(), i8["gw"]))
+    assert zg.dtype == np.int32
+    assert np.array_equal(zg.astype(np.int64), o.logits_i8(i8["x"][:4], i8["w"]))
+
+
+def test_int8_logprob(i8, o):
+    B = 64
+    t = i8["target"][:B]
+    lp = host(lmhead.logprob(i8["gx"][:B].contiguous(), i8["gw"], gpu(t),
+                             row_scale=i8["gs"][:B].contiguous()))
+    rows = np.array([0, 5, 31, 63])
+    ref = o.logprob_i8(i8["x"][rows], i8["w"], t[rows], i8["scale"][rows])
+    assert np.max(np.abs(lp[rows] - ref)) <= TOL
+
+
+def test_int8_extremes_exact(o):
+    """The int32 bound: all-127 rows against +-127 and -128 W rows (H = 4096)."""
+    H, V = 4096, 300
+    rng = np.random.default_rng(7)
+    x = np.stack([np.full(H, 127, np.int8), np.full(H, -128, np.int8),
+                  rng.integers(-128, 128, H).astype(np.int8)])
+    w = rng.integers(-128, 128, (V, H)).astype(np.int8)
+    w[0], w[1], w[2] = 127, -128, -127
+    zg = host(lmhead.logits(gpu(x), gpu(w)))
+    assert np.array_equal(zg.astype(np.int64), o.logits_i8(x, w))
+    assert zg[0, 0] == 4096 * 127 * 127 and zg[1, 1] == 4096 * 128 * 128
+    ids, vals, margin, raw = lmhead.greedy_top2(gpu(x), gpu(w))
+    o_ids, o_raw, o_vals, o_margin = o.greedy_i8(x, w)
+    assert np.array_equal(host(ids), o_ids) and np.array_equal(host(raw), o_raw)
+
+
+# ---------------------------------------------------------------- edges
+@pytest.mark.parametrize("mode", ["bf16", "int8"])
+@pytest.mark.parametrize("B,H,V", [(1, 64, 2), (2, 64, 3), (5, 128, 17), (17, 64, 129),
+                                   (70, 192, 130), (300, 64, 1000), (1, 4096, 257)])
+def test_edge_shapes(o, mode, B, H, V):
+    rng = np.random.default_rng(B * 1000 + V)
+    t = rng.integers(0, V, B).astype(np.int32)
+    if mode == "bf16":
+        x = synth.bf16_from_f32(rng.standard_normal((B, H)).astype(np.float32))
+        w = synth.bf16_from_f32((0.1 * rng.standard_normal((V, H))).astype(np.float32))
+        gx, gw = gpu_bf16(x), gpu_bf16(w)
+        assert np.max(np.abs(host(lmhead.logits(gx, gw)) - o.logits_bf16(x, w))) <= TOL
+        ids, vals, margin, _ = lmhead.greedy_top2(gx, gw)
+        check_greedy_bf16(ids, vals, margin, *o.greedy_bf16(x, w))
+        lp = host(lmhead.logprob(gx, gw, gpu(t)))
+        assert np.max(np.abs(lp - o.logprob_bf16(x, w, t))) <= TOL
+    else:
+        x = rng.integers(-127, 128, (B, H)).astype(np.int8)
+        w = rng.integers(-127, 128, (V, H)).astype(np.int8)
+        s = (2.0 ** -12 * rng.uniform(0.5, 2, B)).astype(np.float32)
+        gx, gw, gs = gpu(x), gpu(w), gpu(s)
+        assert np.array_equal(host(lmhead.logits(gx, gw)).astype(np.int64), o.logits_i8(x, w))
+        ids, vals, margin, raw = lmhead.greedy_top2(gx, gw, row_scale=gs)
+        o_ids, o_raw, o_vals, o_margin = o.greedy_i8(x, w, s)
+        assert np.array_equal(host(ids), o_ids) and np.array_equal(host(raw), o_raw)
+        assert np.array_equal(host(vals).view(np.int32), o_vals.view(np.int32))
+        assert np.array_equal(host(margin).view(np.int32), o_margin.view(np.int32))
+        lp = host(lmhead.logprob(gx, gw, gpu(t), row_scale=gs))
+        assert np.max(np.abs(lp - o.logprob_i8(x, w, t, s))) <= TOL
+
+
+def test_exact_ties_go_to_lowest_id():
+    """Identical W rows tie exactly on the GPU too (same arithmetic wherever the
+    column sits): the lowest id wins and the margin is exactly 0."""
+    rng = np.random.default_rng(3)
+    H, V = 256, 1000
+    x = synth.bf16_from_f32(rng.standard_normal((40, H)).astype(np.float32))
+    w = synth.bf16_from_f32((0.02 * rng.standard_normal((V, H))).astype(np.float32))
+    for r in range(40):
+        # the row's best direction planted at 3 ids: same tile, other tile, other block
+        a = rng.choice(V, 3, replace=False)
+        w[a] = synth.bf16_from_f32(synth.bf16_to_f32(x[r]) * np.float32(0.1))
+        ids, vals, margin, _ = lmhead.greedy_top2(gpu_bf16(x[r:r + 1]), gpu_bf16(w))
+        s = np.sort(a)
+        assert list(host(ids)[0]) == [s[0], s[1]], (r, a)
+        assert host(margin)[0] == 0.0
+    xi = rng.integers(-127, 128, (1, H)).astype(np.int8)
+    wi = rng.integers(-3, 4, (V, H)).astype(np.int8)
+    wi[[900, 17, 400]] = xi[0]
+    ids, vals, margin, raw = lmhead.greedy_top2(gpu(xi), gpu(wi))
+    assert list(host(ids)[0]) == [17, 400] and host(margin)[0] == 0.0
+
+
+def test_invalid_target_and_scale_give_nan(o):
+    rng = np.random.default_rng(5)
+    H, V, B = 64, 300, 6
+    x = synth.bf16_from_f32(rng.standard_normal((B, H)).astype(np.float32))
+    w = synth.bf16_from_f32((0.1 * rng.standard_normal((V, H))).astype(np.float32))
+    t = np.array([-1, 0, V, 299, 2 ** 31 - 1, 5], np.int32)
+    lp = host(lmhead.logprob(gpu_bf16(x), gpu_bf16(w), gpu(t)))
+    assert np.isnan(lp[[0, 2, 4]]).all() and np.isfinite(lp[[1, 3, 5]]).all()
+    xi = rng.integers(-127, 128, (B, H)).astype(np.int8)
+    wi = rng.integers(-127, 128, (V, H)).astype(np.int8)
+    s = np.array([1e-4, 0.0, -1.0, np.inf, np.nan, 2e-4], np.float32)
+    ids, vals, margin, raw = lmhead.greedy_top2(gpu(xi), gpu(wi), row_scale=gpu(s))
+    o_ids, o_raw, _, _ = o.greedy_i8(xi, wi, s)
+    assert np.array_equal(host(ids), o_ids) and np.array_equal(host(raw), o_raw)
+    v = host(vals)
+    assert np.isnan(v[1:5]).all() and np.isfinite(v[[0, 5]]).all()
+    lp = host(lmhead.logprob(gpu(xi), gpu(wi), gpu(np.full(B, 3, np.int32)), row_scale=gpu(s)))
+    assert np.isnan(lp[1:5]).all() and np.isfinite(lp[[0, 5]]).all()
+
+
+def test_workspace_reused_across_calls(tl):
+    """One workspace serves consecutive calls of different sizes (the library
+    leaves it zeroed); results equal those of a fresh workspace."""
+    ws = torch.zeros(lmhead.workspace_bytes(0, 512, 2048, 32000), dtype=torch.uint8, device=DEV)
+    runs = []
+    for B in (512, 7, 512, 1, 300):
+        runs.append(lmhead.greedy_top2(tl["gx"][:B].contiguous(), tl["gw"], ws=ws))
+        assert int(ws[:256].count_nonzero()) == 0      # tickets back to zero
+    fresh = lmhead.greedy_top2(tl["gx"], tl["gw"], ws=torch.zeros_like(ws))
+    for B, r in zip((512, 7, 512, 1, 300), runs):
+        for a, b in zip(r[:3], fresh[:3]):
+            assert torch.equal(a, b[:B])
+
+
+def test_self_check_reports_no_mismatch(tl, i8):
+    assert lmhead.self_check(tl["gx"][:6].contiguous(), tl["gw"]) == 0
+    assert lmhead.self_check(i8["gx"][:5].contiguous(), i8["gw"]) == 0
+
+
+def test_bad_arguments_raise_before_launch(tl):
+    x, w = tl["gx"][:4].contiguous(), tl["gw"]
+    small = torch.zeros(64, dtype=torch.uint8, device=DEV)
+    with pytest.raises(lmhead.LMHeadError) as e:
+        lmhead.greedy_top2(x, w, ws=small)
+    assert e.value.status == 6
+    with pytest.raises(lmhead.LMHeadError) as e:
+        lmhead.logits(x[:, :100].contiguous(), w[:, :100].contiguous())
+    assert e.value.status == 2
