@@ -47,8 +47,20 @@ def build(force: bool = True) -> Path:
     return LIBRARY
 
 
+def default_threads() -> int:
+    """Worker threads when none are given: OMP_NUM_THREADS if set, else the
+    online CPUs, at most 16 (a GPU machine's CPU share)."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    n = int(env) if env.isdigit() and int(env) > 0 else (os.cpu_count() or 1)
+    return max(1, min(n, 16))
+
+
 def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _nt(n):
+    return default_threads() if n is None else n
 
 
 def _c(a, dtype):
@@ -92,24 +104,24 @@ class Oracle:
         return self.lib.oracle_threads(n)
 
     # -------------------------------------------------------- logits
-    def logits_bf16(self, x, w, nthreads: int = 0) -> np.ndarray:
+    def logits_bf16(self, x, w, nthreads: int | None = None) -> np.ndarray:
         """z[r, v] = sum_k x[r, k] * w[v, k] in float64, k ascending (bf16 bits in)."""
         x, w = _c(x, np.uint16), _c(w, np.uint16)
         B, H, V = _shape(x, w)
         z = np.empty((B, V), np.float64)
-        assert self.lib.oracle_logits_bf16(_ptr(x), _ptr(w), B, H, V, _ptr(z), nthreads) == 0
+        assert self.lib.oracle_logits_bf16(_ptr(x), _ptr(w), B, H, V, _ptr(z), _nt(nthreads)) == 0
         return z
 
-    def logits_i8(self, x, w, nthreads: int = 0) -> np.ndarray:
+    def logits_i8(self, x, w, nthreads: int | None = None) -> np.ndarray:
         """z[r, v] = sum_k x[r, k] * w[v, k] exactly in int64."""
         x, w = _c(x, np.int8), _c(w, np.int8)
         B, H, V = _shape(x, w)
         z = np.empty((B, V), np.int64)
-        assert self.lib.oracle_logits_i8(_ptr(x), _ptr(w), B, H, V, _ptr(z), nthreads) == 0
+        assert self.lib.oracle_logits_i8(_ptr(x), _ptr(w), B, H, V, _ptr(z), _nt(nthreads)) == 0
         return z
 
     # -------------------------------------------------------- greedy
-    def greedy_bf16(self, x, w, round_bf16: bool = False, nthreads: int = 0):
+    def greedy_bf16(self, x, w, round_bf16: bool = False, nthreads: int | None = None):
         """Top-2 ids, values and margin of each row's float64 logits.
 
         Ties go to the lowest id.  With ``round_bf16`` the logits are first
@@ -122,11 +134,11 @@ class Oracle:
         vals = np.empty((B, 2), np.float64)
         margin = np.empty(B, np.float64)
         rc = self.lib.oracle_greedy_bf16(_ptr(x), _ptr(w), B, H, V, int(round_bf16),
-                                         _ptr(ids), _ptr(vals), _ptr(margin), nthreads)
+                                         _ptr(ids), _ptr(vals), _ptr(margin), _nt(nthreads))
         assert rc == 0
         return ids, vals, margin
 
-    def greedy_i8(self, x, w, scale=None, nthreads: int = 0):
+    def greedy_i8(self, x, w, scale=None, nthreads: int | None = None):
         """Top-2 on exact int64 logits, then the per-row scale.
 
         Returns (ids[B,2] int32, raw[B,2] int64, vals[B,2] float32, margin[B]
@@ -143,22 +155,22 @@ class Oracle:
         margin = np.empty(B, np.float32)
         rc = self.lib.oracle_greedy_i8(_ptr(x), _ptr(w), B, H, V,
                                        None if s is None else _ptr(s),
-                                       _ptr(ids), _ptr(raw), _ptr(vals), _ptr(margin), nthreads)
+                                       _ptr(ids), _ptr(raw), _ptr(vals), _ptr(margin), _nt(nthreads))
         assert rc == 0
         return ids, raw, vals, margin
 
     # ------------------------------------------------------ log-prob
-    def logprob_bf16(self, x, w, target, nthreads: int = 0) -> np.ndarray:
+    def logprob_bf16(self, x, w, target, nthreads: int | None = None) -> np.ndarray:
         """log p(target[r]) under softmax of row r's float64 logits (NaN if out of range)."""
         x, w = _c(x, np.uint16), _c(w, np.uint16)
         B, H, V = _shape(x, w)
         t = _c(target, np.int32)
         out = np.empty(B, np.float64)
         assert self.lib.oracle_logprob_bf16(_ptr(x), _ptr(w), B, H, V, _ptr(t), _ptr(out),
-                                            nthreads) == 0
+                                            _nt(nthreads)) == 0
         return out
 
-    def logprob_i8(self, x, w, target, scale=None, nthreads: int = 0) -> np.ndarray:
+    def logprob_i8(self, x, w, target, scale=None, nthreads: int | None = None) -> np.ndarray:
         """log p(target[r]) under softmax of scale[r] * z (exact int differences)."""
         x, w = _c(x, np.int8), _c(w, np.int8)
         B, H, V = _shape(x, w)
@@ -167,7 +179,7 @@ class Oracle:
         out = np.empty(B, np.float64)
         assert self.lib.oracle_logprob_i8(_ptr(x), _ptr(w), B, H, V,
                                           None if s is None else _ptr(s), _ptr(t), _ptr(out),
-                                          nthreads) == 0
+                                          _nt(nthreads)) == 0
         return out
 
     # ------------------------------------------- per-row definitions
