@@ -1,0 +1,329 @@
+"""Benchmark of the batch-invariant LM head on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
+
+Workload (the metric's): the TinyLlama-shaped head, H = 2048, V = 32000, bf16
+hidden rows (RMS-normalised Gaussian) and W ~ N(0, 0.02) in bf16, synthetic and
+seeded.  One step = one fused greedy top-2 call (float32 head, logits never
+stored) at each batch size 1, 8, 64, 256 and 512: 841 rows.  value = rows /
+second over the K timed steps.  Inputs are resident in HBM before timing; four
+copies of W (524 MB, more than the 256 MB Infinity Cache) rotate from call to
+call, so W is read from HBM, not from the cache.
+
+Printed as ONE JSON line on stdout, with:
+  roofline      the dominant kernel (the largest batch) against MI355X's peak,
+                from HIP events on the stream the kernel runs on;
+  per_batch     every batch size: us per call, rows/s, GB/s, TFLOP/s, roofline;
+  cpu_baseline  the float64 CPU oracle timed on this host on a bounded sample;
+  other         the other workloads (log-prob scoring at H = 4096, V = 151936;
+                int8 head at H = 4096, V = 128256; near-tie stress; full logits).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK = 8.0e12           # bytes/s, MI355X HBM3E
+MFMA_PEAK = {"bf16": 2.5e15, "int8": 5.0e15}   # dense, per second
+METRIC = "LM-head rows/s + % of HBM/MFMA roofline, V=32000 H=2048, batch 1..512"
+SWEEP = (1, 8, 64, 256, 512)
+NCOPIES = 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def roofline(B, H, V, t, esize=2, out_bytes_per_row=20, mode="bf16", extra_bytes=0):
+    """Algorithmic bytes (W once + X + outputs) and flops (2 B V H) against t seconds."""
+    nbytes = V * H * esize + B * H * esize + B * out_bytes_per_row + extra_bytes
+    flops = 2.0 * B * V * H
+    t_hbm, t_mfma = nbytes / HBM_PEAK, flops / MFMA_PEAK[mode]
+    if t_hbm >= t_mfma:
+        return {"bound": "hbm", "achieved": nbytes / t / 1e9, "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": t_hbm / t, "bytes": nbytes, "flops": flops}
+    return {"bound": "mfma", "achieved": flops / t / 1e12, "peak": MFMA_PEAK[mode] / 1e12,
+            "unit": "TFLOP/s" if mode == "bf16" else "TOP/s", "frac": t_mfma / t,
+            "bytes": nbytes, "flops": flops}
+
+
+class Caller:
+    """Direct ctypes calls with pre-built arguments (keeps Python overhead per
+    launch well under the kernel time; torch allocates nothing in the loop)."""
+
+    def __init__(self, torch, lmhead, x_list, w_list, B, H, V, mode=0, kind="greedy",
+                 target=None, scale=None):
+        self.torch = torch
+        lib = lmhead.library()
+        dev = x_list[0].device
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        ws_bytes = lmhead.workspace_bytes(mode, B, H, V)
+        self.ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+        self.calls = []
+        if kind == "greedy":
+            ids = torch.empty((B, 2), dtype=torch.int32, device=dev)
+            vals = torch.empty((B, 2), dtype=torch.float32, device=dev)
+            margin = torch.empty((B,), dtype=torch.float32, device=dev)
+            raw = torch.empty((B, 2), dtype=torch.int32, device=dev) if mode == 1 else None
+            self.keep = (ids, vals, margin, raw)
+            for xx, ww in zip(x_list, w_list):
+                self.calls.append((lib.lmhead_greedy_top2, (
+                    mode, 0, P(xx), P(ww), B, H, V, P(scale), P(ids), P(vals), P(margin), P(raw),
+                    P(self.ws), ws_bytes, self.stream)))
+        elif kind == "logprob":
+            out = torch.empty((B,), dtype=torch.float32, device=dev)
+            self.keep = (out,)
+            for xx, ww in zip(x_list, w_list):
+                self.calls.append((lib.lmhead_logprob, (
+                    mode, P(xx), P(ww), B, H, V, P(scale), P(target), P(out), P(self.ws),
+                    ws_bytes, self.stream)))
+        elif kind == "logits":
+            out = torch.empty((B, V), dtype=torch.float32 if mode == 0 else torch.int32, device=dev)
+            self.keep = (out,)
+            for xx, ww in zip(x_list, w_list):
+                self.calls.append((lib.lmhead_logits, (mode, 0, P(xx), P(ww), B, H, V, P(out),
+                                                       self.stream)))
+        self.i = 0
+
+    def __call__(self, i=None):
+        """Launch once; i picks the W copy (default: this caller's own rotation)."""
+        if i is None:
+            i = self.i
+            self.i = (self.i + 1) % len(self.calls)
+        fn, args = self.calls[i % len(self.calls)]
+        st = fn(*args)
+        if st != 0:
+            raise RuntimeError(f"lmhead call failed with status {st}")
+
+
+def time_calls(torch, caller, n, warmup=3):
+    """Average seconds per launch from HIP events on the current stream."""
+    for _ in range(warmup):
+        caller()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(n):
+        caller()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / 1e3 / n
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted((ROOT / "invariant_lm_head_amd" / "csrc").glob("*")):
+        h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_tag: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources (else None)."""
+    path = ROOT / "profiles" / f"counters_{kernel_tag}.md"
+    if not path.exists():
+        return None
+    src, val = None, None
+    for line in path.read_text().splitlines():
+        if line.startswith("source_digest:"):
+            src = line.split(":", 1)[1].strip()
+        if line.startswith("hbm_bytes_per_launch:"):
+            val = float(line.split(":", 1)[1].strip())
+    return val if src == source_digest() else None
+
+
+def cpu_baseline():
+    import oracle
+    import synth
+    d = synth.make_inputs("tinyllama", rows=256)
+    n = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.greedy_bf16(d["x"], d["w"], nthreads=n)
+    dt = time.perf_counter() - t0
+    return {"value": 256 / dt, "unit": "rows/s", "cores": n, "kind": "oracle",
+            "sample": "float64 greedy top-2 of rows 0..255 of the H=2048, V=32000 head "
+                      f"({dt:.1f} s wall on {n} threads)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows shard across GPUs with no exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from invariant_lm_head_amd import lmhead
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    wl = synth.WORKLOADS["tinyllama"]
+    H, V = wl.H, wl.V
+    d = synth.make_inputs("tinyllama")
+    x = bf16(d["x"])
+    ws_ = [bf16(d["w"]) for _ in range(NCOPIES)]
+    torch.cuda.synchronize()
+
+    callers = {B: Caller(torch, lmhead, [x[:B].contiguous()] * NCOPIES, ws_, B, H, V)
+               for B in SWEEP}
+
+    # ---- the timed steps (whole sweep per step)
+    # consecutive calls always read different W copies (global rotation)
+    k = 0
+    for _ in range(args.warmup):
+        for B in SWEEP:
+            callers[B](k)
+            k += 1
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    s.record()
+    for _ in range(args.steps):
+        for B in SWEEP:
+            callers[B](k)
+            k += 1
+    e.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    step_s = s.elapsed_time(e) / 1e3 / args.steps
+    rows = sum(SWEEP)
+    value = rows / step_s
+    log(f"step: {step_s * 1e6:.1f} us for {rows} rows -> {value / 1e6:.3f} M rows/s "
+        f"(wall {t_wall:.3f} s for {args.steps} steps)")
+
+    # ---- per-batch kernel times (HIP events, cold W) and warm (one W copy)
+    per_batch = []
+    for B in SWEEP:
+        t = time_calls(torch, callers[B], 200)
+        warm = Caller(torch, lmhead, [x[:B].contiguous()], ws_[:1], B, H, V)
+        tw = time_calls(torch, warm, 200)
+        rf = roofline(B, H, V, t)
+        per_batch.append({"batch": B, "us_per_call": t * 1e6, "rows_per_s": B / t,
+                          "roofline": {k: rf[k] for k in ("bound", "achieved", "peak", "unit", "frac")},
+                          "gbps": rf["bytes"] / t / 1e9, "tflops": rf["flops"] / t / 1e12,
+                          "us_per_call_warm_mall": tw * 1e6})
+        log(f"B={B:4d}: {t * 1e6:8.2f} us  {B / t / 1e6:8.3f} M rows/s  {rf['bound']} "
+            f"{rf['achieved']:8.1f} {rf['unit']} = {100 * rf['frac']:5.1f}% "
+            f"(warm MALL {tw * 1e6:.2f} us)")
+
+    dom = max(per_batch, key=lambda r: r["us_per_call"])
+    rf = dict(dom["roofline"])
+    traffic = traffic_from_profile(f"greedy_tinyllama_b{dom['batch']}")
+    rf["traffic"] = traffic
+    rf["kernel"] = f"greedy top-2, batch {dom['batch']}"
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_s * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "TinyLlama-shaped head H=2048 V=32000, fused greedy top-2 "
+                               "(float32 head), one call per batch 1,8,64,256,512",
+                   "H": H, "V": V, "batches": list(SWEEP), "rows_per_step": rows,
+                   "w_copies_rotated": NCOPIES, "parallelism": "single GPU"},
+        "roofline": rf,
+        "per_batch": per_batch,
+        "source_digest": source_digest(),
+    }
+
+    # ---- other workloads (reported, not in value)
+    if not args.no_extras:
+        out["other"] = extras(torch, lmhead, synth, bf16, x, ws_, d)
+    del callers
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline()
+        log(f"cpu oracle: {out['cpu_baseline']['value']:.1f} rows/s on "
+            f"{out['cpu_baseline']['cores']} threads")
+    print(json.dumps(out), flush=True)
+
+
+def extras(torch, lmhead, synth, bf16, x, w_copies, d):
+    H, V = 2048, 32000
+    res = {}
+    B = 512
+    t = torch.from_numpy(d["target"][:B]).to(x.device)
+    c = Caller(torch, lmhead, [x[:B].contiguous()] * NCOPIES, w_copies, B, H, V, kind="logprob",
+               target=t)
+    tt = time_calls(torch, c, 100)
+    res["tinyllama_logprob_b512"] = {"us_per_call": tt * 1e6, "rows_per_s": B / tt,
+                                     "roofline": roofline(B, H, V, tt, out_bytes_per_row=8)}
+    c = Caller(torch, lmhead, [x[:B].contiguous()] * NCOPIES, w_copies, B, H, V, kind="logits")
+    tt = time_calls(torch, c, 100)
+    res["tinyllama_logits_b512"] = {"us_per_call": tt * 1e6, "rows_per_s": B / tt,
+                                    "roofline": roofline(B, H, V, tt, out_bytes_per_row=4 * V)}
+    del c
+    log("tinyllama logprob/logits B=512: "
+        f"{res['tinyllama_logprob_b512']['us_per_call']:.1f} / "
+        f"{res['tinyllama_logits_b512']['us_per_call']:.1f} us")
+
+    # near-tie stress, 4096 rows
+    nt = synth.make_inputs("neartie")
+    xn, wn = bf16(nt["x"]), bf16(nt["w"])
+    c = Caller(torch, lmhead, [xn], [wn], 4096, H, V)
+    tt = time_calls(torch, c, 30)
+    res["neartie_4096"] = {"us_per_call": tt * 1e6, "rows_per_s": 4096 / tt,
+                           "roofline": roofline(4096, H, V, tt)}
+    del c, xn, wn, nt
+    log(f"near-tie 4096 rows: {tt * 1e6:.1f} us")
+
+    # log-prob scoring, 16384 x 151936 x 4096
+    lp = synth.make_inputs("logprob")
+    Hl, Vl, Bl = lp["H"], lp["V"], lp["B"]
+    xl, wl_ = bf16(lp["x"]), bf16(lp["w"])
+    tl = torch.from_numpy(lp["target"]).to(x.device)
+    del lp
+    c = Caller(torch, lmhead, [xl], [wl_], Bl, Hl, Vl, kind="logprob", target=tl)
+    tt = time_calls(torch, c, 5, warmup=1)
+    res["logprob_16384x151936x4096"] = {"ms_per_call": tt * 1e3, "rows_per_s": Bl / tt,
+                                        "roofline": roofline(Bl, Hl, Vl, tt, out_bytes_per_row=8),
+                                        "exp_per_s": Bl * Vl / tt}
+    del c, xl, wl_, tl
+    torch.cuda.empty_cache()
+    log(f"log-prob 16384x151936x4096: {tt * 1e3:.2f} ms = "
+        f"{100 * res['logprob_16384x151936x4096']['roofline']['frac']:.1f}% of MFMA peak")
+
+    # int8 head, 4096 x 128256, batch 1 and 512
+    i8 = synth.make_inputs("int8")
+    Hi, Vi = i8["H"], i8["V"]
+    xi = torch.from_numpy(i8["x"]).to(x.device)
+    wi = [torch.from_numpy(i8["w"]).to(x.device)]
+    si = torch.from_numpy(i8["scale"]).to(x.device)
+    del i8
+    for B in (1, 512):
+        c = Caller(torch, lmhead, [xi[:B].contiguous()], wi, B, Hi, Vi, mode=1, scale=si[:B])
+        tt = time_calls(torch, c, 50)
+        res[f"int8_b{B}"] = {"us_per_call": tt * 1e6, "rows_per_s": B / tt,
+                             "roofline": roofline(B, Hi, Vi, tt, esize=1, out_bytes_per_row=28,
+                                                  mode="int8")}
+        r = res[f"int8_b{B}"]["roofline"]
+        log(f"int8 B={B}: {tt * 1e6:.1f} us, {r['bound']} {100 * r['frac']:.1f}%")
+    return res
+
+
+if __name__ == "__main__":
+    main()
