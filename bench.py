@@ -11,8 +11,11 @@ copies of W (524 MB, more than the 256 MB Infinity Cache) rotate from call to
 call, so W is read from HBM, not from the cache.
 
 Printed as ONE JSON line on stdout, with:
-  roofline      the dominant kernel (the largest batch) against MI355X's peak,
-                from HIP events on the stream the kernel runs on;
+  roofline      the dominant call (the largest batch: its tile kernel plus the
+                row-fold kernel) against MI355X's peak, from HIP events on the
+                stream the kernels run on; traffic = HBM bytes per call from the
+                committed rocprofv3 counter summary (null once the kernel
+                sources differ from the ones it was taken on);
   per_batch     every batch size: us per call, rows/s, GB/s, TFLOP/s, roofline;
   cpu_baseline  the float64 CPU oracle timed on this host on a bounded sample;
   other         the other workloads (log-prob scoring at H = 4096, V = 151936;
@@ -164,6 +167,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
+    ap.add_argument("--counters", action="store_true",
+                    help="only launch what the HBM counter runs read: a 512 MiB device copy "
+                         "(calibration) and the greedy top-2 call at batch 1 and 512")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -181,6 +187,10 @@ def main():
 
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    if args.counters:
+        counters_run(torch, lmhead, synth, dev)
+        return
 
     wl = synth.WORKLOADS["tinyllama"]
     H, V = wl.H, wl.V
@@ -235,7 +245,8 @@ def main():
     rf = dict(dom["roofline"])
     traffic = traffic_from_profile(f"greedy_tinyllama_b{dom['batch']}")
     rf["traffic"] = traffic
-    rf["kernel"] = f"greedy top-2, batch {dom['batch']}"
+    rf["kernel"] = (f"one greedy top-2 call at batch {dom['batch']} "
+                    f"({'tile kernel with fused fold' if dom['batch'] <= 32 else 'tile kernel + merge kernel'})")
 
     out = {
         "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1,
@@ -260,6 +271,32 @@ def main():
         log(f"cpu oracle: {out['cpu_baseline']['value']:.1f} rows/s on "
             f"{out['cpu_baseline']['cores']} threads")
     print(json.dumps(out), flush=True)
+
+
+def counters_run(torch, lmhead, synth, dev):
+    """Launch sequence for the rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE):
+    3 copies of 512 MiB (read 512 MiB + write 512 MiB each: the calibration),
+    then 5 greedy top-2 calls at batch 512 and 5 at batch 1 (H=2048, V=32000,
+    four rotating W copies)."""
+    src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    d = synth.make_inputs("tinyllama")
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x = bf16(d["x"])
+    w = [bf16(d["w"]) for _ in range(NCOPIES)]
+    for B in (512, 1):
+        c = Caller(torch, lmhead, [x[:B].contiguous()] * NCOPIES, w, B, 2048, 32000)
+        for _ in range(5):
+            c()
+        torch.cuda.synchronize()
+    log("counter launches done")
 
 
 def extras(torch, lmhead, synth, bf16, x, w_copies, d):
