@@ -37,6 +37,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "lmhead_internal.h"
 
 namespace lmh {
@@ -111,19 +113,27 @@ template <int P, class V> __device__ __forceinline__ V perm(V x) {
 }
 
 // --------------------------------------------------------------- tiling
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BKB_, int NS_>
+// A workgroup computes a BM x BN tile of logits (BM hidden rows, BN vocabulary
+// rows) with WAVES_M x WAVES_N waves.  The k dimension is staged BKB bytes of
+// every row at a time, in two LDS rings: NSX stages of the X rows (read from
+// L2: every vocabulary tile re-reads them) and NSW > NSX stages of the W rows
+// (streamed from HBM once), so W loads are issued NSW - 1 stages ahead of use.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BKB_, int NSX_, int NSW_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-  static constexpr int BKB = BKB_, NS = NS_;
+  static constexpr int BKB = BKB_, NSX = NSX_, NSW = NSW_;
   static constexpr int NW = WAVES_M * WAVES_N, NT = NW * 64;
   static constexpr int WM = BM / WAVES_M / 32;  // 32-row MFMA tiles per wave
   static constexpr int WN = BN / WAVES_N / 32;  // 32-column MFMA tiles per wave
   static constexpr int STEPS = BKB / 32;        // MFMA k-steps per stage
-  static constexpr int STAGE = (BM + BN) * BKB; // LDS bytes per stage
-  static constexpr int SPANS = STAGE / 1024;    // 1 KB wave loads per stage
-  static constexpr int SPW_MAX = (SPANS + NW - 1) / NW;
-  static constexpr int SPW_MIN = SPANS / NW;
-  static constexpr int LDS = NS * STAGE;
+  static constexpr int XSTAGE = BM * BKB;       // LDS bytes per X stage
+  static constexpr int WSTAGE = BN * BKB;       // LDS bytes per W stage
+  static constexpr int XSPANS = XSTAGE / 1024;  // 1 KB wave loads per X stage
+  static constexpr int WSPANS = WSTAGE / 1024;
+  static constexpr int SPWX_MAX = (XSPANS + NW - 1) / NW, SPWX_MIN = XSPANS / NW;
+  static constexpr int SPWW_MAX = (WSPANS + NW - 1) / NW, SPWW_MIN = WSPANS / NW;
+  static constexpr int WRING = NSX * XSTAGE;    // LDS offset of the W ring
+  static constexpr int LDS = NSX * XSTAGE + NSW * WSTAGE;
   static constexpr int WCOLS = WN * 32;         // vocabulary columns per wave
   static constexpr int TPB = kBlockCols / 32;   // column tiles per block (4)
   // a wave covers BPW whole blocks, or PARTS waves share one block
@@ -131,20 +141,32 @@ struct Tile {
   static constexpr int PARTS = WN >= TPB ? 1 : TPB / WN;
   static constexpr int NTB = WN >= TPB ? TPB : WN;  // column tiles per block in one wave
   static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "tile shape");
-  static_assert(STAGE % 1024 == 0 && (BM * BKB) % 1024 == 0, "1 KB load spans");
+  static_assert(XSTAGE % 1024 == 0 && WSTAGE % 1024 == 0, "1 KB load spans");
   static_assert(BN % kBlockCols == 0 && (WN % TPB == 0 || TPB % WN == 0), "blocks");
   static_assert(BKB == 64 || BKB == 128 || BKB == 256, "stage width");
+  static_assert(NSX >= 2 && NSW > NSX, "ring depths: W loads lead X loads");
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  static_assert(SPW_MIN * (NS - 1) < 64, "vmcnt range");
+  // loads of one wave in flight at once (after a boundary's issue) stay below
+  // the 6-bit vmcnt counter
+  static_assert((NSX - 1) * SPWX_MAX + (NSW - 1) * SPWW_MAX < 64, "vmcnt range");
+  // this wave's loads issued after X stage s by the time stage s is awaited
+  // (steady state; fewer near the last stages)
+  static constexpr int AFTER_MAX = SPWW_MIN + (NSX - 2) * (SPWX_MIN + SPWW_MIN);
   static_assert(STEPS % 2 == 0, "fragment double buffer parity");
   // epilogue exchange areas (one 32-row tile per wave row at a time) fit in LDS
   static_assert(WAVES_M * 32 * WAVES_N * (4 + 32 * 4) <= LDS && BM * WAVES_N * 16 <= LDS,
                 "exchange");
 };
 
-// 16-byte chunk swizzle within a staged row (conflict-free ds_read_b128)
+// 16-byte chunk swizzle within a staged row.  LDS has 64 banks of 4 bytes and
+// serves a ds_read_b128 16 lanes at a time; the fragment reads of 16 lanes touch
+// 16 consecutive rows at one logical chunk, and the swizzle spreads them over all
+// 64 banks (BKB / 4 banks per row: rows that share bank offsets get different
+// chunks).
 template <int BKB> __device__ __forceinline__ int swz(int row) {
-  return BKB >= 128 ? (row & 7) : ((row >> 1) & 3);
+  if constexpr (BKB == 64) return (row >> 2) & 3;
+  else if constexpr (BKB == 128) return (row >> 1) & 7;
+  else return row & 15;
 }
 
 template <int N> __device__ __forceinline__ void wait_vm() {
@@ -152,39 +174,37 @@ template <int N> __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// wait until at most n (0 <= n <= K) of this wave's loads are in flight, n
+// rounded down to a value with its own s_waitcnt (waiting for more is safe)
+template <int K> __device__ __forceinline__ void wait_vm_le(int n) {
+  if constexpr (K <= 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= K) wait_vm<K>();
+    else wait_vm_le<K - 1>(n);
+  }
+}
+
 __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
-// wait until at most `ahead` (<= K) stages of this wave's loads are still in flight
-template <class T, int K> __device__ __forceinline__ void wait_stages(int ahead) {
-  if constexpr (K <= 0) {
-    wait_vm<0>();
-  } else {
-    if (ahead >= K) {
-      wait_vm<K * T::SPW_MIN>();
-    } else {
-      wait_stages<T, K - 1>(ahead);
-    }
-  }
-}
-
-// 16 bytes per lane global -> LDS (global_load_lds_dwordx4): lane i writes LDS
-// bytes [lds + 16 i, +16).  Issued as inline asm so the compiler does not guard
-// every later LDS read with a full vmcnt(0) drain; completion is tracked by the
-// explicit vmcnt waits of the pipeline (wait_stages) instead.  m0 (the copy's LDS
-// base) is saved and restored around it; the s_nop is the one wait state
-// required between an SALU write of m0 and its use.
-__device__ __forceinline__ void dma16(const void *gptr, unsigned lds) {
+// 16 bytes per lane global -> LDS (global_load_lds_dwordx4, scalar base + 32-bit
+// lane offset): lane i writes LDS bytes [lds + 16 i, +16).  Issued as inline asm
+// so the compiler does not guard every later LDS read with a full vmcnt(0)
+// drain; completion is tracked by the pipeline's explicit vmcnt waits instead.
+// m0 (the copy's LDS base) is saved and restored around it; the s_nop is the
+// one wait state required between an SALU write of m0 and its use.
+__device__ __forceinline__ void dma16(unsigned voff, const void *sbase, unsigned lds) {
   unsigned saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(gptr), "s"(lds)
+      : "v"(voff), "s"(sbase), "s"(lds)
       : "memory");
 }
 
@@ -198,72 +218,102 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// ------------------------------------------------------------ top-2 records
-template <class V> struct Top2 {
-  V v1, v2;
-  int i1, i2;
-};
-// (a, ia) ranks above (b, ib): larger value, or equal value and lower id
-template <class V> __device__ __forceinline__ bool better(V a, int ia, V b, int ib) {
-  return (a > b) | ((a == b) & (ia < ib));
-}
-template <class V> __device__ __forceinline__ Top2<V> t2_neutral() {
-  Top2<V> t;
-  t.v1 = t.v2 = lowest_of<V>();
-  t.i1 = t.i2 = INT_MAX;
-  return t;
-}
-// branch-free: every lane runs the same selects
-template <class V> __device__ __forceinline__ void t2_insert(Top2<V> &t, V v, int i) {
-  const bool w1 = better(v, i, t.v1, t.i1);
-  const bool w2 = better(v, i, t.v2, t.i2);
-  const V v2 = w1 ? t.v1 : (w2 ? v : t.v2);
-  const int i2 = w1 ? t.i1 : (w2 ? i : t.i2);
-  t.v1 = w1 ? v : t.v1;
-  t.i1 = w1 ? i : t.i1;
-  t.v2 = v2;
-  t.i2 = i2;
-}
-template <class V> __device__ __forceinline__ Top2<V> t2_merge(const Top2<V> &a, const Top2<V> &b) {
-  const bool bw = better(b.v1, b.i1, a.v1, a.i1);  // b's best is the overall best
-  // runner-up: the loser of the two bests against the winner's own second
-  const V lv = bw ? a.v1 : b.v1;
-  const int li = bw ? a.i1 : b.i1;
-  const V sv = bw ? b.v2 : a.v2;
-  const int si = bw ? b.i2 : a.i2;
-  const bool lw = better(lv, li, sv, si);
-  Top2<V> r;
-  r.v1 = bw ? b.v1 : a.v1;
-  r.i1 = bw ? b.i1 : a.i1;
-  r.v2 = lw ? lv : sv;
-  r.i2 = lw ? li : si;
-  return r;
-}
-template <int P, class V> __device__ __forceinline__ Top2<V> perm(const Top2<V> &t) {
-  Top2<V> o;
-  o.v1 = perm<P>(t.v1); o.i1 = perm_i<P>(t.i1);
-  o.v2 = perm<P>(t.v2); o.i2 = perm_i<P>(t.i2);
-  return o;
-}
-template <class V> __device__ __forceinline__ Top2<V> pick(bool c, const Top2<V> &a, const Top2<V> &b) {
-  Top2<V> r;
-  r.v1 = c ? a.v1 : b.v1; r.i1 = c ? a.i1 : b.i1;
-  r.v2 = c ? a.v2 : b.v2; r.i2 = c ? a.i2 : b.i2;
-  return r;
-}
-template <class V> __device__ __forceinline__ uint4 t2_pack(const Top2<V> &t) {
-  return make_uint4((unsigned)vbits(t.v1), (unsigned)t.i1, (unsigned)vbits(t.v2), (unsigned)t.i2);
-}
-template <class V> __device__ __forceinline__ Top2<V> t2_unpack(uint4 r) {
-  Top2<V> t;
-  t.v1 = vfrom<V>((int)r.x); t.i1 = (int)r.y;
-  t.v2 = vfrom<V>((int)r.z); t.i2 = (int)r.w;
-  return t;
+// Scheduling hint for one k-step: NR fragment reads (of the next step) spread
+// between NM MFMAs, each read after NM / NR MFMAs.  Only the order of issue
+// changes; every accumulator still sees its MFMAs in k order.
+template <int NR, int NM> __device__ __forceinline__ void interleave_reads() {
+  constexpr int per = NM / NR > 0 ? NM / NR : 1;
+  constexpr int rounds = NR < NM ? NR : NM;
+#pragma unroll
+  for (int i = 0; i < rounds; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, per, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
+  }
+  if constexpr (NM > per * rounds) __builtin_amdgcn_sched_group_barrier(0x008, NM - per * rounds, 0);
+  if constexpr (NR > rounds) __builtin_amdgcn_sched_group_barrier(0x100, NR - rounds, 0);
 }
 
-template <class V> __device__ __forceinline__ uint4 kNeutralTop2() {
-  return make_uint4((unsigned)vbits(lowest_of<V>()), (unsigned)INT_MAX,
-                    (unsigned)vbits(lowest_of<V>()), (unsigned)INT_MAX);
+// ------------------------------------------------------------ top-2 records
+// A candidate is ranked by one 64-bit key: an order-preserving 32-bit image of
+// its logit in the high half and the complement of its token id in the low
+// half, so a larger key is a larger logit, or an equal logit with a lower id
+// (the lowest-id tie rule).  Key 0 ranks below every real candidate.
+__device__ __forceinline__ unsigned okey(float z) {
+  const unsigned u = __float_as_uint(z + 0.0f);  // -0 and +0 compare equal: one key
+  return u ^ ((unsigned)((int)u >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ unsigned okey(int z) { return (unsigned)z ^ 0x80000000u; }
+template <class V> __device__ __forceinline__ V okey_value(unsigned k);
+template <> __device__ __forceinline__ float okey_value<float>(unsigned k) {
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+template <> __device__ __forceinline__ int okey_value<int>(unsigned k) {
+  return (int)(k ^ 0x80000000u);
+}
+__device__ __forceinline__ uint64_t rank_key(unsigned vk, int id) {
+  return ((uint64_t)vk << 32) | (unsigned)~id;
+}
+__device__ __forceinline__ int key_id(uint64_t k) { return (int)~(unsigned)k; }
+
+struct Top2 {
+  uint64_t k1, k2;  // k1 > k2
+};
+__device__ __forceinline__ Top2 t2_merge(const Top2 &a, const Top2 &b) {
+  const bool bw = b.k1 > a.k1;  // b's best is the overall best
+  // runner-up: the loser of the two bests against the winner's own second
+  const uint64_t l = bw ? a.k1 : b.k1;
+  const uint64_t s = bw ? b.k2 : a.k2;
+  Top2 r;
+  r.k1 = bw ? b.k1 : a.k1;
+  r.k2 = l > s ? l : s;
+  return r;
+}
+template <int P> __device__ __forceinline__ uint64_t perm64(uint64_t x) {
+  const unsigned lo = (unsigned)perm_i<P>((int)(unsigned)x);
+  const unsigned hi = (unsigned)perm_i<P>((int)(unsigned)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+template <int P> __device__ __forceinline__ Top2 perm(const Top2 &t) {
+  return Top2{perm64<P>(t.k1), perm64<P>(t.k2)};
+}
+__device__ __forceinline__ Top2 pick(bool c, const Top2 &a, const Top2 &b) {
+  return Top2{c ? a.k1 : b.k1, c ? a.k2 : b.k2};
+}
+__device__ __forceinline__ uint4 t2_pack(const Top2 &t) {
+  return make_uint4((unsigned)t.k1, (unsigned)(t.k1 >> 32), (unsigned)t.k2, (unsigned)(t.k2 >> 32));
+}
+__device__ __forceinline__ Top2 t2_unpack(uint4 r) {
+  return Top2{((uint64_t)r.y << 32) | r.x, ((uint64_t)r.w << 32) | r.z};
+}
+
+// Top-2 of the NTB (1, 2 or 4) logits z[0..NTB) a lane holds for one row, whose
+// token ids increase with the index (ties go to the lower index), as keys.
+// cbase = ~(id of z[0]); ids step by 32.
+template <int NTB, class V>
+__device__ __forceinline__ Top2 lane_top2(const V (&z)[NTB], unsigned cbase) {
+  auto key = [&](V v, int i) { return ((uint64_t)okey(v) << 32) | (cbase - 32u * (unsigned)i); };
+  if constexpr (NTB == 1) {
+    return Top2{key(z[0], 0), 0};
+  } else if constexpr (NTB == 2) {
+    const bool c = z[0] >= z[1];
+    return Top2{key(c ? z[0] : z[1], c ? 0 : 1), key(c ? z[1] : z[0], c ? 1 : 0)};
+  } else {
+    static_assert(NTB == 4, "column tiles per block");
+    const bool c01 = z[0] >= z[1], c23 = z[2] >= z[3];
+    const V a = c01 ? z[0] : z[1], b = c01 ? z[1] : z[0];
+    const int ia = c01 ? 0 : 1, ib = c01 ? 1 : 0;
+    const V c = c23 ? z[2] : z[3], d = c23 ? z[3] : z[2];
+    const int ic = c23 ? 2 : 3, id = c23 ? 3 : 2;
+    const bool cac = a >= c;  // a has the lower id
+    const V t1 = cac ? a : c;
+    const int i1 = cac ? ia : ic;
+    // runner-up: the loser of (a, c) against the winner's partner; the candidate
+    // from columns 0..1 has the lower id
+    const V pv = cac ? b : a, qv = cac ? c : d;
+    const int ip = cac ? ib : ia, iq = cac ? ic : id;
+    const bool cpq = pv >= qv;
+    return Top2{key(t1, i1), key(cpq ? pv : qv, cpq ? ip : iq)};
+  }
 }
 
 // softmax partial carried through the lane tree: the block max (identical on
@@ -273,9 +323,7 @@ struct Lse {
   float s;
 };
 
-template <class V> __device__ __forceinline__ Top2<V> combine(const Top2<V> &a, const Top2<V> &b) {
-  return t2_merge(a, b);
-}
+__device__ __forceinline__ Top2 combine(const Top2 &a, const Top2 &b) { return t2_merge(a, b); }
 __device__ __forceinline__ Lse combine(const Lse &a, const Lse &b) { return Lse{a.m, a.s + b.s}; }
 template <int P> __device__ __forceinline__ Lse perm(const Lse &x) { return Lse{x.m, perm<P>(x.s)}; }
 __device__ __forceinline__ Lse pick(bool c, const Lse &a, const Lse &b) {
@@ -341,41 +389,43 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
     const int row = row0 + g;
     const uint4 *rec = p.records + (int64_t)row * nb;
     if constexpr (EPI == kTop2) {
-      Top2<val_t> t = t2_neutral<val_t>();
+      Top2 t{0, 0};
       // 16 records per slot in flight per round (one memory latency per round)
       for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
+        // every load is issued (a clamped index stays in bounds), so all 16 are
+        // in flight at once; blocks past the row's end are replaced afterwards
         uint4 r[kChunk];
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q) {
-          const int b = b0 + q * kSlots;
-          r[q] = b < nb ? rec[b] : kNeutralTop2<val_t>();
-        }
+        for (int q = 0; q < kChunk; ++q) r[q] = rec[min(b0 + q * kSlots, nb - 1)];
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q) t = t2_merge(t, t2_unpack<val_t>(r[q]));
+        for (int q = 0; q < kChunk; ++q)
+          if (b0 + q * kSlots < nb) t = t2_merge(t, t2_unpack(r[q]));
       }
       t = t2_merge(t, perm<kQuadX1>(t));
       t = t2_merge(t, perm<kQuadX2>(t));
       t = t2_merge(t, perm<kHalfMirror>(t));
       t = t2_merge(t, perm<kMirror>(t));
       if (slot == 0) {
-        p.top_id[2 * row] = t.i1;
-        p.top_id[2 * row + 1] = t.i2;
+        const val_t v1 = okey_value<val_t>((unsigned)(t.k1 >> 32));
+        const val_t v2 = okey_value<val_t>((unsigned)(t.k2 >> 32));
+        p.top_id[2 * row] = key_id(t.k1);
+        p.top_id[2 * row + 1] = key_id(t.k2);
         if constexpr (MODE == 0) {
-          p.top_val[2 * row] = t.v1;
-          p.top_val[2 * row + 1] = t.v2;
-          p.margin[row] = t.v1 - t.v2;
+          p.top_val[2 * row] = v1;
+          p.top_val[2 * row + 1] = v2;
+          p.margin[row] = v1 - v2;
         } else {
           const float s = p.scale ? p.scale[row] : 1.0f;
           if (p.top_raw) {
-            p.top_raw[2 * row] = t.v1;
-            p.top_raw[2 * row + 1] = t.v2;
+            p.top_raw[2 * row] = v1;
+            p.top_raw[2 * row + 1] = v2;
           }
           const bool ok = scale_ok(s);
           const float nan = __builtin_nanf("");
           // one rounding of an exact float64 product (|raw| < 2^31, 24-bit scale)
-          p.top_val[2 * row] = ok ? (float)((double)t.v1 * (double)s) : nan;
-          p.top_val[2 * row + 1] = ok ? (float)((double)t.v2 * (double)s) : nan;
-          p.margin[row] = ok ? (float)((double)(t.v1 - t.v2) * (double)s) : nan;
+          p.top_val[2 * row] = ok ? (float)((double)v1 * (double)s) : nan;
+          p.top_val[2 * row + 1] = ok ? (float)((double)v2 * (double)s) : nan;
+          p.margin[row] = ok ? (float)((double)(v1 - v2) * (double)s) : nan;
         }
       }
     } else {
@@ -384,13 +434,10 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
       for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
         int m[kChunk];
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q) {
-          const int b = b0 + q * kSlots;
-          m[q] = b < nb ? (int)rec[b].x : vbits(lowest_of<val_t>());
-        }
+        for (int q = 0; q < kChunk; ++q) m[q] = (int)rec[min(b0 + q * kSlots, nb - 1)].x;
 #pragma unroll
         for (int q = 0; q < kChunk; ++q) {
-          const val_t o = vfrom<val_t>(m[q]);
+          const val_t o = vfrom<val_t>(m[q]);  // a repeated last block cannot change a max
           mx = o > mx ? o : mx;
         }
       }
@@ -408,10 +455,7 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
       for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
         uint2 r[kChunk];
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q) {
-          const int b = b0 + q * kSlots;
-          r[q] = b < nb ? *(const uint2 *)&rec[b] : make_uint2(0u, 0u);
-        }
+        for (int q = 0; q < kChunk; ++q) r[q] = *(const uint2 *)&rec[min(b0 + q * kSlots, nb - 1)];
 #pragma unroll
         for (int q = 0; q < kChunk; ++q) {
           if (b0 + q * kSlots < nb) {
@@ -475,34 +519,43 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   }
   const int m0 = tm * T::BM, n0 = tn * T::BN;
 
-  // ---- per-lane source of each 1 KB LDS span this wave fills every stage
-  const char *src[T::SPW_MAX];
-#pragma unroll
-  for (int i = 0; i < T::SPW_MAX; ++i) {
-    int span = wave + i * T::NW;
-    if (span >= T::SPANS) span = T::SPANS - 1;
-    int off = span * 1024 + lane * 16;
-    const char *base;
-    int r0, rmax;
-    if (off < T::BM * T::BKB) {
-      base = p.x; r0 = m0; rmax = p.B - 1;
-    } else {
-      off -= T::BM * T::BKB;
-      base = p.w; r0 = n0; rmax = p.V - 1;
-    }
+  // ---- per-lane 32-bit source offset (from the tile's first row) of each 1 KB
+  // LDS span this wave fills every stage; rows past B / V re-read the last row
+  // (their results are masked in the epilogue)
+  const char *xtile = p.x + (int64_t)m0 * p.rowbytes;
+  const char *wtile = p.w + (int64_t)n0 * p.rowbytes;
+  auto span_offset = [&](int span, int first, int last) -> unsigned {
+    const int off = span * 1024 + lane * 16;
     const int row = off / T::BKB;
     const int chunk = ((off % T::BKB) >> 4) ^ swz<T::BKB>(row);
-    const int r = min(r0 + row, rmax);  // rows past B / V re-read the last row; masked later
-    src[i] = base + (int64_t)r * p.rowbytes + chunk * 16;
-  }
-  auto issue = [&](int stage, int buf) {
-    char *dst = smem + buf * T::STAGE;
+    return (unsigned)(min(first + row, last) - first) * (unsigned)p.rowbytes + 16u * chunk;
+  };
+  unsigned xoff[T::SPWX_MAX], woff[T::SPWW_MAX];
 #pragma unroll
-    for (int i = 0; i < T::SPW_MAX; ++i) {
+  for (int i = 0; i < T::SPWX_MAX; ++i)
+    xoff[i] = span_offset(min(wave + i * T::NW, T::XSPANS - 1), m0, p.B - 1);
+#pragma unroll
+  for (int i = 0; i < T::SPWW_MAX; ++i)
+    woff[i] = span_offset(min(wave + i * T::NW, T::WSPANS - 1), n0, p.V - 1);
+  const unsigned lds0 = lds_addr(smem);
+  auto issue_x = [&](int stage, int buf) {
+    const char *base = xtile + (int64_t)stage * T::BKB;
+#pragma unroll
+    for (int i = 0; i < T::SPWX_MAX; ++i) {
       const int span = wave + i * T::NW;
-      if (T::SPANS % T::NW == 0 || span < T::SPANS)
-        dma16(src[i] + (int64_t)stage * T::BKB,
-              __builtin_amdgcn_readfirstlane(lds_addr(dst + span * 1024)));
+      if (T::XSPANS % T::NW == 0 || span < T::XSPANS)
+        dma16(xoff[i], base,
+              __builtin_amdgcn_readfirstlane(lds0 + buf * T::XSTAGE + span * 1024));
+    }
+  };
+  auto issue_w = [&](int stage, int buf) {
+    const char *base = wtile + (int64_t)stage * T::BKB;
+#pragma unroll
+    for (int i = 0; i < T::SPWW_MAX; ++i) {
+      const int span = wave + i * T::NW;
+      if (T::WSPANS % T::NW == 0 || span < T::WSPANS)
+        dma16(woff[i], base,
+              __builtin_amdgcn_readfirstlane(lds0 + T::WRING + buf * T::WSTAGE + span * 1024));
     }
   };
 
@@ -513,7 +566,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   for (int s = 0; s < T::STEPS; ++s) {
     const int c = (2 * s + h) ^ swz<T::BKB>(j);
     a_off[s] = (wm * T::WM * 32 + j) * T::BKB + 16 * c;
-    b_off[s] = T::BM * T::BKB + (wn * T::WN * 32 + j) * T::BKB + 16 * c;
+    b_off[s] = (wn * T::WN * 32 + j) * T::BKB + 16 * c;
   }
 
   acc_t acc[T::WM][T::WN];
@@ -524,49 +577,100 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mt][nt][v] = 0;
 
-  // ---- main loop: k ascending, one MFMA chain per logit.  All NS buffers are
-  // filled up front; k-step fragments are double-buffered in registers (step
-  // s + 1 is read while step s multiplies); at the end of a stage every wave
-  // waits for the next stage, the barrier frees the finished buffer for stage
-  // t + NS, and the next stage's first fragments are read before the stage's
-  // last MFMAs issue.
-  auto read_frags = [&](const char *buf, int s, i32x4 (&af)[T::WM], i32x4 (&bfr)[T::WN]) {
+  // ---- main loop: k ascending, one MFMA chain per logit.
+  // Loads: boundary b (after stage b; boundaries -NSW..-1 before the loop)
+  // loads, in this order, X stage b + NSX into X buffer b mod NSX and W stage
+  // b + NSW into W buffer b mod NSW.  In the loop the X loads are issued at the
+  // boundary and the W loads are spread over the next stage's k-steps, so the
+  // address unit is not handed a whole stage at once.  Stage s is awaited at
+  // boundary s - 1, before that boundary's loads: loads complete in issue order
+  // and W stage s was issued before X stage s (NSW > NSX), so it suffices that
+  // this wave has at most after(s) loads in flight, the number it issued after
+  // X stage s.
+  // Compute: within a stage, the fragments of k-step s + 1 are read while the
+  // MFMAs of step s issue (one read per MFMA, so LDS latency hides behind the
+  // matrix pipe); after the stage's last MFMAs every wave waits for stage t + 1,
+  // the barrier frees stage t's buffers, boundary t's X loads are issued and the
+  // next stage's first fragments are read.
+  auto read_frags = [&](const char *xb, const char *wb, int s, i32x4 (&af)[T::WM],
+                        i32x4 (&bfr)[T::WN]) {
 #pragma unroll
     for (int mt = 0; mt < T::WM; ++mt)
-      af[mt] = *(const i32x4 *)(buf + a_off[s] + mt * 32 * T::BKB);
+      af[mt] = *(const i32x4 *)(xb + a_off[s] + mt * 32 * T::BKB);
 #pragma unroll
     for (int nt = 0; nt < T::WN; ++nt)
-      bfr[nt] = *(const i32x4 *)(buf + b_off[s] + nt * 32 * T::BKB);
+      bfr[nt] = *(const i32x4 *)(wb + b_off[s] + nt * 32 * T::BKB);
+  };
+  auto mfmas = [&](const i32x4 (&af)[T::WM], const i32x4 (&bfr)[T::WN]) {
+#pragma unroll
+    for (int mt = 0; mt < T::WM; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < T::WN; ++nt) acc[mt][nt] = A::mfma(af[mt], bfr[nt], acc[mt][nt]);
   };
   const int nst = (int)(p.rowbytes / T::BKB);
+  auto boundary = [&](int b) {  // b >= -NSW; buffers of stages b + NSX, b + NSW
+    const int sx = b + T::NSX, sw = b + T::NSW;
+    if (sx >= 0 && sx < nst) issue_x(sx, sx % T::NSX);
+    if (sw < nst) issue_w(sw, sw % T::NSW);
+  };
+  // loads this wave issued after X stage s, once boundaries <= s - 2 are issued
+  auto after = [&](int s) {
+    int n = s - T::NSX + T::NSW < nst ? T::SPWW_MIN : 0;
+    const int lo = s - T::NSX + 1, hi = s - 2;  // whole boundaries after X stage s
+    n += T::SPWX_MIN * max(0, min(hi, nst - 1 - T::NSX) - lo + 1);
+    n += T::SPWW_MIN * max(0, min(hi, nst - 1 - T::NSW) - lo + 1);
+    return n;
+  };
 #pragma unroll
-  for (int s = 0; s < T::NS; ++s)
-    if (s < nst) issue(s, s);
-  wait_stages<T, T::NS - 1>(min(T::NS - 1, nst - 1));  // stage 0 has landed
+  for (int b = -T::NSW; b <= -2; ++b) boundary(b);
+  wait_vm_le<T::AFTER_MAX>(after(0));  // stage 0 has landed
   lds_barrier();
+  boundary(-1);
   i32x4 fa[2][T::WM], fb[2][T::WN];
-  read_frags(smem, 0, fa[0], fb[0]);
-  for (int t = 0; t < nst; ++t) {
-    const char *buf = smem + (t % T::NS) * T::STAGE;
+  read_frags(smem, smem + T::WRING, 0, fa[0], fb[0]);
+  // W spans of one boundary, PER of them after each of the first k-steps
+  constexpr int PER = (T::SPWW_MAX + T::STEPS - 2) / (T::STEPS - 1);
+  auto issue_w_part = [&](int stage, int buf, int i0) {
+    const char *base = wtile + (int64_t)stage * T::BKB;
 #pragma unroll
-    for (int s = 0; s < T::STEPS; ++s) {
-      const int cur = s & 1;  // STEPS is even, so the parity carries across stages
-      if (s + 1 < T::STEPS) {
-        read_frags(buf, s + 1, fa[cur ^ 1], fb[cur ^ 1]);
-      } else if (t + 1 < nst) {
-        wait_lgkm0();                                        // this wave's reads of stage t
-        wait_stages<T, T::NS - 2>(min(T::NS - 2, nst - 2 - t));  // stage t + 1 has landed
-        lds_barrier();
-        if (t + T::NS < nst) issue(t + T::NS, t % T::NS);
-        read_frags(smem + ((t + 1) % T::NS) * T::STAGE, 0, fa[cur ^ 1], fb[cur ^ 1]);
-      }
-#pragma unroll
-      for (int mt = 0; mt < T::WM; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < T::WN; ++nt)
-          acc[mt][nt] = A::mfma(fa[cur][mt], fb[cur][nt], acc[mt][nt]);
+    for (int q = 0; q < PER; ++q) {
+      const int i = i0 + q;
+      const int span = wave + i * T::NW;
+      if (i < T::SPWW_MAX && (T::WSPANS % T::NW == 0 || span < T::WSPANS))
+        dma16(woff[i < T::SPWW_MAX ? i : 0], base,
+              __builtin_amdgcn_readfirstlane(lds0 + T::WRING + buf * T::WSTAGE + span * 1024));
     }
-  }
+  };
+  // one stage; PEND: this stage carries the W loads of boundary t - 1
+  auto stage = [&](int t, auto pend) {
+    const int pw = t - 1 + T::NSW;
+    const char *xb = smem + (t % T::NSX) * T::XSTAGE;
+    const char *wb = smem + T::WRING + (t % T::NSW) * T::WSTAGE;
+#pragma unroll
+    for (int s = 0; s + 1 < T::STEPS; ++s) {
+      const int cur = s & 1;
+      read_frags(xb, wb, s + 1, fa[cur ^ 1], fb[cur ^ 1]);
+      if constexpr (decltype(pend)::value) issue_w_part(pw, pw % T::NSW, s * PER);
+      mfmas(fa[cur], fb[cur]);
+      interleave_reads<T::WM + T::WN, T::WM * T::WN>();
+    }
+    constexpr int last = (T::STEPS - 1) & 1;  // STEPS is even: the next stage starts in slot 0
+    mfmas(fa[last], fb[last]);
+    if (t + 1 < nst) {
+      wait_lgkm0();                            // this wave's reads of stage t
+      wait_vm_le<T::AFTER_MAX>(after(t + 1));  // stage t + 1 has landed
+      lds_barrier();
+      if (t + T::NSX < nst) issue_x(t + T::NSX, t % T::NSX);
+      read_frags(smem + ((t + 1) % T::NSX) * T::XSTAGE,
+                 smem + T::WRING + ((t + 1) % T::NSW) * T::WSTAGE, 0, fa[last ^ 1], fb[last ^ 1]);
+    }
+  };
+  // stage 0 follows the whole boundary -1; stages 1 .. nst - NSW carry the W
+  // loads of the boundary before them (W stages NSW .. nst - 1)
+  stage(0, std::false_type{});
+  int t = 1;
+  for (; t <= nst - T::NSW; ++t) stage(t, std::true_type{});
+  for (; t < nst; ++t) stage(t, std::false_type{});
 
   // lane (j, h) of MFMA tile (mt, nt) holds Z[row0 + acc_row(v, h)][col0 + j], v = 0..15
   const int wrow0 = m0 + wm * T::WM * 32;  // first row of this wave
@@ -603,29 +707,27 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
 
     if constexpr (EPI == kTop2) {
       uint4 *xch = (uint4 *)smem;  // [BM rows][WAVES_N] records
+      // ROUND: rank the bf16-rounded logits (the bf16-output head)
+      auto top2_blocks = [&](auto round) {
 #pragma unroll
       for (int mt = 0; mt < T::WM; ++mt) {
         const int lrow = wm * T::WM * 32 + mt * 32 + acc_row(u, h);  // row this lane ends with
 #pragma unroll
         for (int b = 0; b < T::BPW; ++b) {
-          Top2<val_t> t[16];
+          const int col0 = wcol0 + b * T::NTB * 32 + j;  // this lane's first column of the block
+          Top2 t[16];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) t[v] = t2_neutral<val_t>();
+          for (int v = 0; v < 16; ++v) {
+            val_t z[T::NTB];
 #pragma unroll
-          for (int k = 0; k < T::NTB; ++k) {
-            const int nt = b * T::NTB + k;
-            const int col = wcol0 + nt * 32 + j;
-            if (col < p.V) {
-#pragma unroll
-              for (int v = 0; v < 16; ++v) {
-                val_t z = acc[mt][nt][v];
-                if constexpr (MODE == 0)
-                  if (p.round_bf16) z = bf16_round(z);
-                t2_insert(t[v], z, col);
-              }
+            for (int k = 0; k < T::NTB; ++k) {
+              val_t zz = acc[mt][b * T::NTB + k][v];
+              if constexpr (MODE == 0 && decltype(round)::value) zz = bf16_round(zz);
+              z[k] = col0 + 32 * k < p.V ? zz : lowest_of<val_t>();
             }
+            t[v] = lane_top2<T::NTB>(z, ~(unsigned)col0);
           }
-          const Top2<val_t> r = reduce_scatter(t, j);
+          const Top2 r = reduce_scatter(t, j);
           if constexpr (T::PARTS == 1) {
             const int row = m0 + lrow;
             const int blk = wcol0 / kBlockCols + b;
@@ -636,15 +738,18 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
           }
         }
       }
+      };
+      if (MODE == 0 && p.round_bf16) top2_blocks(std::true_type{});
+      else top2_blocks(std::false_type{});
       if constexpr (T::PARTS > 1) {
         __syncthreads();
         if (wn % T::PARTS == 0 && lane < T::WM * 32) {
           const int lrow = wm * T::WM * 32 + lane;
           const int row = m0 + lrow;
-          Top2<val_t> t = t2_unpack<val_t>(xch[lrow * T::WAVES_N + wn]);
+          Top2 t = t2_unpack(xch[lrow * T::WAVES_N + wn]);
 #pragma unroll
           for (int pp = 1; pp < T::PARTS; ++pp)
-            t = t2_merge(t, t2_unpack<val_t>(xch[lrow * T::WAVES_N + wn + pp]));
+            t = t2_merge(t, t2_unpack(xch[lrow * T::WAVES_N + wn + pp]));
           const int blk = wcol0 / kBlockCols;
           if (row < p.B && blk < p.nblocks) p.records[(int64_t)row * p.nblocks + blk] = t2_pack(t);
         }
@@ -808,20 +913,22 @@ __global__ void reverse_rows_kernel(const char *src, char *dst, int64_t rows, in
 
 // ------------------------------------------------------------ dispatch
 // tile shapes, indexed by Plan::variant
-//   0: 32 x 128 (batch <= 32, fold fused)   1: 64 x 128 (<= 64)
-//   2: 128 x 128 (<= 256)                   3: 256 x 256 (> 256)
+//   0: 32 x 128  (batch <= 32, fold fused)   1: 64 x 128  (<= 64)
+//   2: 128 x 128 (<= 128)                    3: 256 x 128 (<= 256)
+//   4: 256 x 256 (> 256)
+#ifndef LMH_V4_TILE
+#define LMH_V4_TILE 256, 256, 4, 2, 128, 2, 3
+#endif
 #ifndef LMH_V3_TILE
-#define LMH_V3_TILE 256, 256, 4, 2, 128, 2
+#define LMH_V3_TILE 256, 128, 4, 2, BKB, 2, 4
 #endif
-#ifndef LMH_V2_TILE
-#define LMH_V2_TILE 128, 128, 2, 2, BKB, 4
-#endif
-template <int BKB> using V0 = Tile<32, 128, 1, 4, BKB, 3>;
-template <int BKB> using V1 = Tile<64, 128, 2, 2, BKB, 3>;
-template <int BKB> using V2 = Tile<LMH_V2_TILE>;
-using V3 = Tile<LMH_V3_TILE>;
-// V3 when the row is not a whole number of its stages
-using V3s = Tile<256, 256, 2, 2, 64, 4>;
+template <int BKB> using V0 = Tile<32, 128, 1, 4, BKB, 2, 4>;
+template <int BKB> using V1 = Tile<64, 128, 2, 2, BKB, 2, 3>;
+template <int BKB> using V2 = Tile<128, 128, 2, 2, BKB, 2, 4>;
+template <int BKB> using V3 = Tile<LMH_V3_TILE>;
+using V4 = Tile<LMH_V4_TILE>;
+// V4 when the row is not a whole number of its stages
+using V4s = Tile<256, 256, 4, 2, 64, 2, 6>;
 
 template <class T, int MODE, bool FUSED>
 hipError_t launch_tile(int epi, const Params &p, hipStream_t s) {
@@ -863,9 +970,12 @@ hipError_t launch_mode(int epi, const Plan &plan, const Params &p, hipStream_t s
     case 2:
       if (plan.bkb == 128) return launch_tile<V2<128>, MODE, false>(epi, p, s);
       return launch_tile<V2<64>, MODE, false>(epi, p, s);
+    case 3:
+      if (plan.bkb == 128) return launch_tile<V3<128>, MODE, false>(epi, p, s);
+      return launch_tile<V3<64>, MODE, false>(epi, p, s);
     default:
-      if (plan.bkb == V3::BKB) return launch_tile<V3, MODE, false>(epi, p, s);
-      return launch_tile<V3s, MODE, false>(epi, p, s);
+      if (plan.bkb == V4::BKB) return launch_tile<V4, MODE, false>(epi, p, s);
+      return launch_tile<V4s, MODE, false>(epi, p, s);
   }
 }
 
@@ -879,12 +989,14 @@ Plan plan_for(int64_t B, int64_t rowbytes, int64_t V) {
     pl.variant = 0; pl.bm = 32; pl.bn = 128; pl.bkb = bkb256;
   } else if (B <= 64) {
     pl.variant = 1; pl.bm = 64; pl.bn = 128; pl.bkb = bkb256;
+  } else if (B <= 128) {
+    pl.variant = 2; pl.bm = 128; pl.bn = 128; pl.bkb = bkb128;
   } else if (B <= 256) {
-    pl.variant = 2; pl.bm = V2<128>::BM; pl.bn = V2<128>::BN; pl.bkb = bkb128;
-  } else if (rowbytes % V3::BKB == 0) {
-    pl.variant = 3; pl.bm = V3::BM; pl.bn = V3::BN; pl.bkb = V3::BKB;
+    pl.variant = 3; pl.bm = V3<128>::BM; pl.bn = V3<128>::BN; pl.bkb = bkb128;
+  } else if (rowbytes % V4::BKB == 0) {
+    pl.variant = 4; pl.bm = V4::BM; pl.bn = V4::BN; pl.bkb = V4::BKB;
   } else {
-    pl.variant = 3; pl.bm = V3s::BM; pl.bn = V3s::BN; pl.bkb = V3s::BKB;
+    pl.variant = 4; pl.bm = V4s::BM; pl.bn = V4s::BN; pl.bkb = V4s::BKB;
   }
   pl.grid_m = (int)((B + pl.bm - 1) / pl.bm);
   pl.grid_n = (int)((V + pl.bn - 1) / pl.bn);
