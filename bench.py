@@ -66,7 +66,7 @@ class Caller:
     launch well under the kernel time; torch allocates nothing in the loop)."""
 
     def __init__(self, torch, lmhead, x_list, w_list, B, H, V, mode=0, kind="greedy",
-                 target=None, scale=None):
+                 target=None, scale=None, round_bf16=0, tau=0.0):
         self.torch = torch
         lib = lmhead.library()
         dev = x_list[0].device
@@ -83,8 +83,18 @@ class Caller:
             self.keep = (ids, vals, margin, raw)
             for xx, ww in zip(x_list, w_list):
                 self.calls.append((lib.lmhead_greedy_top2, (
-                    mode, 0, P(xx), P(ww), B, H, V, P(scale), P(ids), P(vals), P(margin), P(raw),
-                    P(self.ws), ws_bytes, self.stream)))
+                    mode, round_bf16, P(xx), P(ww), B, H, V, P(scale), P(ids), P(vals), P(margin),
+                    P(raw), P(self.ws), ws_bytes, self.stream)))
+        elif kind == "gated":
+            ids = torch.empty((B, 2), dtype=torch.int32, device=dev)
+            vals = torch.empty((B, 2), dtype=torch.float32, device=dev)
+            margin = torch.empty((B,), dtype=torch.float32, device=dev)
+            gated = torch.empty((B,), dtype=torch.int32, device=dev)
+            self.keep = (ids, vals, margin, gated)
+            for xx, ww in zip(x_list, w_list):
+                self.calls.append((lib.lmhead_greedy_gated, (
+                    mode, P(xx), P(ww), B, H, V, ctypes.c_float(tau), P(ids), P(vals), P(margin),
+                    P(gated), P(self.ws), ws_bytes, self.stream)))
         elif kind == "logprob":
             out = torch.empty((B,), dtype=torch.float32, device=dev)
             self.keep = (out,)
@@ -318,6 +328,18 @@ def extras(torch, lmhead, synth, bf16, x, w_copies, d):
         f"{res['tinyllama_logprob_b512']['us_per_call']:.1f} / "
         f"{res['tinyllama_logits_b512']['us_per_call']:.1f} us")
 
+    # margin-gated float32 recompute (tau = 1e-3) against the plain bf16-output head
+    for B in (1, 512):
+        xb = [x[:B].contiguous()] * NCOPIES
+        plain = Caller(torch, lmhead, xb, w_copies, B, H, V, round_bf16=1)
+        gated = Caller(torch, lmhead, xb, w_copies, B, H, V, kind="gated", tau=1e-3)
+        tp, tg = time_calls(torch, plain, 100), time_calls(torch, gated, 100)
+        rate = float(gated.keep[3].float().mean().item())
+        res[f"gated_tau1e-3_b{B}"] = {"us_per_call": tg * 1e6, "us_bf16_head": tp * 1e6,
+                                       "overhead": tg / tp - 1.0, "gate_rate": rate}
+        log(f"gated B={B}: {tg * 1e6:.1f} us vs bf16 head {tp * 1e6:.1f} us "
+            f"({100 * (tg / tp - 1):+.1f}%), gate rate {100 * rate:.2f}%")
+
     # near-tie stress, 4096 rows
     nt = synth.make_inputs("neartie")
     xn, wn = bf16(nt["x"]), bf16(nt["w"])
@@ -325,6 +347,10 @@ def extras(torch, lmhead, synth, bf16, x, w_copies, d):
     tt = time_calls(torch, c, 30)
     res["neartie_4096"] = {"us_per_call": tt * 1e6, "rows_per_s": 4096 / tt,
                            "roofline": roofline(4096, H, V, tt)}
+    c = Caller(torch, lmhead, [xn], [wn], 4096, H, V, kind="gated", tau=1e-3)
+    tg = time_calls(torch, c, 30)
+    res["neartie_4096_gated_tau1e-3"] = {"us_per_call": tg * 1e6,
+                                         "gate_rate": float(c.keep[3].float().mean().item())}
     del c, xn, wn, nt
     log(f"near-tie 4096 rows: {tt * 1e6:.1f} us")
 

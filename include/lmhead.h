@@ -59,7 +59,8 @@ typedef enum {
   LMHEAD_E_MODE = 4,      /* unknown mode / rounding, or rounding not valid for the mode */
   LMHEAD_E_OVERFLOW = 5,  /* int8: H * 128^2 could exceed int32 (H > 131071) */
   LMHEAD_E_WORKSPACE = 6, /* workspace NULL or smaller than lmhead_workspace_bytes() */
-  LMHEAD_E_HIP = 7        /* the HIP runtime refused the launch */
+  LMHEAD_E_HIP = 7,       /* the HIP runtime refused the launch */
+  LMHEAD_E_VALUE = 8      /* a scalar argument is out of range (e.g. a NaN or negative tau) */
 } lmhead_status;
 
 typedef enum { LMHEAD_MODE_BF16 = 0, LMHEAD_MODE_INT8 = 1 } lmhead_mode;
@@ -116,6 +117,26 @@ lmhead_status lmhead_greedy_top2(int mode, int round, const void *x, const void 
 lmhead_status lmhead_logprob(int mode, const void *x, const void *w, int64_t B, int64_t H,
                              int64_t V, const float *row_scale, const int32_t *target,
                              float *logprob, void *ws, size_t ws_bytes, void *stream);
+
+/* Margin-gated float32 recompute of the greedy decision ("Greedy Decoding Has
+ * a Precision Clause", section "Correct the vulnerable token decisions, not
+ * every calculation": ordinary inference decides unless the top-2 logit margin
+ * is below a calibrated threshold; such steps recompute the output projection
+ * in FP32, and recomputing the two leading candidates sufficed).  MODE_BF16
+ * only (LMHEAD_E_MODE otherwise).
+ *   1. greedy top-2 of the bf16-output head, exactly as lmhead_greedy_top2 with
+ *      LMHEAD_ROUND_BF16 (ids, bf16-rounded values, margin);
+ *   2. every row whose margin is below tau recomputes the logits of its two
+ *      candidates with the float32 head (bitwise the values lmhead_logits gives
+ *      them: same MFMA instruction and k order) and re-ranks them, lowest id on
+ *      a tie; top_val and margin of that row then hold float32 logits.
+ *   gated[b] = 1 for a recomputed row, 0 otherwise.
+ * tau >= 0 (0 recomputes nothing, +inf every row); NaN or negative tau gives
+ * LMHEAD_E_VALUE.  ws / ws_bytes as for lmhead_greedy_top2. */
+lmhead_status lmhead_greedy_gated(int mode, const void *x, const void *w, int64_t B, int64_t H,
+                                  int64_t V, float tau, int32_t *top_id, float *top_val,
+                                  float *margin, int32_t *gated, void *ws, size_t ws_bytes,
+                                  void *stream);
 
 /* Device self-check of the row property ("12 Exactness", section 12.8: a
  * load-time self-check proves on the device that every row gets the same bits

@@ -149,6 +149,30 @@ lmhead_status lmhead_logprob(int mode, const void *x, const void *w, int64_t B, 
   return launched(lmh::launch(mode, lmh::kLse, plan, p, (hipStream_t)stream));
 }
 
+lmhead_status lmhead_greedy_gated(int mode, const void *x, const void *w, int64_t B, int64_t H,
+                                  int64_t V, float tau, int32_t *top_id, float *top_val,
+                                  float *margin, int32_t *gated, void *ws, size_t ws_bytes,
+                                  void *stream) {
+  lmhead_status st = check_common(mode, LMHEAD_ROUND_BF16, x, w, B, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (!gated) return LMHEAD_E_NULL;
+  if (!aligned4(gated)) return LMHEAD_E_ALIGN;
+  if (!(tau >= 0.0f)) return LMHEAD_E_VALUE;  // NaN or negative
+  st = lmhead_greedy_top2(mode, LMHEAD_ROUND_BF16, x, w, B, H, V, nullptr, top_id, top_val,
+                          margin, nullptr, ws, ws_bytes, stream);
+  if (st != LMHEAD_OK) return st;
+  lmh::GateParams g;
+  g.x = (const char *)x;
+  g.w = (const char *)w;
+  g.rowbytes = row_bytes(mode, H);
+  g.tau = tau;
+  g.top_id = top_id;
+  g.top_val = top_val;
+  g.margin = margin;
+  g.gated = gated;
+  return launched(lmh::launch_gate(g, B, (hipStream_t)stream));
+}
+
 // scratch: [B, V] batch logits | [V] one-row logits | [B, V] reversed-batch logits |
 //          [B, H] reversed rows; every region 256-byte aligned
 static size_t self_check_layout(int mode, int64_t B, int64_t H, int64_t V, size_t off[4]) {
@@ -213,6 +237,7 @@ const char *lmhead_status_string(int status) {
     case LMHEAD_E_OVERFLOW: return "int8 head: H too large for exact int32 accumulation";
     case LMHEAD_E_WORKSPACE: return "workspace missing or too small";
     case LMHEAD_E_HIP: return "HIP launch failed (see lmhead_last_error)";
+    case LMHEAD_E_VALUE: return "a scalar argument is out of range";
     default: return "unknown status";
   }
 }

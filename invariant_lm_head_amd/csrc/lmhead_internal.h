@@ -48,6 +48,18 @@ size_t workspace_layout(int64_t B, int64_t V, size_t *off_zt, size_t *off_record
 
 hipError_t launch(int mode, int epilogue, const Plan &plan, const Params &p, hipStream_t s);
 
+// Margin-gated recompute of the two greedy candidates with the float32 head.
+struct GateParams {
+  const char *x, *w;
+  int64_t rowbytes;
+  float tau;
+  int32_t *top_id;  // [B, 2] in: bf16-head candidates; out: re-ranked
+  float *top_val;   // [B, 2]
+  float *margin;    // [B]
+  int32_t *gated;   // [B]
+};
+hipError_t launch_gate(const GateParams &g, int64_t B, hipStream_t s);
+
 hipError_t launch_compare(const void *a, const void *b, int64_t nwords,
                           unsigned long long *mismatches, hipStream_t s);
 hipError_t launch_reverse_rows(const void *src, void *dst, int64_t rows, int64_t rowbytes,

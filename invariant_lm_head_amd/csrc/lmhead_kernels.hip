@@ -891,6 +891,43 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(Params p) {
   merge_rows<MODE, EPI>(p, row0, min(256 / kSlots, p.B - row0), threadIdx.x, 256);
 }
 
+// ------------------------------------------------------ gated recompute
+// One wave per row.  A row whose bf16-head margin is below tau recomputes the
+// logits of its two candidates with the float32 head: every k-step feeds the
+// row (A, all 32 MFMA rows) and the candidate W rows (B, MFMA column 0 and 1;
+// the other columns repeat candidate 0) to the same MFMA instruction, with the
+// same k order and lane layout as the contraction kernel, so the values equal
+// the float32 head's bit for bit.  The two are then ranked, lowest id on a tie.
+__global__ __launch_bounds__(64) void lmhead_gate_kernel(GateParams g) {
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x, j = lane & 31, h = lane >> 5;
+  const bool gate = g.margin[row] < g.tau;  // the same in every lane
+  if (lane == 0) g.gated[row] = gate ? 1 : 0;
+  if (!gate) return;
+  const int c1 = g.top_id[2 * row], c2 = g.top_id[2 * row + 1];
+  const char *xr = g.x + (int64_t)row * g.rowbytes + 16 * h;
+  const char *wr = g.w + (int64_t)(j == 1 ? c2 : c1) * g.rowbytes + 16 * h;
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  const int nsteps = (int)(g.rowbytes / 32);
+#pragma unroll 8
+  for (int k = 0; k < nsteps; ++k)
+    acc = Arith<0>::mfma(*(const i32x4 *)(xr + 32 * k), *(const i32x4 *)(wr + 32 * k), acc);
+  // MFMA row 0 of column c is value 0 of lane (j = c, h = 0)
+  const float z1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[0]), 0));
+  const float z2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[0]), 1));
+  if (lane == 0) {
+    const bool second = (z2 > z1) | ((z2 == z1) & (c2 < c1));
+    g.top_id[2 * row] = second ? c2 : c1;
+    g.top_id[2 * row + 1] = second ? c1 : c2;
+    const float t1 = second ? z2 : z1, t2 = second ? z1 : z2;
+    g.top_val[2 * row] = t1;
+    g.top_val[2 * row + 1] = t2;
+    g.margin[row] = t1 - t2;
+  }
+}
+
 // ---------------------------------------------------------- small kernels
 __global__ void compare_words_kernel(const unsigned *a, const unsigned *b, int64_t n,
                                      unsigned long long *mismatches) {
@@ -1005,6 +1042,11 @@ Plan plan_for(int64_t B, int64_t rowbytes, int64_t V) {
 
 hipError_t launch(int mode, int epi, const Plan &plan, const Params &p, hipStream_t s) {
   return mode == 0 ? launch_mode<0>(epi, plan, p, s) : launch_mode<1>(epi, plan, p, s);
+}
+
+hipError_t launch_gate(const GateParams &g, int64_t B, hipStream_t s) {
+  hipLaunchKernelGGL(lmhead_gate_kernel, dim3((unsigned)B), dim3(64), 0, s, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_compare(const void *a, const void *b, int64_t nwords,

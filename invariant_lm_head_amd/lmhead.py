@@ -18,7 +18,7 @@ ROUND_F32, ROUND_BF16 = 0, 1
 
 _STATUS = {0: "LMHEAD_OK", 1: "LMHEAD_E_NULL", 2: "LMHEAD_E_SHAPE", 3: "LMHEAD_E_ALIGN",
            4: "LMHEAD_E_MODE", 5: "LMHEAD_E_OVERFLOW", 6: "LMHEAD_E_WORKSPACE",
-           7: "LMHEAD_E_HIP"}
+           7: "LMHEAD_E_HIP", 8: "LMHEAD_E_VALUE"}
 
 # every function the header declares, with its C signature
 _P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -27,6 +27,8 @@ SIGNATURES = {
     "lmhead_logits": ([_I, _I, _P, _P, _I64, _I64, _I64, _P, _P], _I),
     "lmhead_greedy_top2": ([_I, _I, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "lmhead_logprob": ([_I, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _I),
+    "lmhead_greedy_gated": ([_I, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, _P, _P,
+                             _SZ, _P], _I),
     "lmhead_self_check_bytes": ([_I, _I64, _I64, _I64], _SZ),
     "lmhead_self_check": ([_I, _P, _P, _I64, _I64, _I64, _P, _SZ, _P, _P], _I),
     "lmhead_status_string": ([_I], ctypes.c_char_p),
@@ -167,6 +169,28 @@ def logprob(x: torch.Tensor, w: torch.Tensor, target: torch.Tensor,
                                   ws.numel() * ws.element_size(), _stream(dev))
     _check("lmhead_logprob", st)
     return out
+
+
+def greedy_gated(x: torch.Tensor, w: torch.Tensor, tau: float,
+                 ws: torch.Tensor | None = None):
+    """bf16-output greedy top-2 whose rows with margin < tau are re-ranked on
+    their two candidates' float32 logits: ids [B,2] int32, values [B,2] float32,
+    margin [B] float32, gated [B] int32 (1 = recomputed)."""
+    mode = _mode_of(x, w)
+    B, H, V = _dims(x, w)
+    dev = x.device
+    ids = torch.empty((B, 2), dtype=torch.int32, device=dev)
+    vals = torch.empty((B, 2), dtype=torch.float32, device=dev)
+    margin = torch.empty((B,), dtype=torch.float32, device=dev)
+    gated = torch.empty((B,), dtype=torch.int32, device=dev)
+    need = workspace_bytes(mode, B, H, V)
+    if ws is None:
+        ws = workspace(need, dev)
+    st = library().lmhead_greedy_gated(mode, _ptr(x), _ptr(w), B, H, V, float(tau), _ptr(ids),
+                                       _ptr(vals), _ptr(margin), _ptr(gated), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(dev))
+    _check("lmhead_greedy_gated", st)
+    return ids, vals, margin, gated
 
 
 def self_check(x: torch.Tensor, w: torch.Tensor) -> int:

@@ -159,6 +159,28 @@ class Oracle:
         assert rc == 0
         return ids, raw, vals, margin
 
+    # --------------------------------------------------- gated recompute
+    def greedy_gated_bf16(self, x, w, tau: float, nthreads: int | None = None):
+        """The margin-gated head ("Greedy Decoding Has a Precision Clause",
+        section "Correct the vulnerable token decisions, not every calculation").
+
+        The bf16-output head (float64 logits rounded to bf16, lowest id on a
+        tie) decides every row whose top-2 margin is at least tau.  A row whose
+        margin is below tau re-ranks its two candidates on their unrounded
+        float64 logits, lowest id on a tie.  Returns (ids[B,2] int32,
+        vals[B,2] float64, margin[B] float64, gated[B] bool).
+        """
+        x, w = _c(x, np.uint16), _c(w, np.uint16)
+        ids, vals, margin = self.greedy_bf16(x, w, round_bf16=True, nthreads=nthreads)
+        gated = margin < tau
+        for r in np.nonzero(gated)[0]:
+            cand = ids[r].copy()
+            z = self.logits_bf16(x[r:r + 1], w[cand], nthreads=1)[0]
+            if z[1] > z[0] or (z[1] == z[0] and cand[1] < cand[0]):
+                cand, z = cand[::-1], z[::-1]
+            ids[r], vals[r], margin[r] = cand, z, z[0] - z[1]
+        return ids, vals, margin, gated
+
     # ------------------------------------------------------ log-prob
     def logprob_bf16(self, x, w, target, nthreads: int | None = None) -> np.ndarray:
         """log p(target[r]) under softmax of row r's float64 logits (NaN if out of range)."""

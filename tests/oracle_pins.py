@@ -245,6 +245,71 @@ def pin_greedy_near_ties(o):
             assert list(ids16[0]) == [9, 4] and margin16[0] == g
 
 
+def pin_gated_hand_cases(o):
+    """The margin-gated head on the near-tie rows of pin_greedy_near_ties (ids
+    9 and 4 share the logit 6.0; id 9 adds the gap g), one row per gap in one
+    batch.  The bf16-output head ties every gap below half a bf16 ulp of 6.0
+    (margin 0, id 4 first); with tau = 1e-3 those rows are recomputed and the
+    exact float64 logits decide (6 + g against 6, id 4 on g = 0).  The one-ulp
+    gap (1/32 >= tau) keeps the bf16 decision and its rounded values; tau = 0
+    recomputes nothing; tau = 0.05 recomputes the one-ulp row as well."""
+    H, V = 64, 12
+    gaps = [0.0, 2.0 ** -50, 2.0 ** -17, 2.0 ** -14, 2.0 ** -13, 2.0 ** -5]
+    rng = np.random.default_rng(26)
+    x = bf16_const(1.0, (len(gaps), H))
+    # one W per gap: rows are processed independently, so stack the cases as
+    # separate calls over the same x row and check the batch call row by row
+    ws = []
+    for g in gaps:
+        w = rand_bf16(rng, (V, H), emin=-14, emax=-12)
+        w[4] = w[9] = 0
+        w[4, 0] = w[9, 0] = bf16_const(6.0, ()).item()
+        w[9, H - 1] = synth.bf16_from_f32(np.float32(g)).item()
+        ws.append(w)
+    for tau in (0.0, 1e-3, 0.05):
+        for g, w in zip(gaps, ws):
+            ids, vals, margin, gated = o.greedy_gated_bf16(x[:1], w, tau)
+            bf16_tie = g < 2.0 ** -6
+            bf16_margin = 0.0 if bf16_tie else g
+            assert gated[0] == (bf16_margin < tau), (tau, g)
+            if gated[0]:
+                want = [4, 9] if g == 0.0 else [9, 4]
+                assert list(ids[0]) == want and vals[0, 0] == 6.0 + g and vals[0, 1] == 6.0
+                assert margin[0] == g
+            elif bf16_tie:
+                assert list(ids[0]) == [4, 9] and list(vals[0]) == [6.0, 6.0] and margin[0] == 0.0
+            else:
+                assert list(ids[0]) == [9, 4] and margin[0] == g and vals[0, 0] == 6.0 + g
+    # several rows of one call are gated independently: rows 0..2 share one W
+    w = ws[2]                                     # gap 2^-17: a bf16 tie
+    xx = np.concatenate([x[:1], bf16_const(2.0, (1, H)), bf16_const(0.0, (1, H))])
+    ids, vals, margin, gated = o.greedy_gated_bf16(xx, w, 1e-3)
+    assert list(gated) == [True, True, True]     # row 2: every logit is 0 -> margin 0
+    assert list(ids[0]) == [9, 4] and list(ids[1]) == [9, 4] and margin[1] == 2 * 2.0 ** -17
+    assert list(ids[2]) == [0, 1] and margin[2] == 0.0
+
+
+def pin_gated_rerank_bruteforce(o):
+    """tau = inf recomputes every row: the ids are the bf16-output head's two
+    candidates, ranked by their exact rational logits (lowest id on a tie),
+    and the values are those logits (brute force with fractions)."""
+    rng = np.random.default_rng(27)
+    for trial in range(4):
+        B, H, V = 3, 64, 10
+        x = rand_bf16(rng, (B, H), emin=-3, emax=0)
+        w = rand_bf16(rng, (V, H), emin=-3, emax=0)
+        ids16, _, _ = o.greedy_bf16(x, w, round_bf16=True)
+        ids, vals, margin, gated = o.greedy_gated_bf16(x, w, float("inf"))
+        assert gated.all()
+        xf, wf = fracs(synth.bf16_to_f64(x)), fracs(synth.bf16_to_f64(w))
+        for r in range(B):
+            cand = sorted(int(c) for c in ids16[r])
+            z = {c: sum(a * b for a, b in zip(xf[r], wf[c])) for c in cand}
+            order = sorted(cand, key=lambda c: (-z[c], c))
+            assert list(ids[r]) == order, (trial, r)
+            assert vals[r, 0] == float(z[order[0]]) and vals[r, 1] == float(z[order[1]])
+
+
 def pin_int_scaled_values(o):
     """int8 top-2 values and margin are the nearest float32 of the exact
     rational raw * scale; a non-positive scale gives NaN values but valid ids."""
@@ -441,7 +506,8 @@ FAST = [
     pin_logits_bruteforce, pin_logits_one_hot, pin_logits_closed_forms,
     pin_int_logits_bruteforce, pin_int_overflow_bound, pin_top2_bruteforce,
     pin_top2_hand_ties, pin_greedy_identical_rows, pin_greedy_permutation,
-    pin_greedy_near_ties, pin_int_scaled_values, pin_logsoftmax_sums_to_one,
+    pin_greedy_near_ties, pin_gated_hand_cases, pin_gated_rerank_bruteforce,
+    pin_int_scaled_values, pin_logsoftmax_sums_to_one,
     pin_logprob_closed_forms, pin_logprob_shift_invariance, pin_logprob_decimal,
     pin_logprob_out_of_range, pin_round_bf16, pin_pages_float_examples,
 ]

@@ -11,7 +11,7 @@ from invariant_lm_head_amd import _build, lmhead
 
 HEADER = Path(__file__).resolve().parents[1] / "include" / "lmhead.h"
 
-OK, E_NULL, E_SHAPE, E_ALIGN, E_MODE, E_OVERFLOW, E_WORKSPACE, E_HIP = range(8)
+OK, E_NULL, E_SHAPE, E_ALIGN, E_MODE, E_OVERFLOW, E_WORKSPACE, E_HIP, E_VALUE = range(9)
 A = ctypes.c_void_p(0x10000)      # aligned, never dereferenced
 A2 = ctypes.c_void_p(0x20000)
 MIS = ctypes.c_void_p(0x10008)    # 8-byte aligned only
@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(lmhead.SIGNATURES)
@@ -126,6 +126,28 @@ def test_logprob_validation(lib):
     assert call(w=MIS) == E_ALIGN
     assert call(nws=16) == E_WORKSPACE
     assert call(mode=1, H=1 << 18) == E_OVERFLOW
+
+
+def test_gated_validation(lib):
+    ws_need = lib.lmhead_workspace_bytes(0, 4, 64, 1000)
+
+    def call(mode=0, x=A, w=A, B=4, H=64, V=1000, tau=1e-3, ids=A, vals=A, margin=A, gated=A,
+             ws=A2, nws=ws_need):
+        return lib.lmhead_greedy_gated(mode, x, w, B, H, V, tau, ids, vals, margin, gated, ws,
+                                       nws, S)
+
+    assert call(mode=1) == E_MODE              # the float32 recompute is a bf16-mode step
+    assert call(mode=3) == E_MODE
+    assert call(gated=None) == E_NULL
+    assert call(gated=ODD) == E_ALIGN
+    assert call(tau=-1.0) == E_VALUE
+    assert call(tau=float("nan")) == E_VALUE
+    assert call(tau=-0.0, ids=None) == E_NULL  # -0 is a valid tau; the inner call refuses
+    assert call(ids=None) == E_NULL
+    assert call(margin=ODD) == E_ALIGN
+    assert call(nws=ws_need - 1) == E_WORKSPACE
+    assert call(V=1) == E_SHAPE
+    assert lib.lmhead_status_string(E_VALUE) == b"a scalar argument is out of range"
 
 
 def test_self_check_validation(lib):
