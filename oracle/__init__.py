@@ -92,6 +92,10 @@ class Oracle:
             "oracle_logsoftmax_f64": ([P, i64, P], None),
             "oracle_logprob_i64_row": ([P, i64, D, i64], D),
             "oracle_round_bf16": ([D], D),
+            "oracle_philox4x64": ([P, P, P], None),
+            "oracle_gumbel": ([ctypes.c_uint64, i64, i64], D),
+            "oracle_sample_bf16": ([P, P, i64, i64, i64, D, P, P, P, P, P, i32], ctypes.c_int),
+            "oracle_sample_i8": ([P, P, i64, i64, i64, P, D, P, P, P, P, P, i32], ctypes.c_int),
             "oracle_threads": ([i32], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
@@ -180,6 +184,48 @@ class Oracle:
                 cand, z = cand[::-1], z[::-1]
             ids[r], vals[r], margin[r] = cand, z, z[0] - z[1]
         return ids, vals, margin, gated
+
+    # ------------------------------------------------------- sampling
+    def philox4x64(self, ctr, key):
+        """Philox4x64-10 of a 4-word counter under a 2-word key (4 uint64 words)."""
+        c = np.ascontiguousarray(ctr, dtype=np.uint64)
+        k = np.ascontiguousarray(key, dtype=np.uint64)
+        out = np.empty(4, np.uint64)
+        self.lib.oracle_philox4x64(_ptr(c), _ptr(k), _ptr(out))
+        return out
+
+    def gumbel(self, seed: int, position: int, v: int) -> float:
+        """Gumbel noise of token v for the draw keyed by (seed, position)."""
+        return self.lib.oracle_gumbel(int(seed) & (2 ** 64 - 1), int(position), int(v))
+
+    def sample_bf16(self, x, w, temperature: float, seed, position, nthreads: int | None = None):
+        """Seeded Gumbel-max draw of every row ("12 Exactness", section 12.5):
+        token = argmax_v z_v / T + G(seed[r], position[r], v), lowest id on a
+        tie.  Returns (token[B] int32, value[B] float64 (the winning score),
+        gap[B] float64 (its lead over the runner-up))."""
+        x, w = _c(x, np.uint16), _c(w, np.uint16)
+        B, H, V = _shape(x, w)
+        sd, ps = _c(seed, np.uint64), _c(position, np.int64)
+        tok, val, gap = np.empty(B, np.int32), np.empty(B, np.float64), np.empty(B, np.float64)
+        assert self.lib.oracle_sample_bf16(_ptr(x), _ptr(w), B, H, V, float(temperature),
+                                           _ptr(sd), _ptr(ps), _ptr(tok), _ptr(val), _ptr(gap),
+                                           _nt(nthreads)) == 0
+        return tok, val, gap
+
+    def sample_i8(self, x, w, temperature: float, seed, position, scale=None,
+                  nthreads: int | None = None):
+        """As sample_bf16 on the scaled int8 logits raw * scale[r]; a row whose
+        scale is not a positive finite number draws token -1 (value, gap NaN)."""
+        x, w = _c(x, np.int8), _c(w, np.int8)
+        B, H, V = _shape(x, w)
+        sd, ps = _c(seed, np.uint64), _c(position, np.int64)
+        sc = None if scale is None else _c(scale, np.float32)
+        tok, val, gap = np.empty(B, np.int32), np.empty(B, np.float64), np.empty(B, np.float64)
+        assert self.lib.oracle_sample_i8(_ptr(x), _ptr(w), B, H, V,
+                                         None if sc is None else _ptr(sc), float(temperature),
+                                         _ptr(sd), _ptr(ps), _ptr(tok), _ptr(val), _ptr(gap),
+                                         _nt(nthreads)) == 0
+        return tok, val, gap
 
     # ------------------------------------------------------ log-prob
     def logprob_bf16(self, x, w, target, nthreads: int | None = None) -> np.ndarray:

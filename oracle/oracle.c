@@ -34,6 +34,10 @@
  *             with the differences taken exactly: S = sum exp(s_r (z_v - zmax)),
  *             log p(t) = s_r (z_t - zmax) - ln S.
  *
+ *  sampling   seeded Gumbel-max: token = argmax_v z_v / T + G(seed, t, v), the
+ *             noise from Philox4x64-10 keyed by (seed, t) (see oracle_gumbel);
+ *             int8 rows use the scaled logits raw_v * s_r.
+ *
  * Threads only split independent rows or independent vocab entries; the order
  * of every per-element sum is the one stated above.
  */
@@ -237,6 +241,44 @@ double oracle_logprob_i64_row(const int64_t *z, int64_t V, double scale, int64_t
   return scale * (double)(z[t] - zmax) - log(s);
 }
 
+/* ------------------------------------------- seeded Gumbel-max sampling */
+/* Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+ * easy as 1, 2, 3", SC 2011): ten rounds of two 64 x 64 -> 128-bit products
+ * of counter words with fixed multipliers, the high halves mixed with the other
+ * counter words and the key, the key bumped by fixed Weyl constants between
+ * rounds.  Counter and key are the whole state: output = f(counter, key). */
+void oracle_philox4x64(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+  uint64_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+  uint64_t k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += W0; k1 += W1; }
+    unsigned __int128 p0 = (unsigned __int128)M0 * x0;
+    unsigned __int128 p1 = (unsigned __int128)M1 * x2;
+    uint64_t y0 = (uint64_t)(p1 >> 64) ^ x1 ^ k0, y1 = (uint64_t)p1;
+    uint64_t y2 = (uint64_t)(p0 >> 64) ^ x3 ^ k1, y3 = (uint64_t)p0;
+    x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+  }
+  out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+/* Gumbel noise of token v for the draw keyed by (seed, position) ("12
+ * Exactness", section 12.5: the token at index t is the argmax of
+ * log p_t + G_t, G_t Gumbel noise from a generator seeded by (seed, t)).
+ * Word (v >> 5) & 3 of Philox4x64-10 at counter (32 (v >> 7) + (v & 31), 0, 0, 0)
+ * under key (seed, position); its top 23 bits u give U = (2u + 1) 2^-24 in
+ * (0, 1); G = -ln(-ln U). */
+double oracle_gumbel(uint64_t seed, int64_t position, int64_t v) {
+  const uint64_t ctr[4] = {32 * (uint64_t)(v >> 7) + (uint64_t)(v & 31), 0, 0, 0};
+  const uint64_t key[2] = {seed, (uint64_t)position};
+  uint64_t out[4];
+  oracle_philox4x64(ctr, key, out);
+  const uint64_t u = out[(v >> 5) & 3] >> 41;
+  const double U = (double)(2 * u + 1) * 0x1p-24;
+  return -log(-log(U));
+}
+
 /* ------------------------------------------------------- row pipelines */
 /* rows are processed in chunks so the logits buffer stays near 256 MB */
 static int64_t chunk_rows(int64_t B, int64_t V) {
@@ -255,6 +297,11 @@ typedef struct {
   double *vals_d, *margin_d, *logp;
   int64_t *raw;
   float *vals_f, *margin_f;
+  double temperature;       /* sampling */
+  const uint64_t *seed;
+  const int64_t *position;
+  int32_t *token;
+  double *value, *gap;
 } scan_job;
 
 static float scaled_f32(int64_t z, float s) {
@@ -302,6 +349,31 @@ static void logprob_task(void *ctx, int64_t rr) {
   else
     j->logp[r] = oracle_logprob_i64_row((const int64_t *)j->z + rr * V, V,
                                         j->scale ? (double)j->scale[r] : 1.0, j->target[r]);
+}
+
+/* y_v = z_v / T + G(seed, position, v) for every token, then the top two with
+ * strict comparisons (the lowest id wins a tie).  int8: z_v = raw_v * scale. */
+static void sample_task(void *ctx, int64_t rr) {
+  const scan_job *j = (const scan_job *)ctx;
+  int64_t r = j->r0 + rr, V = j->V;
+  double s = 1.0;
+  if (j->mode == MODE_I8 && j->scale) {
+    s = (double)j->scale[r];
+    if (!(s > 0.0) || !isfinite(s)) {
+      j->token[r] = -1; j->value[r] = NAN; j->gap[r] = NAN;
+      return;
+    }
+  }
+  double b1 = -INFINITY, b2 = -INFINITY;
+  int32_t i1 = -1;
+  for (int64_t v = 0; v < V; ++v) {
+    double z = j->mode == MODE_BF16 ? ((const double *)j->z)[rr * V + v]
+                                    : (double)((const int64_t *)j->z)[rr * V + v] * s;
+    double y = z / j->temperature + oracle_gumbel(j->seed[r], j->position[r], v);
+    if (y > b1) { b2 = b1; b1 = y; i1 = (int32_t)v; }
+    else if (y > b2) { b2 = y; }
+  }
+  j->token[r] = i1; j->value[r] = b1; j->gap[r] = b1 - b2;
 }
 
 static int run_rows(scan_job *job, const void *x, const void *w, int64_t B, int64_t H,
@@ -359,6 +431,29 @@ int oracle_logprob_i8(const int8_t *x, const int8_t *w, int64_t B, int64_t H, in
   memset(&j, 0, sizeof j);
   j.mode = MODE_I8; j.V = V; j.scale = scale; j.target = target; j.logp = logp;
   return run_rows(&j, x, w, B, H, logprob_task, nthreads);
+}
+
+int oracle_sample_bf16(const uint16_t *x, const uint16_t *w, int64_t B, int64_t H, int64_t V,
+                       double temperature, const uint64_t *seed, const int64_t *position,
+                       int32_t *token, double *value, double *gap, int nthreads) {
+  if (bad_shape(B, H, V) || V < 2 || !(temperature > 0.0)) return 1;
+  scan_job j;
+  memset(&j, 0, sizeof j);
+  j.mode = MODE_BF16; j.V = V; j.temperature = temperature; j.seed = seed; j.position = position;
+  j.token = token; j.value = value; j.gap = gap;
+  return run_rows(&j, x, w, B, H, sample_task, nthreads);
+}
+
+int oracle_sample_i8(const int8_t *x, const int8_t *w, int64_t B, int64_t H, int64_t V,
+                     const float *scale, double temperature, const uint64_t *seed,
+                     const int64_t *position, int32_t *token, double *value, double *gap,
+                     int nthreads) {
+  if (bad_shape(B, H, V) || V < 2 || !(temperature > 0.0)) return 1;
+  scan_job j;
+  memset(&j, 0, sizeof j);
+  j.mode = MODE_I8; j.V = V; j.scale = scale; j.temperature = temperature; j.seed = seed;
+  j.position = position; j.token = token; j.value = value; j.gap = gap;
+  return run_rows(&j, x, w, B, H, sample_task, nthreads);
 }
 
 int oracle_threads(int nthreads) { return resolve_threads(nthreads); }

@@ -310,6 +310,123 @@ def pin_gated_rerank_bruteforce(o):
             assert vals[r, 0] == float(z[order[0]]) and vals[r, 1] == float(z[order[1]])
 
 
+# ------------------------------------------------------------ sampling
+def _chi2_sf(stat, dof):
+    """Survival function of the chi-square distribution (scipy's routine)."""
+    from scipy.stats import chi2
+    return float(chi2.sf(stat, dof))
+
+
+def pin_philox_vs_numpy(o):
+    """Philox4x64-10 against numpy.random.Philox (an independent library
+    implementation of the same published generator; numpy advances the counter
+    before each block, so its counter c - 1 yields block c), including a carry
+    out of the low counter word."""
+    rng = np.random.default_rng(41)
+    cases = [([1, 0, 0, 0], [0, 0]), ([0, 9, 3, 1], [5, 6])]
+    for _ in range(64):
+        c = rng.integers(0, 2 ** 63, 4, dtype=np.uint64) * np.uint64(2) + np.uint64(1)
+        cases.append((list(c), list(rng.integers(0, 2 ** 63, 2, dtype=np.uint64) * np.uint64(2))))
+    for ctr, key in cases:
+        prev = np.array(ctr, dtype=np.uint64)
+        if prev[0] == 0:                         # borrow from word 1
+            prev[0] = np.uint64(2 ** 64 - 1)
+            prev[1] -= np.uint64(1)
+        else:
+            prev[0] -= np.uint64(1)
+        ref = np.random.Philox(counter=prev, key=np.array(key, dtype=np.uint64)).random_raw(4)
+        assert np.array_equal(o.philox4x64(ctr, key), ref), (ctr, key)
+
+
+def pin_gumbel_decimal(o):
+    """G = -ln(-ln U) to 50 digits, with U = (2u + 1) 2^-24 from the top 23
+    bits u of numpy's Philox block: word (v >> 5) & 3 of counter
+    32 (v >> 7) + (v & 31) under key (seed, position)."""
+    getcontext().prec = 50
+    rng = np.random.default_rng(42)
+    for _ in range(40):
+        seed, pos, v = int(rng.integers(0, 2 ** 63)), int(rng.integers(0, 2 ** 40)), \
+            int(rng.integers(0, 200000))
+        c = 32 * (v >> 7) + (v & 31)
+        blk = np.random.Philox(counter=np.array([c - 1 if c else 2 ** 64 - 1, 0 if c else 2 ** 64 - 1,
+                                                 0 if c else 2 ** 64 - 1, 0 if c else 2 ** 64 - 1],
+                                                dtype=np.uint64),
+                               key=np.array([seed, pos], dtype=np.uint64)).random_raw(4)
+        u = int(blk[(v >> 5) & 3]) >> 41
+        U = Decimal(2 * u + 1) / Decimal(2 ** 24)
+        g = -(-(U.ln())).ln()
+        assert abs(Decimal(o.gumbel(seed, pos, v)) - g) < Decimal("1e-12"), (seed, pos, v)
+
+
+def _sample_rows(o, z_cols, T, n, seed=7):
+    """n draws from one fixed logit row z_cols (exact in bf16; x = e_0, W[:, 0]
+    = z), keyed by (seed, position = draw index)."""
+    V, H = len(z_cols), 64
+    x = np.zeros((n, H), np.uint16)
+    x[:, 0] = bf16_const(1.0, ()).item()
+    w = np.zeros((V, H), np.uint16)
+    w[:, 0] = synth.bf16_from_f32(np.asarray(z_cols, np.float32))
+    assert np.array_equal(synth.bf16_to_f64(w[:, 0]), np.asarray(z_cols, np.float64))
+    return o.sample_bf16(x, w, T, np.full(n, seed, np.uint64), np.arange(n, dtype=np.int64))
+
+
+def pin_sample_distribution(o):
+    """Gumbel-max draws follow softmax(z / T): chi-square of 40,000 draws over
+    6 tokens at T = 1 and T = 0.5 (p > 1e-6), and a uniform draw when all
+    logits are equal."""
+    z = np.array([1.0, 0.5, 0.0, -0.5, 2.0, 1.0])
+    n = 40000
+    for T in (1.0, 0.5):
+        tok, val, gap = _sample_rows(o, z, T, n)
+        p = np.exp(z / T - np.max(z / T))
+        p /= p.sum()
+        cnt = np.bincount(tok, minlength=len(z))
+        stat = float(np.sum((cnt - n * p) ** 2 / (n * p)))
+        assert _chi2_sf(stat, len(z) - 1) > 1e-6, (T, cnt, n * p)
+        assert np.all(gap >= 0)
+    tok, _, _ = _sample_rows(o, np.zeros(8), 1.0, n, seed=8)
+    cnt = np.bincount(tok, minlength=8)
+    assert _chi2_sf(float(np.sum((cnt - n / 8) ** 2 / (n / 8))), 7) > 1e-6, cnt
+
+
+def pin_sample_limits_and_keys(o):
+    """T -> 0 is the greedy argmax (logit gaps of 2^-4 against noise in
+    [-2.9, 16.7] at T = 2^-16); the same (seed, position) draws the same token
+    in any row order; int8 and bf16 rows with equal logits draw equally; an
+    invalid int8 scale draws -1."""
+    rng = np.random.default_rng(43)
+    H, V, B = 64, 40, 30
+    x = np.zeros((B, H), np.uint16)
+    x[:, 0] = bf16_const(1.0, ()).item()
+    z = rng.permutation(V).astype(np.float64) / 16.0        # distinct, gaps >= 1/16
+    w = np.zeros((V, H), np.uint16)
+    w[:, 0] = synth.bf16_from_f32(z.astype(np.float32))
+    seed = rng.integers(0, 2 ** 63, B, dtype=np.uint64)
+    pos = rng.integers(0, 2 ** 31, B).astype(np.int64)
+    tok, _, _ = o.sample_bf16(x, w, 2.0 ** -16, seed, pos)
+    assert np.all(tok == int(np.argmax(z)))
+    tok, val, gap = o.sample_bf16(x, w, 1.0, seed, pos)
+    perm = rng.permutation(B)
+    tok_p, val_p, _ = o.sample_bf16(x[perm], w, 1.0, seed[perm], pos[perm])
+    assert np.array_equal(tok_p, tok[perm]) and np.array_equal(val_p, val[perm])
+    assert len(set(tok.tolist())) > 1                       # different keys, different draws
+    # int8: x = e_0, W[:, 0] = small integers, scale 1 -> the same logits
+    zi = rng.integers(-40, 41, V)
+    xi = np.zeros((B, H), np.int8)
+    xi[:, 0] = 1
+    wi = np.zeros((V, H), np.int8)
+    wi[:, 0] = zi
+    wb = np.zeros((V, H), np.uint16)
+    wb[:, 0] = synth.bf16_from_f32(zi.astype(np.float32))
+    t8, v8, g8 = o.sample_i8(xi, wi, 0.7, seed, pos, scale=np.ones(B, np.float32))
+    tb, vb, gb = o.sample_bf16(x, wb, 0.7, seed, pos)
+    assert np.array_equal(t8, tb) and np.array_equal(v8, vb) and np.array_equal(g8, gb)
+    sc = np.ones(B, np.float32)
+    sc[3], sc[5] = 0.0, np.nan
+    t8, v8, _ = o.sample_i8(xi, wi, 0.7, seed, pos, scale=sc)
+    assert t8[3] == -1 and t8[5] == -1 and np.isnan(v8[3]) and t8[4] == tb[4]
+
+
 def pin_int_scaled_values(o):
     """int8 top-2 values and margin are the nearest float32 of the exact
     rational raw * scale; a non-positive scale gives NaN values but valid ids."""
@@ -507,6 +624,7 @@ FAST = [
     pin_int_logits_bruteforce, pin_int_overflow_bound, pin_top2_bruteforce,
     pin_top2_hand_ties, pin_greedy_identical_rows, pin_greedy_permutation,
     pin_greedy_near_ties, pin_gated_hand_cases, pin_gated_rerank_bruteforce,
+    pin_philox_vs_numpy, pin_gumbel_decimal, pin_sample_distribution, pin_sample_limits_and_keys,
     pin_int_scaled_values, pin_logsoftmax_sums_to_one,
     pin_logprob_closed_forms, pin_logprob_shift_invariance, pin_logprob_decimal,
     pin_logprob_out_of_range, pin_round_bf16, pin_pages_float_examples,
