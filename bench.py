@@ -85,6 +85,18 @@ class Caller:
                 self.calls.append((lib.lmhead_greedy_top2, (
                     mode, round_bf16, P(xx), P(ww), B, H, V, P(scale), P(ids), P(vals), P(margin),
                     P(raw), P(self.ws), ws_bytes, self.stream)))
+        elif kind == "sample":
+            token = torch.empty((B,), dtype=torch.int32, device=dev)
+            value = torch.empty((B,), dtype=torch.float32, device=dev)
+            gap = torch.empty((B,), dtype=torch.float32, device=dev)
+            g = torch.Generator().manual_seed(B)
+            seed = torch.randint(0, 2 ** 62, (B,), generator=g, dtype=torch.int64).to(dev)
+            pos = torch.arange(B, dtype=torch.int64).to(dev)
+            self.keep = (token, value, gap, seed, pos)
+            for xx, ww in zip(x_list, w_list):
+                self.calls.append((lib.lmhead_sample_gumbel, (
+                    mode, P(xx), P(ww), B, H, V, ctypes.c_float(tau or 1.0), P(scale), P(seed),
+                    P(pos), P(token), P(value), P(gap), P(self.ws), ws_bytes, self.stream)))
         elif kind == "gated":
             ids = torch.empty((B, 2), dtype=torch.int32, device=dev)
             vals = torch.empty((B, 2), dtype=torch.float32, device=dev)
@@ -339,6 +351,17 @@ def extras(torch, lmhead, synth, bf16, x, w_copies, d):
                                        "overhead": tg / tp - 1.0, "gate_rate": rate}
         log(f"gated B={B}: {tg * 1e6:.1f} us vs bf16 head {tp * 1e6:.1f} us "
             f"({100 * (tg / tp - 1):+.1f}%), gate rate {100 * rate:.2f}%")
+
+    # seeded Gumbel-max sampling (T = 1) against the float32 greedy head
+    for B in (1, 512):
+        xb = [x[:B].contiguous()] * NCOPIES
+        greedy = Caller(torch, lmhead, xb, w_copies, B, H, V)
+        samp = Caller(torch, lmhead, xb, w_copies, B, H, V, kind="sample", tau=1.0)
+        tgr, tsa = time_calls(torch, greedy, 100), time_calls(torch, samp, 100)
+        res[f"sample_gumbel_b{B}"] = {"us_per_call": tsa * 1e6, "us_greedy": tgr * 1e6,
+                                      "overhead": tsa / tgr - 1.0, "rows_per_s": B / tsa}
+        log(f"sample B={B}: {tsa * 1e6:.1f} us vs greedy {tgr * 1e6:.1f} us "
+            f"({100 * (tsa / tgr - 1):+.1f}%)")
 
     # near-tie stress, 4096 rows
     nt = synth.make_inputs("neartie")

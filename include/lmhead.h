@@ -138,6 +138,29 @@ lmhead_status lmhead_greedy_gated(int mode, const void *x, const void *w, int64_
                                   float *margin, int32_t *gated, void *ws, size_t ws_bytes,
                                   void *stream);
 
+/* Seeded Gumbel-max sampling ("12 Exactness", section 12.5: the token at index
+ * t is the argmax of log p_t + G_t, with Gumbel noise G_t from a generator
+ * seeded by (seed, t); an exact draw from p_t).  Since log p_t differs from
+ * z / T by a constant per row:
+ *   token[b] = argmax_v ( z[b, v] / temperature + G(seed[b], position[b], v) ),
+ *              the lowest id on a tie;
+ *   G(s, t, v) = -ln(-ln U), U = (2u + 1) 2^-24, u the top 23 bits of word
+ *              (v >> 5) & 3 of Philox4x64-10 (Salmon et al., SC 2011) at counter
+ *              (32 (v >> 7) + (v & 31), 0, 0, 0) under key (s, t).
+ * A row's draw depends on its own (seed, position) and logits only, never on
+ * the batch.  value[b] (optional) = the winning score, gap[b] (optional) = its
+ * lead over the runner-up (small gaps are where float32 rounding could pick
+ * the other token).  MODE_INT8 uses the scaled logits row_scale[b] * z (NULL =
+ * 1); a non-positive or non-finite scale draws token -1 with NaN value and gap.
+ * temperature must be positive and finite (LMHEAD_E_VALUE otherwise).  seed and
+ * position: device arrays of B, 8-byte aligned.  ws / ws_bytes as for
+ * lmhead_greedy_top2. */
+lmhead_status lmhead_sample_gumbel(int mode, const void *x, const void *w, int64_t B, int64_t H,
+                                   int64_t V, float temperature, const float *row_scale,
+                                   const uint64_t *seed, const int64_t *position, int32_t *token,
+                                   float *value, float *gap, void *ws, size_t ws_bytes,
+                                   void *stream);
+
 /* Device self-check of the row property ("12 Exactness", section 12.8: a
  * load-time self-check proves on the device that every row gets the same bits
  * whatever the number of rows).  Computes the logits of x[0..B) as one batch,

@@ -173,6 +173,33 @@ lmhead_status lmhead_greedy_gated(int mode, const void *x, const void *w, int64_
   return launched(lmh::launch_gate(g, B, (hipStream_t)stream));
 }
 
+lmhead_status lmhead_sample_gumbel(int mode, const void *x, const void *w, int64_t B, int64_t H,
+                                   int64_t V, float temperature, const float *row_scale,
+                                   const uint64_t *seed, const int64_t *position, int32_t *token,
+                                   float *value, float *gap, void *ws, size_t ws_bytes,
+                                   void *stream) {
+  lmhead_status st = check_common(mode, LMHEAD_ROUND_F32, x, w, B, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (!seed || !position || !token) return LMHEAD_E_NULL;
+  if (((uintptr_t)seed & 7u) || ((uintptr_t)position & 7u) || !aligned4(token) ||
+      (value && !aligned4(value)) || (gap && !aligned4(gap)) ||
+      (row_scale && !aligned4(row_scale)))
+    return LMHEAD_E_ALIGN;
+  if (!(temperature > 0.0f) || !(temperature <= 3.4e38f)) return LMHEAD_E_VALUE;
+  const lmh::Plan plan = lmh::plan_for(B, row_bytes(mode, H), V);
+  lmh::Params p = base_params(mode, x, w, B, H, V, plan);
+  st = bind_workspace(p, ws, ws_bytes, B, V);
+  if (st != LMHEAD_OK) return st;
+  p.scale = mode == LMHEAD_MODE_INT8 ? row_scale : nullptr;
+  p.inv_t = 1.0f / temperature;
+  p.seed = seed;
+  p.position = position;
+  p.token = token;
+  p.value = value;
+  p.gap = gap;
+  return launched(lmh::launch(mode, lmh::kSample, plan, p, (hipStream_t)stream));
+}
+
 // scratch: [B, V] batch logits | [V] one-row logits | [B, V] reversed-batch logits |
 //          [B, H] reversed rows; every region 256-byte aligned
 static size_t self_check_layout(int mode, int64_t B, int64_t H, int64_t V, size_t off[4]) {

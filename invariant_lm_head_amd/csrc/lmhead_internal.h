@@ -7,7 +7,7 @@
 
 namespace lmh {
 
-enum Epilogue { kStore = 0, kTop2 = 1, kLse = 2 };
+enum Epilogue { kStore = 0, kTop2 = 1, kLse = 2, kSample = 3 };
 
 // Softmax partial sums and top-2 partial records are kept per block of 128
 // vocabulary columns; the block grid depends on V only.
@@ -31,6 +31,12 @@ struct Params {
   unsigned *tickets;      // [ceil(B/16)] zero on entry and on exit
   int32_t *zt;            // [B] target logit bits (float32 or int32)
   uint4 *records;         // [B][nblocks] per-block partials
+  // kSample: seeded Gumbel-max draw of every row
+  float inv_t;                // 1 / temperature
+  const uint64_t *seed;       // [B]
+  const int64_t *position;    // [B]
+  int32_t *token;             // [B]
+  float *value, *gap;         // [B] (each may be null)
 };
 
 // One tiling of the grid: which kernel instance runs and its grid shape.

@@ -4,7 +4,8 @@
 // tile of rows x vocabulary columns and reduces them in its epilogue:
 //   kStore  writes Z (float32, bf16-rounded, or int32);
 //   kTop2   per-row top-2 (value, id) of every 128-column vocabulary block;
-//   kLse    per-row (block max, sum of exp) of every block, and the target logit.
+//   kLse    per-row (block max, sum of exp) of every block, and the target logit;
+//   kSample per-row top-2 of z / T + Gumbel noise (seeded Gumbel-max draw).
 // The block partials of a row are then folded into the outputs by merge_rows(),
 // either by the last workgroup of the launch (atomic ticket, small batches) or
 // by a second, row-parallel kernel (larger batches); both run the same code.
@@ -233,6 +234,57 @@ template <int NR, int NM> __device__ __forceinline__ void interleave_reads() {
   if constexpr (NR > rounds) __builtin_amdgcn_sched_group_barrier(0x100, NR - rounds, 0);
 }
 
+// ----------------------------------------------------- Gumbel-max noise
+// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, SC 2011): ten rounds of two
+// 64 x 64 -> 128-bit products of counter words with fixed multipliers, the high
+// halves mixed with the other counter words and the key, the key bumped by
+// fixed Weyl constants between rounds.  Here the counter is (c, 0, 0, 0).
+__device__ __forceinline__ void philox4x64(uint64_t c, uint64_t k0, uint64_t k1,
+                                           uint64_t (&out)[4]) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+  uint64_t x0 = c, x1 = 0, x2 = 0, x3 = 0;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += W0; k1 += W1; }
+    const uint64_t h0 = __umul64hi(M0, x0), l0 = M0 * x0;
+    const uint64_t h1 = __umul64hi(M1, x2), l1 = M1 * x2;
+    const uint64_t y0 = h1 ^ x1 ^ k0, y2 = h0 ^ x3 ^ k1;
+    x0 = y0; x1 = l1; x2 = y2; x3 = l0;
+  }
+  out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+// G = -ln(-ln U), U = (2u + 1) 2^-24 from the top 23 bits u of a Philox word.
+// -ln U: for U < 1/2 from the hardware log2 (no cancellation there); for
+// U >= 1/2 from d = 1 - U (exact) as 2 atanh(d / (2 - d)), whose series in
+// s = d / (2 - d) <= 1/3 is summed to s^17 (terms shrink at least 9-fold).
+__device__ __forceinline__ float gumbel_of(uint64_t word) {
+  const unsigned u = (unsigned)(word >> 41);
+  const float U = (float)(2u * u + 1u) * 0x1p-24f;
+  const float d = (float)((1u << 24) - 2u * u - 1u) * 0x1p-24f;  // 1 - U, exact
+  const float s = d / (2.0f - d);
+  const float s2 = s * s;
+  float a = 1.0f / 17.0f;
+  a = a * s2 + 1.0f / 15.0f;
+  a = a * s2 + 1.0f / 13.0f;
+  a = a * s2 + 1.0f / 11.0f;
+  a = a * s2 + 1.0f / 9.0f;
+  a = a * s2 + 1.0f / 7.0f;
+  a = a * s2 + 1.0f / 5.0f;
+  a = a * s2 + 1.0f / 3.0f;
+  a = a * s2 + 1.0f;
+  const float L_series = 2.0f * (s * a);
+  const float L_log = -kLn2 * log2_hw(U);
+  const float L = U < 0.5f ? L_log : L_series;
+  return -kLn2 * log2_hw(L);
+}
+
+__device__ __forceinline__ uint64_t word_of(const uint64_t (&w)[4], int q) {
+  const uint64_t a = (q & 1) ? w[1] : w[0], b = (q & 1) ? w[3] : w[2];
+  return (q & 2) ? b : a;
+}
+
 // ------------------------------------------------------------ top-2 records
 // A candidate is ranked by one 64-bit key: an order-preserving 32-bit image of
 // its logit in the high half and the complement of its token id in the low
@@ -388,7 +440,7 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
   for (int g = tid / kSlots; g < nrows; g += nthreads / kSlots) {
     const int row = row0 + g;
     const uint4 *rec = p.records + (int64_t)row * nb;
-    if constexpr (EPI == kTop2) {
+    if constexpr (EPI == kTop2 || EPI == kSample) {
       Top2 t{0, 0};
       // 16 records per slot in flight per round (one memory latency per round)
       for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
@@ -405,7 +457,16 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
       t = t2_merge(t, perm<kQuadX2>(t));
       t = t2_merge(t, perm<kHalfMirror>(t));
       t = t2_merge(t, perm<kMirror>(t));
-      if (slot == 0) {
+      if (EPI == kSample && slot == 0) {
+        bool ok = true;
+        if constexpr (MODE == 1) ok = scale_ok(p.scale ? p.scale[row] : 1.0f);
+        const float y1 = okey_value<float>((unsigned)(t.k1 >> 32));
+        const float y2 = okey_value<float>((unsigned)(t.k2 >> 32));
+        const float nan = __builtin_nanf("");
+        p.token[row] = ok ? key_id(t.k1) : -1;
+        if (p.value) p.value[row] = ok ? y1 : nan;
+        if (p.gap) p.gap[row] = ok ? y1 - y2 : nan;
+      } else if (EPI == kTop2 && slot == 0) {
         const val_t v1 = okey_value<val_t>((unsigned)(t.k1 >> 32));
         const val_t v2 = okey_value<val_t>((unsigned)(t.k2 >> 32));
         p.top_id[2 * row] = key_id(t.k1);
@@ -705,42 +766,103 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
     const int u = rs_value_index(j);  // row value this lane holds after a reduce-scatter
     const bool dup = (j & 1) != 0;    // the two lanes holding a row: write from one
 
-    if constexpr (EPI == kTop2) {
+    if constexpr (EPI == kTop2 || EPI == kSample) {
       uint4 *xch = (uint4 *)smem;  // [BM rows][WAVES_N] records
-      // ROUND: rank the bf16-rounded logits (the bf16-output head)
-      auto top2_blocks = [&](auto round) {
+      if constexpr (EPI == kSample) {
+        // seeded Gumbel-max: every logit becomes y = z / T + G(seed, position,
+        // column) in place (float32 bits), then the y are ranked like logits.
+        // One Philox block per (row, 128-column block, column lane) serves the
+        // lane's column tiles of that block.
 #pragma unroll
-      for (int mt = 0; mt < T::WM; ++mt) {
-        const int lrow = wm * T::WM * 32 + mt * 32 + acc_row(u, h);  // row this lane ends with
+        for (int mt = 0; mt < T::WM; ++mt) {
 #pragma unroll
-        for (int b = 0; b < T::BPW; ++b) {
-          const int col0 = wcol0 + b * T::NTB * 32 + j;  // this lane's first column of the block
-          Top2 t[16];
+          for (int b = 0; b < T::BPW; ++b) {
+            const int col0 = wcol0 + b * T::NTB * 32 + j;
+            const uint64_t ctr = 32u * (uint64_t)(col0 >> 7) + (uint64_t)j;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            val_t z[T::NTB];
+            for (int v = 0; v < 16; ++v) {
+              const int row = min(m0 + wm * T::WM * 32 + mt * 32 + acc_row(v, h), p.B - 1);
+              float cr = p.inv_t;
+              if constexpr (MODE == 1) cr = (p.scale ? p.scale[row] : 1.0f) * p.inv_t;
+              uint64_t words[4];
+              philox4x64(ctr, p.seed[row], (uint64_t)p.position[row], words);
 #pragma unroll
-            for (int k = 0; k < T::NTB; ++k) {
-              val_t zz = acc[mt][b * T::NTB + k][v];
-              if constexpr (MODE == 0 && decltype(round)::value) zz = bf16_round(zz);
-              z[k] = col0 + 32 * k < p.V ? zz : lowest_of<val_t>();
+              for (int k = 0; k < T::NTB; ++k) {
+                const int nt = b * T::NTB + k;
+                const float y = (float)acc[mt][nt][v] * cr +
+                                gumbel_of(word_of(words, ((col0 >> 5) + k) & 3));
+                acc[mt][nt][v] = vfrom<val_t>(__float_as_int(y));
+              }
+              // one row value at a time: interleaving the 16 Philox chains would
+              // buy nothing here and run out of registers
+              __builtin_amdgcn_sched_barrier(0);
             }
-            t[v] = lane_top2<T::NTB>(z, ~(unsigned)col0);
-          }
-          const Top2 r = reduce_scatter(t, j);
-          if constexpr (T::PARTS == 1) {
-            const int row = m0 + lrow;
-            const int blk = wcol0 / kBlockCols + b;
-            if (!dup && row < p.B && blk < p.nblocks)
-              p.records[(int64_t)row * p.nblocks + blk] = t2_pack(r);
-          } else {
-            if (!dup) xch[lrow * T::WAVES_N + wn] = t2_pack(r);
           }
         }
+#pragma unroll
+        for (int mt = 0; mt < T::WM; ++mt) {
+          const int lrow = wm * T::WM * 32 + mt * 32 + acc_row(u, h);  // row this lane ends with
+#pragma unroll
+          for (int b = 0; b < T::BPW; ++b) {
+            const int col0 = wcol0 + b * T::NTB * 32 + j;
+            Top2 t[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              float y[T::NTB];
+#pragma unroll
+              for (int k = 0; k < T::NTB; ++k) {
+                const float yy = __int_as_float(vbits(acc[mt][b * T::NTB + k][v]));
+                y[k] = col0 + 32 * k < p.V ? yy : -__builtin_inff();
+              }
+              t[v] = lane_top2<T::NTB>(y, ~(unsigned)col0);
+            }
+            const Top2 r = reduce_scatter(t, j);
+            if constexpr (T::PARTS == 1) {
+              const int row = m0 + lrow;
+              const int blk = wcol0 / kBlockCols + b;
+              if (!dup && row < p.B && blk < p.nblocks)
+                p.records[(int64_t)row * p.nblocks + blk] = t2_pack(r);
+            } else {
+              if (!dup) xch[lrow * T::WAVES_N + wn] = t2_pack(r);
+            }
+          }
+        }
+      } else {
+        // ROUND: rank the bf16-rounded logits (the bf16-output head)
+        auto top2_blocks = [&](auto round) {
+#pragma unroll
+        for (int mt = 0; mt < T::WM; ++mt) {
+          const int lrow = wm * T::WM * 32 + mt * 32 + acc_row(u, h);  // row this lane ends with
+#pragma unroll
+          for (int b = 0; b < T::BPW; ++b) {
+            const int col0 = wcol0 + b * T::NTB * 32 + j;  // this lane's first column of the block
+            Top2 t[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              val_t z[T::NTB];
+#pragma unroll
+              for (int k = 0; k < T::NTB; ++k) {
+                val_t zz = acc[mt][b * T::NTB + k][v];
+                if constexpr (MODE == 0 && decltype(round)::value) zz = bf16_round(zz);
+                z[k] = col0 + 32 * k < p.V ? zz : lowest_of<val_t>();
+              }
+              t[v] = lane_top2<T::NTB>(z, ~(unsigned)col0);
+            }
+            const Top2 r = reduce_scatter(t, j);
+            if constexpr (T::PARTS == 1) {
+              const int row = m0 + lrow;
+              const int blk = wcol0 / kBlockCols + b;
+              if (!dup && row < p.B && blk < p.nblocks)
+                p.records[(int64_t)row * p.nblocks + blk] = t2_pack(r);
+            } else {
+              if (!dup) xch[lrow * T::WAVES_N + wn] = t2_pack(r);
+            }
+          }
+        }
+        };
+        if (MODE == 0 && p.round_bf16) top2_blocks(std::true_type{});
+        else top2_blocks(std::false_type{});
       }
-      };
-      if (MODE == 0 && p.round_bf16) top2_blocks(std::true_type{});
-      else top2_blocks(std::false_type{});
       if constexpr (T::PARTS > 1) {
         __syncthreads();
         if (wn % T::PARTS == 0 && lane < T::WM * 32) {
@@ -977,6 +1099,9 @@ hipError_t launch_tile(int epi, const Params &p, hipStream_t s) {
     case kTop2:
       hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kTop2, FUSED>), grid, block, 0, s, p);
       break;
+    case kSample:
+      hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kSample, FUSED>), grid, block, 0, s, p);
+      break;
     default:
       hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kLse, FUSED>), grid, block, 0, s, p);
       break;
@@ -987,6 +1112,8 @@ hipError_t launch_tile(int epi, const Params &p, hipStream_t s) {
     const dim3 mgrid((p.B + 256 / kSlots - 1) / (256 / kSlots));
     if (epi == kTop2)
       hipLaunchKernelGGL((lmhead_merge_kernel<MODE, kTop2>), mgrid, dim3(256), 0, s, p);
+    else if (epi == kSample)
+      hipLaunchKernelGGL((lmhead_merge_kernel<MODE, kSample>), mgrid, dim3(256), 0, s, p);
     else
       hipLaunchKernelGGL((lmhead_merge_kernel<MODE, kLse>), mgrid, dim3(256), 0, s, p);
   }

@@ -29,6 +29,8 @@ SIGNATURES = {
     "lmhead_logprob": ([_I, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _I),
     "lmhead_greedy_gated": ([_I, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, _P, _P,
                              _SZ, _P], _I),
+    "lmhead_sample_gumbel": ([_I, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, _P, _P,
+                              _P, _P, _SZ, _P], _I),
     "lmhead_self_check_bytes": ([_I, _I64, _I64, _I64], _SZ),
     "lmhead_self_check": ([_I, _P, _P, _I64, _I64, _I64, _P, _SZ, _P, _P], _I),
     "lmhead_status_string": ([_I], ctypes.c_char_p),
@@ -191,6 +193,33 @@ def greedy_gated(x: torch.Tensor, w: torch.Tensor, tau: float,
                                        ws.numel() * ws.element_size(), _stream(dev))
     _check("lmhead_greedy_gated", st)
     return ids, vals, margin, gated
+
+
+def sample_gumbel(x: torch.Tensor, w: torch.Tensor, temperature: float, seed: torch.Tensor,
+                  position: torch.Tensor, row_scale: torch.Tensor | None = None,
+                  ws: torch.Tensor | None = None):
+    """Seeded Gumbel-max draw of every row: token [B] int32, winning score [B]
+    float32 and its gap to the runner-up [B] float32.  seed: [B] uint64 bits
+    (any 64-bit integer tensor), position: [B] int64."""
+    mode = _mode_of(x, w)
+    B, H, V = _dims(x, w)
+    dev = x.device
+    for name, t in (("seed", seed), ("position", position)):
+        if t.numel() != B or not t.is_cuda or t.element_size() != 8:
+            raise ValueError(f"{name} must be a device tensor of B 64-bit integers")
+    token = torch.empty((B,), dtype=torch.int32, device=dev)
+    value = torch.empty((B,), dtype=torch.float32, device=dev)
+    gap = torch.empty((B,), dtype=torch.float32, device=dev)
+    need = workspace_bytes(mode, B, H, V)
+    if ws is None:
+        ws = workspace(need, dev)
+    st = library().lmhead_sample_gumbel(mode, _ptr(x), _ptr(w), B, H, V, float(temperature),
+                                        _ptr(row_scale), _ptr(seed.contiguous()),
+                                        _ptr(position.contiguous()), _ptr(token), _ptr(value),
+                                        _ptr(gap), _ptr(ws), ws.numel() * ws.element_size(),
+                                        _stream(dev))
+    _check("lmhead_sample_gumbel", st)
+    return token, value, gap
 
 
 def self_check(x: torch.Tensor, w: torch.Tensor) -> int:

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(lmhead.SIGNATURES)
@@ -148,6 +148,31 @@ def test_gated_validation(lib):
     assert call(nws=ws_need - 1) == E_WORKSPACE
     assert call(V=1) == E_SHAPE
     assert lib.lmhead_status_string(E_VALUE) == b"a scalar argument is out of range"
+
+
+def test_sample_validation(lib):
+    ws_need = lib.lmhead_workspace_bytes(0, 4, 64, 1000)
+    A8 = ctypes.c_void_p(0x30000)
+
+    def call(mode=0, x=A, w=A, B=4, H=64, V=1000, T=1.0, scale=None, seed=A8, pos=A8, tok=A,
+             val=None, gap=None, ws=A2, nws=ws_need):
+        return lib.lmhead_sample_gumbel(mode, x, w, B, H, V, T, scale, seed, pos, tok, val, gap,
+                                        ws, nws, S)
+
+    assert call(mode=2) == E_MODE
+    assert call(seed=None) == E_NULL
+    assert call(pos=None) == E_NULL
+    assert call(tok=None) == E_NULL
+    assert call(seed=ctypes.c_void_p(0x30004)) == E_ALIGN   # 4-byte aligned only
+    assert call(tok=ODD) == E_ALIGN
+    assert call(val=ODD) == E_ALIGN
+    assert call(T=0.0) == E_VALUE
+    assert call(T=-1.0) == E_VALUE
+    assert call(T=float("inf")) == E_VALUE
+    assert call(T=float("nan")) == E_VALUE
+    assert call(nws=ws_need - 1) == E_WORKSPACE
+    assert call(V=1) == E_SHAPE
+    assert call(mode=1, H=1 << 17) == E_OVERFLOW
 
 
 def test_self_check_validation(lib):
