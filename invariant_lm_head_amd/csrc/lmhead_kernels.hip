@@ -15,7 +15,9 @@
 //     with ONE instruction for every batch size (v_mfma_f32_32x32x16_bf16 or
 //     v_mfma_i32_32x32x32_i8); k-step s covers bytes [32 s, 32 s + 32) of a row,
 //     lane half h holding bytes [32 s + 16 h, +16); no split-K; rows of an MFMA
-//     are independent, so a row's bits do not depend on its neighbours;
+//     are independent, so a row's bits do not depend on its neighbours; the
+//     int8 head takes the k-steps from a column-dependent start (k_rotation),
+//     which cannot change a bit of its exact int32 sums;
 //   * tile shapes change with B only in how many rows and columns a workgroup
 //     covers, which does not change any logit's arithmetic;
 //   * a block's softmax partial is m_b = max over the block (exact), then
@@ -217,6 +219,28 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// Start of the int8 head's k order for vocabulary column `col`: the row is
+// streamed in 256-byte units in ascending order from unit ((col >> 10) mod
+// units), wrapping round.  Workgroups of different column groups then read
+// different 256-byte offsets of their W rows at the same moment, which spreads
+// the concurrent HBM requests over the address bits below the row stride; with
+// every workgroup at the same offset the stream rate depends on where the
+// allocation landed (measured on MI355X: 23-36 us for the same 131 MB read).
+// Integer sums are exact in any order.  The float head does not rotate: a
+// column-dependent order would give two identical W rows different roundings,
+// and their exact tie would no longer go to the lower id.  Rows that are not a
+// whole number of 256-byte units start at byte 0.
+#ifndef LMH_ROT_SHIFT
+#define LMH_ROT_SHIFT 10
+#endif
+#ifndef LMH_ROT_MULT
+#define LMH_ROT_MULT 1
+#endif
+__device__ __forceinline__ int64_t k_rotation(int64_t rowbytes, int col) {
+  if (rowbytes % 256 != 0) return 0;
+  return (int64_t)((((unsigned)col >> LMH_ROT_SHIFT) * LMH_ROT_MULT) % (unsigned)(rowbytes >> 8)) << 8;
 }
 
 // Scheduling hint for one k-step: NR fragment reads (of the next step) spread
@@ -585,6 +609,15 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   // (their results are masked in the epilogue)
   const char *xtile = p.x + (int64_t)m0 * p.rowbytes;
   const char *wtile = p.w + (int64_t)n0 * p.rowbytes;
+  // stage t holds bytes [koff(t), koff(t) + BKB) of every row: the k order of
+  // this tile's columns (a tile never straddles a rotation group, and the
+  // rotation is a whole number of stages)
+  static_assert((1LL << LMH_ROT_SHIFT) % T::BN == 0 && 256 % T::BKB == 0, "tile within one rotation group");
+  const int64_t rot = MODE == 1 ? k_rotation(p.rowbytes, n0) : 0;
+  auto koff = [&](int stage) -> int64_t {
+    const int64_t o = (int64_t)stage * T::BKB + rot;
+    return o >= p.rowbytes ? o - p.rowbytes : o;
+  };
   auto span_offset = [&](int span, int first, int last) -> unsigned {
     const int off = span * 1024 + lane * 16;
     const int row = off / T::BKB;
@@ -600,7 +633,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
     woff[i] = span_offset(min(wave + i * T::NW, T::WSPANS - 1), n0, p.V - 1);
   const unsigned lds0 = lds_addr(smem);
   auto issue_x = [&](int stage, int buf) {
-    const char *base = xtile + (int64_t)stage * T::BKB;
+    const char *base = xtile + koff(stage);
 #pragma unroll
     for (int i = 0; i < T::SPWX_MAX; ++i) {
       const int span = wave + i * T::NW;
@@ -610,7 +643,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
     }
   };
   auto issue_w = [&](int stage, int buf) {
-    const char *base = wtile + (int64_t)stage * T::BKB;
+    const char *base = wtile + koff(stage);
 #pragma unroll
     for (int i = 0; i < T::SPWW_MAX; ++i) {
       const int span = wave + i * T::NW;
@@ -638,7 +671,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mt][nt][v] = 0;
 
-  // ---- main loop: k ascending, one MFMA chain per logit.
+  // ---- main loop: stages in k order (koff), one MFMA chain per logit.
   // Loads: boundary b (after stage b; boundaries -NSW..-1 before the loop)
   // loads, in this order, X stage b + NSX into X buffer b mod NSX and W stage
   // b + NSW into W buffer b mod NSW.  In the loop the X loads are issued at the
@@ -692,7 +725,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   // W spans of one boundary, PER of them after each of the first k-steps
   constexpr int PER = (T::SPWW_MAX + T::STEPS - 2) / (T::STEPS - 1);
   auto issue_w_part = [&](int stage, int buf, int i0) {
-    const char *base = wtile + (int64_t)stage * T::BKB;
+    const char *base = wtile + koff(stage);
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int i = i0 + q;
@@ -1032,10 +1065,11 @@ __global__ __launch_bounds__(64) void lmhead_gate_kernel(GateParams g) {
   f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  const int nsteps = (int)(g.rowbytes / 32);
-#pragma unroll 8
-  for (int k = 0; k < nsteps; ++k)
-    acc = Arith<0>::mfma(*(const i32x4 *)(xr + 32 * k), *(const i32x4 *)(wr + 32 * k), acc);
+  const int nsteps = (int)(g.rowbytes / 32);  // a multiple of 4 (H is of 64)
+  for (int k0 = 0; k0 < nsteps; k0 += 4)
+#pragma unroll
+    for (int k = k0; k < k0 + 4; ++k)
+      acc = Arith<0>::mfma(*(const i32x4 *)(xr + 32 * k), *(const i32x4 *)(wr + 32 * k), acc);
   // MFMA row 0 of column c is value 0 of lane (j = c, h = 0)
   const float z1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[0]), 0));
   const float z2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[0]), 1));
