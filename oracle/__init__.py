@@ -97,6 +97,14 @@ class Oracle:
             "oracle_sample_bf16": ([P, P, i64, i64, i64, D, P, P, P, P, P, i32], ctypes.c_int),
             "oracle_sample_i8": ([P, P, i64, i64, i64, P, D, P, P, P, P, P, i32], ctypes.c_int),
             "oracle_threads": ([i32], ctypes.c_int),
+            "oracle_iexp_q30": ([ctypes.c_uint64], ctypes.c_uint64),
+            "oracle_iln_q30": ([ctypes.c_uint64], i64),
+            "oracle_int_row_scale": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, P, P], ctypes.c_int),
+            "oracle_quantize_rows": ([P, i64, i64, P, P, P], ctypes.c_int),
+            "oracle_logprob_int_row": ([P, i64, i64, ctypes.c_int32, i64], i64),
+            "oracle_logprob_int": ([P, P, i64, i64, i64, ctypes.c_int32, ctypes.c_int32, P, P,
+                                    P, P, i32], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -276,6 +284,59 @@ class Oracle:
     def logprob_i64_row(self, z, scale: float, t: int) -> float:
         z = _c(z, np.int64)
         return self.lib.oracle_logprob_i64_row(_ptr(z), z.size, float(scale), int(t))
+
+    # ------------------------------------------ integer front and back
+    # ("Eliminating Nondeterminism in LLM Inference with Integer-Only
+    # Arithmetic", section "DetLLM": dyadic scales with one rounding rule,
+    # integer exp and softmax, per-token quantisation; the algorithm itself is
+    # stated in oracle.c, "integer front and back")
+    NATS_FRAC = 24            # fractional bits of a log-prob (Q.24 nats)
+    LOGP_INVALID = -2 ** 63   # target out of range or scale not valid
+
+    def iexp_q30(self, T: int) -> int:
+        """e^(-T / 2^24) in Q.30 for T >= 0 in Q.24 nats."""
+        return int(self.lib.oracle_iexp_q30(int(T)))
+
+    def iln_q30(self, S: int) -> int:
+        """ln(S / 2^30) in Q.30 for S >= 2^30."""
+        return int(self.lib.oracle_iln_q30(int(S)))
+
+    def int_row_scale(self, um: int, ue: int, M: int, E: int):
+        """(m, k) with m / 2^k = um 2^ue * M 2^E, m of 31 bits, or None when
+        the scale is not valid (um, M <= 0 or k outside [24, 86])."""
+        m, k = ctypes.c_int64(), ctypes.c_int32()
+        ok = self.lib.oracle_int_row_scale(int(um), int(ue), int(M), int(E),
+                                           ctypes.byref(m), ctypes.byref(k))
+        return (m.value, k.value) if ok else None
+
+    def quantize_rows(self, x):
+        """Per-token int8 quantisation of int32 rows: (q[B,H] int8, M[B] int32,
+        E[B] int32) with the row's step D = M 2^E."""
+        x = _c(x, np.int32)
+        B, H = x.shape
+        q = np.empty((B, H), np.int8)
+        M, E = np.empty(B, np.int32), np.empty(B, np.int32)
+        assert self.lib.oracle_quantize_rows(_ptr(x), B, H, _ptr(q), _ptr(M), _ptr(E)) == 0
+        return q, M, E
+
+    def logprob_int_row(self, z, m: int, k: int, t: int) -> int:
+        """Integer log-softmax of one row of exact integer logits with the
+        logit scale m / 2^k: log p(t) in Q.24 (LOGP_INVALID if invalid)."""
+        z = _c(z, np.int64)
+        return int(self.lib.oracle_logprob_int_row(_ptr(z), z.size, int(m), int(k), int(t)))
+
+    def logprob_int(self, x, w, um: int, ue: int, M, E, target,
+                    nthreads: int | None = None) -> np.ndarray:
+        """log p(target[r]) in Q.24 (int64) of the int8 head with the integer
+        log-softmax; row r's logit scale is um 2^ue * M[r] 2^E[r]."""
+        x, w = _c(x, np.int8), _c(w, np.int8)
+        B, H, V = _shape(x, w)
+        M, E, t = _c(M, np.int32), _c(E, np.int32), _c(target, np.int32)
+        out = np.empty(B, np.int64)
+        assert self.lib.oracle_logprob_int(_ptr(x), _ptr(w), B, H, V, int(um), int(ue),
+                                           _ptr(M), _ptr(E), _ptr(t), _ptr(out),
+                                           _nt(nthreads)) == 0
+        return out
 
     def round_bf16(self, v: float) -> float:
         """Nearest bf16 value (ties to even) of a float64, as float64."""

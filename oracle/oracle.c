@@ -38,6 +38,15 @@
  *             noise from Philox4x64-10 keyed by (seed, t) (see oracle_gumbel);
  *             int8 rows use the scaled logits raw_v * s_r.
  *
+ *  integer    the all-integer front and back of the int8 head, an algorithm
+ *  front and  of our own stated in full at "integer front and back" below:
+ *  back       per-token int8 quantisation with a dyadic step M 2^E, and a
+ *             log-softmax in fixed point (Q.24 nats, exp values in Q.30) from
+ *             exact integer logits, with one rounding rule (half up).
+ *             ("Integer-Only Arithmetic", section "DetLLM": dyadic scales
+ *             m / 2^k with one fixed rounding rule, shift-based integer
+ *             exp and softmax, per-token activation quantisation.)
+ *
  * Threads only split independent rows or independent vocab entries; the order
  * of every per-element sum is the one stated above.
  */
@@ -457,3 +466,226 @@ int oracle_sample_i8(const int8_t *x, const int8_t *w, int64_t B, int64_t H, int
 }
 
 int oracle_threads(int nthreads) { return resolve_threads(nthreads); }
+
+/* ------------------------------------------------ integer front and back */
+/* The pages name the ingredients (dyadic scales m / 2^k rescaled by an integer
+ * multiply and a shift with one rounding rule; shift-based integer exp and
+ * softmax; each token quantised from its own values) but print no algorithm.
+ * This is ours, every step in integers:
+ *
+ *  rounding   every rescale rounds half up: rnd(p, s) = floor((p + 2^(s-1)) / 2^s)
+ *             on a non-negative p; a rounded division is floor((2a + b) / 2b).
+ *
+ *  front      row x (int32) -> q (int8) and step D = M 2^E, 2^14 <= M < 2^15:
+ *             a = max |x|; D is the least number with a 15-bit mantissa such
+ *             that 127 D >= a (a zero row: q = 0, D = 1 = 2^14 2^-14);
+ *             q = sign(x) round_half_away(|x| / D), so |q| <= 127 and the
+ *             largest |x| maps to 127.
+ *
+ *  scale      a row's logit z = sum q w has the real value z * m / 2^k:
+ *             m / 2^k = U * D with the tensor unit U = um 2^ue (the real value
+ *             of one unit of x times one unit of w), the mantissa product
+ *             um * M rounded to 31 bits; valid when 24 <= k <= 86.
+ *
+ *  exp        iexp(T) = e^(-T / 2^24) in Q.30 for T >= 0 in Q.24 nats:
+ *             T = q L + r with L = round(ln 2 * 2^24), 0 <= r < L; e^(-r/2^24)
+ *             by its Taylor series to degree 10 in Horner form with the
+ *             coefficients C_n = round(2^30 / n!); then times 2^-q by rnd.
+ *
+ *  ln         iln(S) = ln(S / 2^30) in Q.30 for S >= 2^30: S = 2^l (1 + f),
+ *             ln(1 + f) = 2 atanh(u), u = f / (2 + f) < 1/3, the odd series
+ *             to u^25; plus (l - 30) round(ln 2 * 2^30).
+ *
+ *  softmax    blocks of 128 vocabulary columns (b = v / 128, fixed by V):
+ *             m_b = max z over the block; S_b = sum iexp(T(m_b - z_v));
+ *             z_max = max m_b; S = sum_b rnd(S_b * iexp(T(z_max - m_b)), 30);
+ *             T(d) = rnd(d * m, k - 24); all sums exact, so in any order.
+ *             log p(t) = -(T(z_max - z_t) + rnd(iln(S), 6)) in Q.24 (int64,
+ *             at least -(2^63 - 1)); INT64_MIN when t is not in [0, V) or the
+ *             scale is not valid.
+ */
+#define FIX_NATS 24   /* fractional bits of a value in nats */
+#define FIX_EXP 30    /* fractional bits of an exp value and of ln inside iln */
+#define EXP_DEGREE 10
+#define ATANH_TERMS 12
+
+static uint64_t rnd(uint64_t p, int s) {   /* p < 2^63 */
+  if (s <= 0) return p;
+  if (s >= 64) return 0;
+  return (p + ((uint64_t)1 << (s - 1))) >> s;
+}
+
+static uint64_t rnd_div(uint64_t a, uint64_t b) { return (2 * a + b) / (2 * b); }
+
+static int bit_length(uint64_t v) {
+  int n = 0;
+  while (v) { ++n; v >>= 1; }
+  return n;
+}
+
+/* round(ln 2 * 2^frac): log(2.0) is within 1e-16 of ln 2 and the product is
+ * more than 1e-4 away from a rounding boundary for frac = 24 and 30 */
+static uint64_t ln2_fixed(int frac) { return (uint64_t)llround(log(2.0) * ldexp(1.0, frac)); }
+
+static uint64_t factorial(int n) {
+  uint64_t f = 1;
+  for (int i = 2; i <= n; ++i) f *= (uint64_t)i;
+  return f;
+}
+
+uint64_t oracle_iexp_q30(uint64_t T) {
+  const uint64_t L = ln2_fixed(FIX_NATS);
+  if (T >= 64 * L) return 0;  /* q >= 64: 2^-q of a Q.30 value rounds to 0 */
+  const uint64_t q = T / L, r = T - q * L;
+  uint64_t y = rnd_div((uint64_t)1 << FIX_EXP, factorial(EXP_DEGREE));
+  for (int n = EXP_DEGREE - 1; n >= 0; --n) {
+    const uint64_t c = rnd_div((uint64_t)1 << FIX_EXP, factorial(n));
+    y = c - rnd(y * r, FIX_NATS);  /* y <= 2^30, r < 2^24; y stays positive */
+  }
+  return rnd(y, (int)q);
+}
+
+int64_t oracle_iln_q30(uint64_t S) {
+  if (S < ((uint64_t)1 << FIX_EXP)) return INT64_MIN;
+  int l = bit_length(S) - 1;                       /* 2^l <= S < 2^(l+1) */
+  uint64_t mant = rnd(S, l - FIX_EXP);             /* in [2^30, 2^31] */
+  if (mant == ((uint64_t)2 << FIX_EXP)) { mant = (uint64_t)1 << FIX_EXP; l += 1; }
+  const uint64_t f = mant - ((uint64_t)1 << FIX_EXP);
+  const uint64_t u = rnd_div(f << FIX_EXP, ((uint64_t)2 << FIX_EXP) + f);
+  const uint64_t u2 = rnd(u * u, FIX_EXP);
+  uint64_t t = u, acc = u;
+  for (int j = 1; j <= ATANH_TERMS; ++j) {
+    t = rnd(t * u2, FIX_EXP);
+    acc += rnd_div(t, (uint64_t)(2 * j + 1));
+  }
+  return (int64_t)(l - FIX_EXP) * (int64_t)ln2_fixed(FIX_EXP) + 2 * (int64_t)acc;
+}
+
+/* logit scale m / 2^k of a row from the tensor unit um 2^ue and the row step
+ * M 2^E; returns 0 (invalid) unless um, M > 0 and 24 <= k <= 86 */
+int oracle_int_row_scale(int32_t um, int32_t ue, int32_t M, int32_t E, int64_t *m, int32_t *k) {
+  if (um <= 0 || M <= 0) return 0;
+  const uint64_t P = (uint64_t)um * (uint64_t)M;   /* < 2^62 */
+  int sh = bit_length(P) - 31;
+  uint64_t mm;
+  if (sh > 0) {
+    mm = rnd(P, sh);
+    if (mm == ((uint64_t)1 << 31)) { mm = (uint64_t)1 << 30; sh += 1; }
+  } else {
+    mm = P << (-sh);
+  }
+  const int64_t kk = -((int64_t)sh + ue + E);       /* real = mm 2^(sh + ue + E) */
+  if (kk < FIX_NATS || kk > FIX_NATS + 62) return 0;
+  *m = (int64_t)mm;
+  *k = (int32_t)kk;
+  return 1;
+}
+
+void oracle_quantize_row(const int32_t *x, int64_t H, int8_t *q, int32_t *M, int32_t *E) {
+  uint64_t a = 0;
+  for (int64_t i = 0; i < H; ++i) {
+    const uint64_t v = x[i] < 0 ? (uint64_t)(-(int64_t)x[i]) : (uint64_t)x[i];
+    if (v > a) a = v;
+  }
+  if (a == 0) {
+    for (int64_t i = 0; i < H; ++i) q[i] = 0;
+    *M = 1 << 14; *E = -14;
+    return;
+  }
+  /* e = floor(log2(a / 127)): the largest e with 127 2^e <= a */
+  int e = 40;
+  for (;; --e) {
+    const int ok = e >= 0 ? ((uint64_t)127 << e) <= a : (uint64_t)127 <= (a << (-e));
+    if (ok) break;
+  }
+  int ee = e - 14;                                  /* D = M 2^ee */
+  uint64_t mm;
+  if (ee <= 0) {
+    mm = ((a << (-ee)) + 126) / 127;                /* ceil(a 2^-ee / 127) */
+  } else {
+    const uint64_t d = (uint64_t)127 << ee;
+    mm = (a + d - 1) / d;
+  }
+  if (mm == ((uint64_t)1 << 15)) { mm = (uint64_t)1 << 14; ee += 1; }
+  const uint64_t num_shift = ee < 0 ? (uint64_t)(-ee) : 0, D = mm << (ee > 0 ? ee : 0);
+  for (int64_t i = 0; i < H; ++i) {
+    const uint64_t v = x[i] < 0 ? (uint64_t)(-(int64_t)x[i]) : (uint64_t)x[i];
+    const uint64_t n = v << num_shift;
+    const int64_t r = (int64_t)((2 * n + D) / (2 * D));   /* round half away from zero */
+    q[i] = (int8_t)(x[i] < 0 ? -r : r);
+  }
+  *M = (int32_t)mm;
+  *E = (int32_t)ee;
+}
+
+int oracle_quantize_rows(const int32_t *x, int64_t B, int64_t H, int8_t *q, int32_t *M,
+                         int32_t *E) {
+  if (B < 0 || H < 1) return 1;
+  for (int64_t r = 0; r < B; ++r) oracle_quantize_row(x + r * H, H, q + r * H, M + r, E + r);
+  return 0;
+}
+
+/* one row of exact integer logits (|z| < 2^31) -> log p(t) in Q.24 */
+int64_t oracle_logprob_int_row(const int64_t *z, int64_t V, int64_t m, int32_t k, int64_t t) {
+  if (t < 0 || t >= V || m <= 0 || k < FIX_NATS || k > FIX_NATS + 62) return INT64_MIN;
+  const int sh = k - FIX_NATS;
+  const int64_t nb = (V + 127) / 128;
+  int64_t zmax = INT64_MIN;
+  for (int64_t v = 0; v < V; ++v) if (z[v] > zmax) zmax = z[v];
+  uint64_t S = 0;
+  for (int64_t b = 0; b < nb; ++b) {
+    const int64_t v0 = b * 128, v1 = v0 + 128 < V ? v0 + 128 : V;
+    int64_t mb = INT64_MIN;
+    for (int64_t v = v0; v < v1; ++v) if (z[v] > mb) mb = z[v];
+    uint64_t Sb = 0;
+    for (int64_t v = v0; v < v1; ++v)
+      Sb += oracle_iexp_q30(rnd((uint64_t)(mb - z[v]) * (uint64_t)m, sh));
+    const uint64_t R = oracle_iexp_q30(rnd((uint64_t)(zmax - mb) * (uint64_t)m, sh));
+    /* rnd(Sb * R, 30) with Sb < 2^38: split Sb at bit 32 so both products fit */
+    S += ((Sb >> 32) * R << 2) + rnd((Sb & 0xffffffffu) * R, FIX_EXP);
+  }
+  const uint64_t Tt = rnd((uint64_t)(zmax - z[t]) * (uint64_t)m, sh);
+  const uint64_t L = rnd((uint64_t)oracle_iln_q30(S), FIX_EXP - FIX_NATS);
+  const uint64_t nl = Tt + L;                  /* < 2^63 + 2^40: no wrap */
+  return nl > (uint64_t)INT64_MAX ? -INT64_MAX : -(int64_t)nl;
+}
+
+typedef struct {
+  int64_t V, r0;
+  const int64_t *z;
+  const int64_t *m;
+  const int32_t *k, *target;
+  int64_t *logp;
+} int_job;
+
+static void logprob_int_task(void *ctx, int64_t rr) {
+  const int_job *j = (const int_job *)ctx;
+  const int64_t r = j->r0 + rr;
+  j->logp[r] = oracle_logprob_int_row(j->z + rr * j->V, j->V, j->m[r], j->k[r], j->target[r]);
+}
+
+/* x, w int8; per-row logit scale from the unit (um, ue) and the row steps
+ * (M, E); log p(target) in Q.24 */
+int oracle_logprob_int(const int8_t *x, const int8_t *w, int64_t B, int64_t H, int64_t V,
+                       int32_t um, int32_t ue, const int32_t *M, const int32_t *E,
+                       const int32_t *target, int64_t *logp, int nthreads) {
+  if (bad_shape(B, H, V)) return 1;
+  int64_t *m = (int64_t *)malloc(sizeof(int64_t) * (size_t)(B ? B : 1));
+  int32_t *k = (int32_t *)malloc(sizeof(int32_t) * (size_t)(B ? B : 1));
+  int64_t c = chunk_rows(B, V);
+  int64_t *z = (int64_t *)malloc((size_t)(c * V * 8));
+  if (!m || !k || !z) { free(m); free(k); free(z); return 2; }
+  for (int64_t r = 0; r < B; ++r)
+    if (!oracle_int_row_scale(um, ue, M[r], E[r], &m[r], &k[r])) { m[r] = 0; k[r] = 0; }
+  nthreads = resolve_threads(nthreads);
+  int_job j = {V, 0, z, m, k, target, logp};
+  for (int64_t r0 = 0; r0 < B; r0 += c) {
+    const int64_t n = (B - r0 < c) ? B - r0 : c;
+    logits_rows(MODE_I8, x, w, H, V, r0, n, z, nthreads);
+    j.r0 = r0;
+    parallel_for(nthreads, n, logprob_int_task, &j);
+  }
+  free(m); free(k); free(z);
+  return 0;
+}
+

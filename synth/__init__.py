@@ -20,6 +20,13 @@ synthetic rows stand in for it):
   (gain 1, eps 0), cast to float32 then rounded to bf16.
 * int8 tensors are uniform integers in [-127, 127]; per-row scales are
   float32(2^-18 * U[0.5, 2]).
+* integer hidden rows (the input of the int8 head's per-token quantisation,
+  stream 6): x ~ N(0,1) with 8 outlier channels (drawn once per seed) scaled
+  by 12, RMS-normalised per row in float64, then round(h * 2^10) as int32.
+  Their tensor unit: one unit of hidden (2^-10) times one unit of W,
+  1 / (32 * 73.6) (73.6 = the standard deviation of uniform integers in
+  [-127, 127]), so a logit has a standard deviation near 2; given as a
+  31-bit dyadic INT_UNIT = (m, e), real value m 2^e.
 
 Workloads (sizes from the head shapes the pages discuss: a TinyLlama-sized
 head, a 151,936-token vocabulary for teacher-forced scoring, a 128,256-token
@@ -41,7 +48,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "bf16_from_f32", "bf16_to_f32", "bf16_to_f64",
     "normal_bf16", "hidden_rms_bf16", "target_ids", "int8_uniform",
-    "row_scales", "near_tie", "make_inputs",
+    "row_scales", "near_tie", "make_inputs", "hidden_int32", "INT_UNIT",
 ]
 
 ROW_BLOCK = 4096  # rows per independently seeded block
@@ -134,6 +141,34 @@ def int8_uniform(seed: int, rows: int, cols: int) -> np.ndarray:
         rng = np.random.default_rng([seed, blk])
         out[lo:hi] = rng.integers(-127, 128, size=(hi - lo, cols), dtype=np.int8)
     return out
+
+
+def hidden_int32(seed: int, rows: int, cols: int, frac_bits: int = 10,
+                 outliers: int = 8, gain: float = 12.0) -> np.ndarray:
+    """RMS-normalised Gaussian rows with a few outlier channels, in fixed
+    point with ``frac_bits`` fractional bits, as int32 [rows, cols]."""
+    chans = np.random.default_rng([seed, 1 << 20]).choice(cols, size=min(outliers, cols),
+                                                          replace=False)
+    out = np.empty((rows, cols), dtype=np.int32)
+    for blk, lo, hi in _blocks(rows):
+        rng = np.random.default_rng([seed, blk])
+        x = rng.standard_normal((hi - lo, cols))
+        x[:, chans] *= gain
+        x /= np.sqrt(np.mean(x * x, axis=1, keepdims=True))
+        out[lo:hi] = np.rint(x * 2.0 ** frac_bits).astype(np.int32)
+    return out
+
+
+def _dyadic31(v: float):
+    """(m, e) with 2^30 <= m < 2^31 and m 2^e the nearest such value to v > 0."""
+    e = math.floor(math.log2(v)) - 30
+    m = round(v / 2.0 ** e)
+    if m == 2 ** 31:
+        m, e = 2 ** 30, e + 1
+    return int(m), int(e)
+
+
+INT_UNIT = _dyadic31(2.0 ** -10 / (32.0 * math.sqrt((255 ** 2 - 1) / 12.0)))
 
 
 def row_scales(seed: int, rows: int) -> np.ndarray:
@@ -238,6 +273,8 @@ def make_inputs(name: str, rows: int | None = None, with_weights: bool = True):
             out["w"] = int8_uniform(seed_of(c, 1), wl.V, wl.H)
         out["x"] = int8_uniform(seed_of(c, 2), B, wl.H)
         out["scale"] = row_scales(seed_of(c, 4), B)
+        out["hidden"] = hidden_int32(seed_of(c, 6), B, wl.H)
+        out["unit"] = INT_UNIT
     elif name == "tiny":
         if with_weights:
             out["w"] = normal_bf16(seed_of(c, 1), wl.V, wl.H, 0.02)

@@ -619,6 +619,217 @@ def pin_neartie_builder(o, rows=48):
         assert abs(margin[r] - gap) <= 1e-9, r
 
 
+# -------------------------------------------- integer front and back
+# The algorithm is ours (the pages name its ingredients only); it is pinned to
+# exact rationals, 50-digit decimals, an independent int64 matmul and the
+# invariants the integer arithmetic guarantees.
+Q24, Q30 = 2 ** 24, 2 ** 30
+
+
+def _dec_exp(fr: Fraction) -> Decimal:
+    getcontext().prec = 50
+    return dec(fr).exp()
+
+
+def _dec_ln(fr: Fraction) -> Decimal:
+    getcontext().prec = 50
+    return dec(fr).ln()
+
+
+def pin_int_quantize(o):
+    """Per-token int8 quantisation: the step D = M 2^E has a 15-bit mantissa,
+    127 D covers max|x| and no smaller 15-bit-mantissa step does; q is the
+    exact round-half-away of x / D (Fraction); the largest |x| maps to +-127;
+    |x - q D| <= D / 2; quantising -x gives -q; x * 2^j gives the same q and M
+    with E + j; a zero row gives q = 0, D = 1."""
+    rng = np.random.default_rng(71)
+    rows = []
+    for mag in (1, 3, 100, 2 ** 12, 2 ** 20, 2 ** 30):
+        for _ in range(3):
+            rows.append(rng.integers(-mag, mag + 1, 24))
+    rows.append(np.array([2 ** 31 - 1, -(2 ** 31 - 1)] + [5] * 22))
+    rows.append(np.array([-(2 ** 31)] + [7] * 23))
+    rows.append(np.array([0] * 23 + [1]))
+    rows.append(np.array([127 * 2 ** k for k in range(24)]))       # exact steps
+    x = np.array(rows, dtype=np.int64).astype(np.int32)
+    q, M, E = o.quantize_rows(x)
+    for r in range(x.shape[0]):
+        a = max(abs(int(v)) for v in x[r])
+        m, e = int(M[r]), int(E[r])
+        assert 2 ** 14 <= m < 2 ** 15, r
+        D = Fraction(m) * Fraction(2) ** e
+        assert 127 * D >= a, r
+        prev = (Fraction(m - 1) * Fraction(2) ** e if m > 2 ** 14
+                else Fraction(2 ** 15 - 1) * Fraction(2) ** (e - 1))
+        assert 127 * prev < a, r
+        for k in range(x.shape[1]):
+            v = Fraction(int(x[r, k]))
+            want = math.floor(abs(v) / D + Fraction(1, 2)) * (1 if v >= 0 else -1)
+            assert int(q[r, k]) == want, (r, k)
+            assert abs(v - int(q[r, k]) * D) <= D / 2, (r, k)
+        big = [k for k in range(x.shape[1]) if abs(int(x[r, k])) == a]
+        assert all(abs(int(q[r, k])) == 127 for k in big), r
+    ok = np.all(x != -(2 ** 31), axis=1)
+    qn, Mn, En = o.quantize_rows(-x[ok])
+    assert np.array_equal(qn, -q[ok]) and np.array_equal(Mn, M[ok]) and np.array_equal(En, E[ok])
+    small = np.all(np.abs(x.astype(np.int64)) < 2 ** 24, axis=1)
+    for j in (1, 5):
+        q2, M2, E2 = o.quantize_rows(x[small] * 2 ** j)
+        assert np.array_equal(q2, q[small]) and np.array_equal(M2, M[small])
+        assert np.array_equal(E2, E[small] + j)
+    q0, M0, E0 = o.quantize_rows(np.zeros((1, 8), np.int32))
+    assert not q0.any() and Fraction(int(M0[0])) * Fraction(2) ** int(E0[0]) == 1
+
+
+def pin_int_exp(o):
+    """Integer exp against 50-digit e^(-T / 2^24) * 2^30: within 3 units of
+    2^-30 on boundaries of the ln 2 reduction and on random T; exactly 2^30 at
+    T = 0; non-increasing in T; 0 far out.  The bound: Horner roundings
+    0.5 (1 + 0.7 + 0.7^2 + ...) < 1.7, series truncation (ln 2)^11 / 11! <
+    0.5, the rounded ln 2 (1.9e-9 relative per halving) < 1.1, and the final
+    shift 0.5."""
+    rng = np.random.default_rng(72)
+    L = round(math.log(2) * Q24)
+    Ts = [0, 1, 2, L - 1, L, L + 1, 7 * L - 1, 7 * L, 31 * L + 3, 33 * L]
+    Ts += [int(t) for t in rng.integers(0, 40 * Q24, 300)]
+    Ts += [int(t) for t in rng.integers(0, Q24, 100)]
+    worst = 0.0
+    for T in Ts:
+        got = o.iexp_q30(T)
+        want = _dec_exp(Fraction(-T, Q24)) * Q30
+        worst = max(worst, abs(float(Decimal(got) - want)))
+    assert worst <= 3.0, worst
+    assert o.iexp_q30(0) == Q30
+    assert o.iexp_q30(2 ** 62) == 0 and o.iexp_q30(64 * Q24) == 0
+    ts = sorted(set(Ts))
+    vals = [o.iexp_q30(t) for t in ts]
+    assert all(a >= b for a, b in zip(vals, vals[1:]))
+
+
+def pin_int_ln(o):
+    """Integer ln against 50-digit ln(S / 2^30) * 2^30: within 12 units of
+    2^-30 for S from 2^30 to 2^50, and 0 at S = 2^30.  The bound: the 30-bit
+    mantissa 0.5, the rounded ln 2 0.05 per octave (0.85), u rounded 0.5
+    times 2 / (1 - u^2) <= 2.25 (1.2), and 2 x (0.5 + a carried 0.2) for each
+    of at most 9 series terms above one unit (8.6); below 2^-26 nats, so under
+    one unit of the Q.24 result."""
+    rng = np.random.default_rng(73)
+    Ss = [Q30, Q30 + 1, 2 * Q30 - 1, 2 * Q30, 3 * Q30, 2 ** 47 + 12345, 2 ** 50 - 1]
+    Ss += [int(Q30 * float(f)) for f in np.exp(rng.uniform(0.0, 13.8, 300))]
+    for S in Ss:
+        got = o.iln_q30(S)
+        want = _dec_ln(Fraction(S, Q30)) * Q30
+        assert abs(Decimal(got) - want) <= 12, (S, got, want)
+    assert o.iln_q30(Q30) == 0
+
+
+def pin_int_row_scale(o):
+    """The row's logit scale m / 2^k equals um 2^ue * M 2^E within half a unit
+    of m's last bit, with 2^30 <= m < 2^31; out-of-range exponents and
+    non-positive mantissas are refused."""
+    rng = np.random.default_rng(74)
+    for _ in range(200):
+        um = int(rng.integers(1, 2 ** 31))
+        M = int(rng.integers(2 ** 14, 2 ** 15))
+        ue, E = int(rng.integers(-70, -20)), int(rng.integers(-21, 12))
+        res = o.int_row_scale(um, ue, M, E)
+        exact = Fraction(um * M) * Fraction(2) ** (ue + E)
+        if res is None:
+            kk = 30 - math.floor(math.log2(exact))
+            assert kk < 24 or kk > 86 or kk in (23, 87), (um, ue, M, E)
+            continue
+        m, k = res
+        assert 2 ** 30 <= m < 2 ** 31
+        assert abs(Fraction(m, 2 ** k) - exact) <= Fraction(1, 2 ** (k + 1)), (um, ue, M, E)
+    assert o.int_row_scale(0, -40, 2 ** 14, 0) is None
+    assert o.int_row_scale(2 ** 30, -40, -5, 0) is None
+    assert o.int_row_scale(2 ** 30, 0, 2 ** 14, 0) is None          # k < 24: too coarse
+
+
+def _int_logsoftmax_check(o, z, m, k, targets):
+    """Integer log-prob of row z against the 50-digit log-softmax of the real
+    logits z m / 2^k, within a bound derived from the arithmetic: 3 output
+    units (2^-24: the rounded T of the target, the rounded ln, the ln error),
+    3 units of 2^-30 per element exp and per block rescale relative to the
+    exact sum of exps, and 15 units of 2^-30 for the rescale factors and the
+    integer ln."""
+    s = Fraction(m, 2 ** k)
+    zmax = max(z)
+    getcontext().prec = 50
+    es = [_dec_exp(s * (int(v) - zmax)) for v in z]
+    S = sum(es)
+    V = len(z)
+    nb = (V + 127) // 128
+    bound = Decimal(3) / Q24 + Decimal(3 * (V + nb)) / Q30 / S + Decimal(15) / Q30
+    for t in targets:
+        got = Decimal(o.logprob_int_row(z, m, k, t)) / Q24
+        want = dec(s * (int(z[t]) - zmax)) - S.ln()
+        assert abs(got - want) <= bound, (V, t, float(got), float(want))
+
+
+def pin_int_logsoftmax(o):
+    """Integer log-softmax: random rows (V across block edges) within the
+    derived bound of the exact log-softmax; uniform logits give -ln V; V = 2;
+    adding a constant to every logit changes no bit; invalid targets and
+    scales give the sentinel."""
+    rng = np.random.default_rng(75)
+    for V in (2, 127, 128, 129, 300, 1000):
+        z = rng.integers(-2 ** 26, 2 ** 26, V)
+        m, k = int(rng.integers(2 ** 30, 2 ** 31)), int(rng.integers(52, 57))
+        _int_logsoftmax_check(o, z, m, k, [0, V - 1, int(rng.integers(0, V))])
+    z = np.full(1000, 12345)
+    _int_logsoftmax_check(o, z, 2 ** 30, 50, [0, 999])
+    got = Decimal(o.logprob_int_row(z, 2 ** 30, 50, 3)) / Q24
+    assert abs(got + Decimal(1000).ln()) <= Decimal(3) / Q24
+    z = np.array([0, 40000], np.int64)                       # V = 2, s (z1 - z0) = 1.2207
+    m, k = 2 ** 30, 45                                       # s = 2^-15
+    got = Decimal(o.logprob_int_row(z, m, k, 0)) / Q24
+    want = -Decimal(math.log1p(math.exp(40000 / 2 ** 15)))
+    assert abs(got - want) <= Decimal(3) / Q24 + Decimal(10) / Q30
+    z = rng.integers(-2 ** 24, 2 ** 24, 700)
+    base = [o.logprob_int_row(z, 1500000000, 50, t) for t in range(0, 700, 37)]
+    for c in (-(2 ** 28), 1, 987654321):
+        moved = [o.logprob_int_row(z + c, 1500000000, 50, t) for t in range(0, 700, 37)]
+        assert moved == base, c
+    bad = o.LOGP_INVALID
+    assert o.logprob_int_row(z, 1500000000, 50, -1) == bad
+    assert o.logprob_int_row(z, 1500000000, 50, 700) == bad
+    assert o.logprob_int_row(z, 0, 50, 3) == bad
+    assert o.logprob_int_row(z, 1500000000, 23, 3) == bad
+
+
+def pin_int_logprob_head(o):
+    """The whole integer path on tiny int8 heads: logits from an independent
+    int64 matmul, the row scale from exact rationals, the log-prob within the
+    derived bound of the exact log-softmax; the sum over every target of
+    exp(log p) is 1 within V times that bound."""
+    rng = np.random.default_rng(76)
+    B, H, V = 3, 64, 260
+    x = rng.integers(-127, 128, (B, H)).astype(np.int8)
+    w = rng.integers(-127, 128, (V, H)).astype(np.int8)
+    um, ue = 1_400_000_000, -58
+    M = rng.integers(2 ** 14, 2 ** 15, B).astype(np.int32)
+    E = np.array([-3, 0, 4], np.int32)
+    t = np.array([5, 0, V - 1], np.int32)
+    got = o.logprob_int(x, w, um, ue, M, E, t)
+    z = x.astype(np.int64) @ w.astype(np.int64).T
+    getcontext().prec = 50
+    for r in range(B):
+        s = Fraction(um) * Fraction(2) ** ue * int(M[r]) * Fraction(2) ** int(E[r])
+        mk = o.int_row_scale(um, ue, int(M[r]), int(E[r]))
+        assert mk is not None and abs(Fraction(mk[0], 2 ** mk[1]) - s) <= s / 2 ** 30
+        zmax = int(z[r].max())
+        S = sum(_dec_exp(s * (int(v) - zmax)) for v in z[r])
+        want = dec(s * (int(z[r, t[r]]) - zmax)) - S.ln()
+        # the 31-bit scale moves a logit difference d by at most d s 2^-30
+        slack = Decimal(float(s) * float(zmax - z[r].min()) / 2 ** 29)
+        bound = Decimal(3) / Q24 + Decimal(3 * (V + 3)) / Q30 / S + slack
+        assert abs(Decimal(int(got[r])) / Q24 - want) <= bound, r
+        every = [o.logprob_int_row(z[r], mk[0], mk[1], v) for v in range(V)]
+        total = sum(math.exp(v / Q24) for v in every)
+        assert abs(total - 1.0) <= V * float(bound), (r, total)
+
+
 FAST = [
     pin_logits_bruteforce, pin_logits_one_hot, pin_logits_closed_forms,
     pin_int_logits_bruteforce, pin_int_overflow_bound, pin_top2_bruteforce,
@@ -628,6 +839,8 @@ FAST = [
     pin_int_scaled_values, pin_logsoftmax_sums_to_one,
     pin_logprob_closed_forms, pin_logprob_shift_invariance, pin_logprob_decimal,
     pin_logprob_out_of_range, pin_round_bf16, pin_pages_float_examples,
+    pin_int_quantize, pin_int_exp, pin_int_ln, pin_int_row_scale, pin_int_logsoftmax,
+    pin_int_logprob_head,
 ]
 SLOW = [pin_logits_vs_blas, pin_int_logits_vs_numpy, pin_neartie_builder]
 ALL = FAST + SLOW

@@ -50,6 +50,30 @@ MUTANTS = [
     ("margin sign",
      "j->margin_d[r] = vals[0] - vals[1];",
      "j->margin_d[r] = vals[1] - vals[0];"),
+    ("integer exp: Horner sign",
+     "y = c - rnd(y * r, FIX_NATS);",
+     "y = c + rnd(y * r, FIX_NATS);"),
+    ("integer exp: coefficient off by one",
+     "const uint64_t c = rnd_div((uint64_t)1 << FIX_EXP, factorial(n));",
+     "const uint64_t c = rnd_div((uint64_t)1 << FIX_EXP, factorial(n + 1));"),
+    ("integer ln: atanh without its factor 2",
+     "* (int64_t)ln2_fixed(FIX_EXP) + 2 * (int64_t)acc;",
+     "* (int64_t)ln2_fixed(FIX_EXP) + (int64_t)acc;"),
+    ("integer softmax: block rescale dropped",
+     "S += ((Sb >> 32) * R << 2) + rnd((Sb & 0xffffffffu) * R, FIX_EXP);",
+     "S += Sb + 0 * R;"),
+    ("integer softmax: scale shift off by one",
+     "const int sh = k - FIX_NATS;",
+     "const int sh = k - FIX_NATS + 1;"),
+    ("quantise: rounds toward zero",
+     "const int64_t r = (int64_t)((2 * n + D) / (2 * D));",
+     "const int64_t r = (int64_t)(n / D);"),
+    ("quantise: step rounded down",
+     "mm = ((a << (-ee)) + 126) / 127;",
+     "mm = (a << (-ee)) / 127;"),
+    ("row scale: exponent sign",
+     "const int64_t kk = -((int64_t)sh + ue + E);",
+     "const int64_t kk = -((int64_t)sh + ue - E);"),
 ]
 
 
