@@ -19,9 +19,10 @@
  *                     matmul; integer sums are exact in any order.)
  *
  * Batch invariance.  Every logit is reduced over k in one order fixed by H
- * alone (one MFMA shape, k ascending, one accumulator), never by the number of
- * rows or a row's position in the batch; the softmax partial sums are fixed by
- * V alone.  A row's outputs are therefore bitwise identical at every batch
+ * alone (one MFMA shape, one accumulator; k ascending in MODE_BF16, and in
+ * MODE_INT8 from a start fixed by the column, which cannot change an exact
+ * integer sum), never by the number of rows or a row's position in the batch;
+ * the softmax partial sums are fixed by V alone.  A row's outputs are therefore bitwise identical at every batch
  * size.  ("12 Exactness", section 12.2: every matrix-product kernel fixes its
  * reduction order by the weight's shape and never by the row count;
  * "Integer-Only Arithmetic", section "Why kernels don't always add in the same
@@ -160,6 +161,50 @@ lmhead_status lmhead_sample_gumbel(int mode, const void *x, const void *w, int64
                                    const uint64_t *seed, const int64_t *position, int32_t *token,
                                    float *value, float *gap, void *ws, size_t ws_bytes,
                                    void *stream);
+
+/* The all-integer front and back of the int8 head ("Eliminating Nondeterminism
+ * in LLM Inference with Integer-Only Arithmetic", section "DetLLM": every
+ * tensor carries a dyadic scale m / 2^k, rescaled by an integer multiply and a
+ * shift with one fixed rounding rule; exp and softmax are integer algorithms;
+ * each token's activations are quantised from that token's own values, so its
+ * bits cannot depend on the batch).  The pages give no algorithm; this one
+ * rounds every rescale half up.
+ *
+ * lmhead_quantize_rows: per-token int8 quantisation of int32 rows x[B, H]
+ * (row-major, any H >= 1).  For row b, a = max |x|; the step D = M 2^E is the
+ * least number with a 15-bit mantissa (2^14 <= M < 2^15) such that 127 D >= a;
+ * q[b, k] = sign(x) floor(|x| / D + 1/2), so |q| <= 127 and the largest |x|
+ * maps to 127.  A zero row gives q = 0, M = 2^14, E = -14 (D = 1).  Outputs
+ * q[B, H] int8, step_m[B], step_e[B] int32; x, step_m, step_e 4-byte aligned.
+ *
+ * lmhead_logprob_int: log p(target[b]) in fixed point Q.24 (int64, units of
+ * 2^-24 nats) from the exact int32 logits z = x w^T of int8 x[B, H], w[V, H].
+ * Row b's real logits are z * unit * D_b with the tensor unit um 2^ue (the real
+ * value of one unit of the hidden input times one unit of w) and the row step
+ * D_b = step_m[b] 2^step_e[b] (as lmhead_quantize_rows gives it).  The scale
+ * is taken as m / 2^k, the mantissa product rounded to 31 bits, valid when
+ * 24 <= k <= 86.  With T(d) = round(d m / 2^(k - 24)) (Q.24 nats):
+ *   exp   e(T) = e^(-T / 2^24) in Q.30: T = q L + r with L = round(ln 2 2^24),
+ *         e^(-r) by its Taylor series to degree 10 (coefficients
+ *         round(2^30 / n!), Horner form), then times 2^-q;
+ *   sum   per block of 128 columns (fixed by V): m_c = max z, S_c = sum of
+ *         e(T(m_c - z)); S = sum over blocks of round(S_c e(T(z_max - m_c)) /
+ *         2^30), every sum exact;
+ *   ln    ln(S / 2^30) in Q.30 by 2 atanh(f / (2 + f)) on the 30-bit mantissa
+ *         1 + f of S, plus the exponent times round(ln 2 2^30);
+ *   out   logprob_q[b] = -(T(z_max - z_target) + round(ln / 2^6)).
+ * Integer arithmetic only, so the result is the same on every device.  A
+ * target outside [0, V) or a row scale that is not valid gives INT64_MIN.
+ * The error against the exact log-softmax of the real logits is a few units of
+ * 2^-24 plus 3 V 2^-30 relative to the sum of exps.  unit_m must be positive
+ * (LMHEAD_E_VALUE otherwise).  ws / ws_bytes as for lmhead_greedy_top2 with
+ * MODE_INT8.  logprob_q 8-byte aligned. */
+lmhead_status lmhead_quantize_rows(const int32_t *x, int64_t B, int64_t H, int8_t *q,
+                                   int32_t *step_m, int32_t *step_e, void *stream);
+lmhead_status lmhead_logprob_int(const void *x, const void *w, int64_t B, int64_t H, int64_t V,
+                                 int32_t unit_m, int32_t unit_e, const int32_t *step_m,
+                                 const int32_t *step_e, const int32_t *target,
+                                 int64_t *logprob_q, void *ws, size_t ws_bytes, void *stream);
 
 /* Device self-check of the row property ("12 Exactness", section 12.8: a
  * load-time self-check proves on the device that every row gets the same bits

@@ -149,6 +149,39 @@ lmhead_status lmhead_logprob(int mode, const void *x, const void *w, int64_t B, 
   return launched(lmh::launch(mode, lmh::kLse, plan, p, (hipStream_t)stream));
 }
 
+lmhead_status lmhead_quantize_rows(const int32_t *x, int64_t B, int64_t H, int8_t *q,
+                                   int32_t *step_m, int32_t *step_e, void *stream) {
+  if (!x || !q || !step_m || !step_e) return LMHEAD_E_NULL;
+  if (B < 1 || H < 1 || B > kMaxRows || H > kMaxHidden) return LMHEAD_E_SHAPE;
+  if (!aligned4(x) || !aligned4(step_m) || !aligned4(step_e)) return LMHEAD_E_ALIGN;
+  return launched(lmh::launch_quantize(x, B, H, q, step_m, step_e, (hipStream_t)stream));
+}
+
+lmhead_status lmhead_logprob_int(const void *x, const void *w, int64_t B, int64_t H, int64_t V,
+                                 int32_t unit_m, int32_t unit_e, const int32_t *step_m,
+                                 const int32_t *step_e, const int32_t *target,
+                                 int64_t *logprob_q, void *ws, size_t ws_bytes, void *stream) {
+  const int mode = LMHEAD_MODE_INT8;
+  lmhead_status st = check_common(mode, LMHEAD_ROUND_F32, x, w, B, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (!step_m || !step_e || !target || !logprob_q) return LMHEAD_E_NULL;
+  if (!aligned4(step_m) || !aligned4(step_e) || !aligned4(target) ||
+      ((uintptr_t)logprob_q & 7) != 0)
+    return LMHEAD_E_ALIGN;
+  if (unit_m <= 0) return LMHEAD_E_VALUE;
+  const lmh::Plan plan = lmh::plan_for(B, row_bytes(mode, H), V);
+  lmh::Params p = base_params(mode, x, w, B, H, V, plan);
+  st = bind_workspace(p, ws, ws_bytes, B, V);
+  if (st != LMHEAD_OK) return st;
+  p.target = target;
+  p.unit_m = unit_m;
+  p.unit_e = unit_e;
+  p.step_m = step_m;
+  p.step_e = step_e;
+  p.logprob_q = logprob_q;
+  return launched(lmh::launch(mode, lmh::kLseInt, plan, p, (hipStream_t)stream));
+}
+
 lmhead_status lmhead_greedy_gated(int mode, const void *x, const void *w, int64_t B, int64_t H,
                                   int64_t V, float tau, int32_t *top_id, float *top_val,
                                   float *margin, int32_t *gated, void *ws, size_t ws_bytes,

@@ -7,7 +7,7 @@
 
 namespace lmh {
 
-enum Epilogue { kStore = 0, kTop2 = 1, kLse = 2, kSample = 3 };
+enum Epilogue { kStore = 0, kTop2 = 1, kLse = 2, kSample = 3, kLseInt = 4 };
 
 // Softmax partial sums and top-2 partial records are kept per block of 128
 // vocabulary columns; the block grid depends on V only.
@@ -37,6 +37,11 @@ struct Params {
   const int64_t *position;    // [B]
   int32_t *token;             // [B]
   float *value, *gap;         // [B] (each may be null)
+  // kLseInt: integer log-softmax; row r's logit scale is unit * step_r
+  int32_t unit_m, unit_e;     // tensor unit um 2^ue
+  const int32_t *step_m;      // [B] row step mantissa M
+  const int32_t *step_e;      // [B] row step exponent E
+  int64_t *logprob_q;         // [B] log p(target) in Q.24
 };
 
 // One tiling of the grid: which kernel instance runs and its grid shape.
@@ -65,6 +70,10 @@ struct GateParams {
   int32_t *gated;   // [B]
 };
 hipError_t launch_gate(const GateParams &g, int64_t B, hipStream_t s);
+
+// Per-token int8 quantisation of int32 rows (one workgroup per row).
+hipError_t launch_quantize(const int32_t *x, int64_t B, int64_t H, int8_t *q, int32_t *step_m,
+                           int32_t *step_e, hipStream_t s);
 
 hipError_t launch_compare(const void *a, const void *b, int64_t nwords,
                           unsigned long long *mismatches, hipStream_t s);

@@ -5,7 +5,9 @@
 //   kStore  writes Z (float32, bf16-rounded, or int32);
 //   kTop2   per-row top-2 (value, id) of every 128-column vocabulary block;
 //   kLse    per-row (block max, sum of exp) of every block, and the target logit;
-//   kSample per-row top-2 of z / T + Gumbel noise (seeded Gumbel-max draw).
+//   kSample per-row top-2 of z / T + Gumbel noise (seeded Gumbel-max draw);
+//   kLseInt (int8) per-row block max and the exact sum of integer exps, for
+//           the all-integer log-softmax (see "integer front and back").
 // The block partials of a row are then folded into the outputs by merge_rows(),
 // either by the last workgroup of the launch (atomic ticket, small batches) or
 // by a second, row-parallel kernel (larger batches); both run the same code.
@@ -392,6 +394,133 @@ __device__ __forceinline__ Top2 lane_top2(const V (&z)[NTB], unsigned cbase) {
   }
 }
 
+// f(integral_constant<int, I>) for I = I0 .. N-1, unrolled by the front end
+// (for loop bodies too large for the unroller's budget)
+template <int I, int N, class F> __device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// ------------------------------------------------ integer front and back
+// The all-integer head ("Integer-Only Arithmetic", section "DetLLM": every
+// tensor carries a dyadic scale m / 2^k, rescaled by an integer multiply and a
+// shift under one rounding rule; exp and softmax are integer algorithms; each
+// token is quantised from its own values).  The pages give no algorithm; this
+// one uses round half up for every rescale, rnd(p, s) = (p + 2^(s-1)) >> s:
+//   * exp: T >= 0 in Q.24 nats -> e^(-T) in Q.30.  T = q L + r with L the
+//     Q.24 ln 2 and 0 <= r < L; e^(-r) by the Taylor series to degree 10 in
+//     Horner form with coefficients round(2^30 / n!); then rnd(., q).
+//   * ln: S >= 2^30 (Q.30) -> ln(S / 2^30) in Q.30: S = 2^l (1 + f) with f
+//     rounded to 30 bits, ln(1 + f) = 2 atanh(f / (2 + f)) by the odd series
+//     to the 25th power (rounded divisions), plus (l - 30) times the Q.30 ln 2.
+//   * a row's logit scale: unit um 2^ue times the row step M 2^E, the mantissa
+//     product rounded to 31 bits, as m / 2^(24 + sh) with 0 <= sh <= 62.
+//   * softmax: per 128-column block (fixed by V) the exact max m_b and the
+//     exact sum S_b of exp(T((m_b - z) m)); the row folds
+//     S = sum_b rnd(S_b exp(T((z_max - m_b) m)), 30) exactly (in any order),
+//     log p(t) = -(T((z_max - z_t) m) + rnd(ln S, 6)) in Q.24.
+constexpr int kNatsFrac = 24;
+constexpr int kExpFrac = 30;
+constexpr uint32_t kLn2Q24 = 11629080u;   // round(ln 2 * 2^24) (ln 2 * 2^24 = 11629079.97)
+constexpr int64_t kLn2Q30 = 744261118;    // round(ln 2 * 2^30) (ln 2 * 2^30 = 744261117.95)
+constexpr int kExpDegree = 10;
+constexpr int kAtanhTerms = 12;
+
+struct TaylorQ30 {  // round(2^30 / n!), n = 0 .. kExpDegree, half up
+  uint32_t c[kExpDegree + 1];
+  constexpr TaylorQ30() : c() {
+    uint64_t f = 1;
+    for (int n = 0; n <= kExpDegree; ++n) {
+      if (n >= 2) f *= (uint64_t)n;
+      c[n] = (uint32_t)((((uint64_t)1 << (kExpFrac + 1)) + f) / (2 * f));
+    }
+  }
+};
+constexpr TaylorQ30 kTaylor{};
+static_assert(kTaylor.c[0] == (1u << 30) && kTaylor.c[1] == (1u << 30) && kTaylor.c[2] == (1u << 29),
+              "Taylor coefficients");
+
+__device__ __forceinline__ uint64_t rnd64(uint64_t p, int s) {  // p < 2^63, 0 <= s <= 63
+  return s == 0 ? p : (p + ((uint64_t)1 << (s - 1))) >> s;
+}
+
+// e^(-T / 2^24) in Q.30 (T in Q.24 nats)
+__device__ __forceinline__ uint32_t iexp_q30(uint64_t T) {
+  // 2^-q with q >= 32 rounds a Q.30 value to 0 (branch-free: select at the end)
+  const bool zero = T >= 32ull * kLn2Q24;
+  const uint32_t t = zero ? 0u : (uint32_t)T;
+  const uint32_t q = t / kLn2Q24, r = t - q * kLn2Q24;
+  uint32_t y = kTaylor.c[kExpDegree];
+#pragma unroll
+  for (int n = kExpDegree - 1; n >= 0; --n)
+    y = kTaylor.c[n] - (uint32_t)(((uint64_t)y * r + (1u << (kNatsFrac - 1))) >> kNatsFrac);
+  const uint32_t e = (uint32_t)(((uint64_t)y + ((1ull << q) >> 1)) >> q);
+  return zero ? 0u : e;
+}
+
+// ln(S / 2^30) in Q.30 for S >= 2^30
+__device__ int64_t iln_q30(uint64_t S) {
+  int l = 63 - __clzll((long long)S);
+  uint64_t mant = rnd64(S, l - kExpFrac);
+  if (mant == (2ull << kExpFrac)) {
+    mant = 1ull << kExpFrac;
+    l += 1;
+  }
+  const uint64_t f = mant - (1ull << kExpFrac);
+  const uint64_t den = (2ull << kExpFrac) + f;
+  const uint64_t u = (2 * (f << kExpFrac) + den) / (2 * den);
+  const uint64_t u2 = rnd64(u * u, kExpFrac);
+  uint64_t t = u, acc = u;
+  for (int j = 1; j <= kAtanhTerms; ++j) {
+    t = rnd64(t * u2, kExpFrac);
+    const uint64_t d = 2 * j + 1;
+    acc += (2 * t + d) / (2 * d);
+  }
+  return (int64_t)(l - kExpFrac) * kLn2Q30 + 2 * (int64_t)acc;
+}
+
+// logit scale m / 2^(24 + sh) of a row; m = 0 when not valid
+struct IntScale {
+  uint32_t m;
+  int sh;
+};
+__device__ __forceinline__ IntScale int_row_scale(int um, int ue, int M, int E) {
+  if (um <= 0 || M <= 0) return IntScale{0u, 0};
+  const uint64_t P = (uint64_t)um * (uint64_t)M;  // < 2^62
+  int sh = (64 - __clzll((long long)P)) - 31;     // bits beyond 31
+  uint64_t mm;
+  if (sh > 0) {
+    mm = (P + (1ull << (sh - 1))) >> sh;
+    if (mm == (1ull << 31)) {
+      mm = 1ull << 30;
+      sh += 1;
+    }
+  } else {
+    mm = P << (-sh);
+  }
+  const int64_t k = -((int64_t)sh + ue + E);  // real = mm 2^-k
+  if (k < kNatsFrac || k > kNatsFrac + 62) return IntScale{0u, 0};
+  return IntScale{(uint32_t)mm, (int)(k - kNatsFrac)};
+}
+
+// T(d) = rnd(d m, sh): a logit difference d >= 0 in Q.24 nats
+__device__ __forceinline__ uint64_t int_nats(uint32_t d, const IntScale &s) {
+  return rnd64((uint64_t)d * s.m, s.sh);
+}
+
+// integer softmax partial carried through the lane tree: the block max and
+// the exact sum as two 32-bit halves (no padding, so it stays in registers)
+struct LseI {
+  int m;
+  unsigned lo, hi;
+  __device__ __forceinline__ uint64_t sum() const { return ((uint64_t)hi << 32) | lo; }
+};
+__device__ __forceinline__ LseI lse_i(int m, uint64_t s) {
+  return LseI{m, (unsigned)s, (unsigned)(s >> 32)};
+}
+
 // softmax partial carried through the lane tree: the block max (identical on
 // both partners of every pairing) and the partial sum
 struct Lse {
@@ -404,6 +533,15 @@ __device__ __forceinline__ Lse combine(const Lse &a, const Lse &b) { return Lse{
 template <int P> __device__ __forceinline__ Lse perm(const Lse &x) { return Lse{x.m, perm<P>(x.s)}; }
 __device__ __forceinline__ Lse pick(bool c, const Lse &a, const Lse &b) {
   return Lse{c ? a.m : b.m, c ? a.s : b.s};
+}
+__device__ __forceinline__ LseI combine(const LseI &a, const LseI &b) {
+  return lse_i(a.m, a.sum() + b.sum());
+}
+template <int P> __device__ __forceinline__ LseI perm(const LseI &x) {
+  return LseI{x.m, (unsigned)perm_i<P>((int)x.lo), (unsigned)perm_i<P>((int)x.hi)};
+}
+__device__ __forceinline__ LseI pick(bool c, const LseI &a, const LseI &b) {
+  return LseI{c ? a.m : b.m, c ? a.lo : b.lo, c ? a.hi : b.hi};
 }
 
 // One halving step of the reduce-scatter over the 32 column lanes: R row
@@ -512,6 +650,52 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
           p.top_val[2 * row + 1] = ok ? (float)((double)v2 * (double)s) : nan;
           p.margin[row] = ok ? (float)((double)(v1 - v2) * (double)s) : nan;
         }
+      }
+    } else if constexpr (EPI == kLseInt) {
+      // pass 1: the row max (exact); pass 2: the exact sum of the rescaled
+      // block sums (integers: the order does not matter)
+      int mx = INT_MIN;
+      for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
+        int m[kChunk];
+#pragma unroll
+        for (int q = 0; q < kChunk; ++q) m[q] = (int)rec[min(b0 + q * kSlots, nb - 1)].x;
+#pragma unroll
+        for (int q = 0; q < kChunk; ++q) mx = m[q] > mx ? m[q] : mx;
+      }
+      int o;
+      o = perm<kQuadX1>(mx); mx = o > mx ? o : mx;
+      o = perm<kQuadX2>(mx); mx = o > mx ? o : mx;
+      o = perm<kHalfMirror>(mx); mx = o > mx ? o : mx;
+      o = perm<kMirror>(mx); mx = o > mx ? o : mx;
+      const IntScale sc = int_row_scale(p.unit_m, p.unit_e, p.step_m[row], p.step_e[row]);
+      uint64_t S = 0;
+      for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
+        uint4 r[kChunk];
+#pragma unroll
+        for (int q = 0; q < kChunk; ++q) r[q] = rec[min(b0 + q * kSlots, nb - 1)];
+#pragma unroll
+        for (int q = 0; q < kChunk; ++q) {
+          if (b0 + q * kSlots < nb) {
+            const uint64_t R = iexp_q30(int_nats((uint32_t)mx - r[q].x, sc));
+            // rnd(S_b R, 30) with S_b < 2^38 split at bit 32: both products fit
+            S += ((uint64_t)r[q].z * R << 2) + rnd64((uint64_t)r[q].y * R, kExpFrac);
+          }
+        }
+      }
+      S += perm64<kQuadX1>(S);
+      S += perm64<kQuadX2>(S);
+      S += perm64<kHalfMirror>(S);
+      S += perm64<kMirror>(S);
+      if (slot == 0) {
+        const int tgt = p.target[row];
+        int64_t lp = INT64_MIN;
+        if (tgt >= 0 && tgt < p.V && sc.m != 0u) {
+          const uint64_t Tt = int_nats((uint32_t)mx - (uint32_t)p.zt[row], sc);
+          const uint64_t L = rnd64((uint64_t)iln_q30(S), kExpFrac - kNatsFrac);
+          const uint64_t nl = Tt + L;  // < 2^63 + 2^40: no wrap
+          lp = nl > (uint64_t)INT64_MAX ? -INT64_MAX : -(int64_t)nl;
+        }
+        p.logprob_q[row] = lp;
       }
     } else {
       // pass 1: the row max (exact); pass 2: the sum in slot order
@@ -909,6 +1093,106 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
           if (row < p.B && blk < p.nblocks) p.records[(int64_t)row * p.nblocks + blk] = t2_pack(t);
         }
       }
+    } else if constexpr (EPI == kLseInt) {
+      // exchange areas for one 32-row tile per wave row: block-part maxima
+      // [WAVES_M * 32][WAVES_N] and block-part sums [WAVES_M * 32][WAVES_N]
+      int *xmax = (int *)smem;
+      uint64_t *xsum = (uint64_t *)(smem + T::WAVES_M * 32 * T::WAVES_N * 4);
+      const int xbase = wm * 32;
+      static_for<0, T::WM>([&](auto mt_) __attribute__((always_inline)) {
+        constexpr int mt = decltype(mt_)::value;
+        const int lbase = wm * T::WM * 32 + mt * 32;  // first local row of this m-tile
+        // per row value: target and logit scale
+        int tgt[16];
+        IntScale sc[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = min(m0 + lbase + acc_row(v, h), p.B - 1);  // rows past B: any scale
+          tgt[v] = m0 + lbase + acc_row(v, h) < p.B ? p.target[row] : -1;
+          sc[v] = int_row_scale(p.unit_m, p.unit_e, p.step_m[row], p.step_e[row]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < T::WN; ++nt) {
+          const int col = wcol0 + nt * 32 + j;
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (col == tgt[v]) p.zt[m0 + lbase + acc_row(v, h)] = (int)acc[mt][nt][v];
+        }
+#pragma unroll
+        for (int b = 0; b < T::BPW; ++b) {
+          // block max (exact), in every lane
+          int mx[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            int m = INT_MIN;
+#pragma unroll
+            for (int k = 0; k < T::NTB; ++k) {
+              const int col = wcol0 + (b * T::NTB + k) * 32 + j;
+              const int z = acc[mt][b * T::NTB + k][v];
+              if (col < p.V && z > m) m = z;
+            }
+            mx[v] = allmax32(m);
+          }
+          if constexpr (T::PARTS > 1) {
+            if (j < 16) {
+              int mine = mx[0];
+#pragma unroll
+              for (int v = 1; v < 16; ++v) mine = (j == v) ? mx[v] : mine;
+              xmax[(xbase + acc_row(j, h)) * T::WAVES_N + wn] = mine;
+            }
+            __syncthreads();
+            const int g0 = wn - wn % T::PARTS;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int xrow = xbase + acc_row(v, h);
+              int m = xmax[xrow * T::WAVES_N + g0];
+#pragma unroll
+              for (int pp = 1; pp < T::PARTS; ++pp) {
+                const int o = xmax[xrow * T::WAVES_N + g0 + pp];
+                m = o > m ? o : m;
+              }
+              mx[v] = m;
+            }
+          }
+          // integer exps of (block max - z), summed exactly
+          LseI part[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            uint64_t e = 0;
+#pragma unroll
+            for (int k = 0; k < T::NTB; ++k) {
+              const int col = wcol0 + (b * T::NTB + k) * 32 + j;
+              const int z = acc[mt][b * T::NTB + k][v];
+              const uint32_t ek = iexp_q30(int_nats((uint32_t)mx[v] - (uint32_t)z, sc[v]));
+              e += col < p.V ? ek : 0u;
+            }
+            part[v] = lse_i(mx[v], e);
+          }
+          const LseI r = reduce_scatter(part, j);
+          const int lrow = lbase + acc_row(u, h);  // local row this lane ends with
+          const int blk = wcol0 / kBlockCols + b;
+          if constexpr (T::PARTS > 1) {
+            if (!dup) xsum[(xbase + acc_row(u, h)) * T::WAVES_N + wn] = r.sum();
+            __syncthreads();
+            if (wn % T::PARTS == 0 && !dup) {
+              uint64_t sum = 0;
+#pragma unroll
+              for (int pp = 0; pp < T::PARTS; ++pp)
+                sum += xsum[(xbase + acc_row(u, h)) * T::WAVES_N + wn + pp];
+              const int row = m0 + lrow;
+              if (row < p.B && blk < p.nblocks)
+                p.records[(int64_t)row * p.nblocks + blk] =
+                    make_uint4((unsigned)r.m, (unsigned)sum, (unsigned)(sum >> 32), 0u);
+            }
+            __syncthreads();
+          } else {
+            const int row = m0 + lrow;
+            if (!dup && row < p.B && blk < p.nblocks)
+              p.records[(int64_t)row * p.nblocks + blk] =
+                  make_uint4((unsigned)r.m, r.lo, r.hi, 0u);
+          }
+        }
+      });
     } else {  // kLse
       // exchange areas for one 32-row tile per wave row: block-part maxima
       // [WAVES_M * 32][WAVES_N] and partial sums [WAVES_M * 32][WAVES_N][32]
@@ -1084,6 +1368,68 @@ __global__ __launch_bounds__(64) void lmhead_gate_kernel(GateParams g) {
   }
 }
 
+// ------------------------------------------------ per-token quantisation
+// One workgroup per row of int32 values x ("Integer-Only Arithmetic", section
+// "DetLLM": each token quantised from its own values, so a row's bits never
+// depend on the batch).  a = max |x| (exact); the step D = M 2^E is the least
+// number with a 15-bit mantissa (2^14 <= M < 2^15) whose 127 multiple covers
+// a; q = sign(x) floor(|x| / D + 1/2) (half away from zero), |q| <= 127.  A
+// zero row gives q = 0 and D = 2^14 2^-14 = 1.
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const int32_t *x, int64_t H, int8_t *q,
+                                                            int32_t *step_m, int32_t *step_e) {
+  __shared__ unsigned s_max[4];
+  const int64_t row = blockIdx.x;
+  const int32_t *xr = x + row * H;
+  int8_t *qr = q + row * H;
+  const int tid = threadIdx.x;
+  auto mag = [](int32_t v) -> uint32_t { return v < 0 ? 0u - (uint32_t)v : (uint32_t)v; };
+  uint32_t a = 0;
+  for (int64_t i = tid; i < H; i += 256) a = max(a, mag(xr[i]));
+  for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off));
+  if ((tid & 63) == 0) s_max[tid >> 6] = a;
+  __syncthreads();
+  a = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+  int M = 1 << 14, E = -14;
+  if (a != 0u) {
+    // e = floor(log2(a / 127)) from the bit length b of a: 127 2^(b-7) < 2^b <= a
+    // always, and 127 2^(b-6) <= a iff 64 a >= 127 2^b
+    const int b = 31 - __clz((int)a);
+    const int e = ((uint64_t)a << 6) >= ((uint64_t)127 << b) ? b - 6 : b - 7;
+    E = e - 14;
+    uint64_t mm;
+    if (E <= 0) {
+      mm = (((uint64_t)a << (-E)) + 126u) / 127u;  // ceil(a 2^-E / 127)
+    } else {
+      const uint64_t d = (uint64_t)127 << E;
+      mm = ((uint64_t)a + d - 1) / d;
+    }
+    if (mm == (1u << 15)) {
+      mm = 1u << 14;
+      E += 1;
+    }
+    M = (int)mm;
+  }
+  // q = floor((2 n + D) / (2 D)) with n = |x| 2^max(0, -E), D = M 2^max(0, E);
+  // the quotient is at most 127, found bit by bit
+  const int ls = E < 0 ? -E : 0;
+  const uint64_t D2 = (uint64_t)M << (E > 0 ? E + 1 : 1);
+  for (int64_t i = tid; i < H; i += 256) {
+    const int32_t v = xr[i];
+    const uint64_t num = ((uint64_t)mag(v) << (ls + 1)) + (D2 >> 1);
+    uint32_t qq = 0;
+#pragma unroll
+    for (int bit = 6; bit >= 0; --bit) {
+      const uint32_t t = qq | (1u << bit);
+      if ((uint64_t)t * D2 <= num) qq = t;
+    }
+    qr[i] = (int8_t)(v < 0 ? -(int)qq : (int)qq);
+  }
+  if (tid == 0) {
+    step_m[row] = M;
+    step_e[row] = E;
+  }
+}
+
 // ---------------------------------------------------------- small kernels
 __global__ void compare_words_kernel(const unsigned *a, const unsigned *b, int64_t n,
                                      unsigned long long *mismatches) {
@@ -1136,6 +1482,12 @@ hipError_t launch_tile(int epi, const Params &p, hipStream_t s) {
     case kSample:
       hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kSample, FUSED>), grid, block, 0, s, p);
       break;
+    case kLseInt:
+      if constexpr (MODE == 1)
+        hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kLseInt, FUSED>), grid, block, 0, s, p);
+      else
+        return hipErrorInvalidValue;
+      break;
     default:
       hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kLse, FUSED>), grid, block, 0, s, p);
       break;
@@ -1148,6 +1500,8 @@ hipError_t launch_tile(int epi, const Params &p, hipStream_t s) {
       hipLaunchKernelGGL((lmhead_merge_kernel<MODE, kTop2>), mgrid, dim3(256), 0, s, p);
     else if (epi == kSample)
       hipLaunchKernelGGL((lmhead_merge_kernel<MODE, kSample>), mgrid, dim3(256), 0, s, p);
+    else if (MODE == 1 && epi == kLseInt)
+      hipLaunchKernelGGL((lmhead_merge_kernel<1, kLseInt>), mgrid, dim3(256), 0, s, p);
     else
       hipLaunchKernelGGL((lmhead_merge_kernel<MODE, kLse>), mgrid, dim3(256), 0, s, p);
   }
@@ -1207,6 +1561,13 @@ hipError_t launch(int mode, int epi, const Plan &plan, const Params &p, hipStrea
 
 hipError_t launch_gate(const GateParams &g, int64_t B, hipStream_t s) {
   hipLaunchKernelGGL(lmhead_gate_kernel, dim3((unsigned)B), dim3(64), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const int32_t *x, int64_t B, int64_t H, int8_t *q, int32_t *step_m,
+                           int32_t *step_e, hipStream_t s) {
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)B), dim3(256), 0, s, x, H, q, step_m,
+                     step_e);
   return hipGetLastError();
 }
 

@@ -31,6 +31,9 @@ SIGNATURES = {
                              _SZ, _P], _I),
     "lmhead_sample_gumbel": ([_I, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, _P, _P,
                               _P, _P, _SZ, _P], _I),
+    "lmhead_quantize_rows": ([_P, _I64, _I64, _P, _P, _P, _P], _I),
+    "lmhead_logprob_int": ([_P, _P, _I64, _I64, _I64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
+                            _P, _P, _SZ, _P], _I),
     "lmhead_self_check_bytes": ([_I, _I64, _I64, _I64], _SZ),
     "lmhead_self_check": ([_I, _P, _P, _I64, _I64, _I64, _P, _SZ, _P, _P], _I),
     "lmhead_status_string": ([_I], ctypes.c_char_p),
@@ -170,6 +173,50 @@ def logprob(x: torch.Tensor, w: torch.Tensor, target: torch.Tensor,
                                   _ptr(target.contiguous()), _ptr(out), _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(dev))
     _check("lmhead_logprob", st)
+    return out
+
+
+LOGP_FRAC = 24             # lmhead_logprob_int: log-probs in units of 2^-24 nats
+LOGP_INVALID = -2 ** 63    # its value for a target out of range or an invalid scale
+
+
+def quantize_rows(x: torch.Tensor):
+    """Per-token int8 quantisation of int32 rows [B, H]: q [B, H] int8 and the
+    row steps D = step_m 2^step_e ([B] int32 each)."""
+    if x.dtype != torch.int32 or x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be a 2-D int32 device tensor")
+    x = x.contiguous()
+    B, H = x.shape
+    dev = x.device
+    q = torch.empty((B, H), dtype=torch.int8, device=dev)
+    step_m = torch.empty((B,), dtype=torch.int32, device=dev)
+    step_e = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = library().lmhead_quantize_rows(_ptr(x), B, H, _ptr(q), _ptr(step_m), _ptr(step_e),
+                                        _stream(dev))
+    _check("lmhead_quantize_rows", st)
+    return q, step_m, step_e
+
+
+def logprob_int(x: torch.Tensor, w: torch.Tensor, unit: tuple, step_m: torch.Tensor,
+                step_e: torch.Tensor, target: torch.Tensor, ws: torch.Tensor | None = None):
+    """All-integer log p(target[b]) [B] int64 in units of 2^-24 nats of the
+    int8 head; row b's logit scale is unit[0] 2^unit[1] * step_m[b] 2^step_e[b]."""
+    if _mode_of(x, w) != MODE_INT8:
+        raise ValueError("logprob_int takes int8 x and w")
+    B, H, V = _dims(x, w)
+    dev = x.device
+    for name, t in (("step_m", step_m), ("step_e", step_e), ("target", target)):
+        if t.dtype != torch.int32 or t.numel() != B or not t.is_cuda:
+            raise ValueError(f"{name} must be a device int32 tensor of B values")
+    out = torch.empty((B,), dtype=torch.int64, device=dev)
+    need = workspace_bytes(MODE_INT8, B, H, V)
+    if ws is None:
+        ws = workspace(need, dev)
+    st = library().lmhead_logprob_int(_ptr(x), _ptr(w), B, H, V, int(unit[0]), int(unit[1]),
+                                      _ptr(step_m.contiguous()), _ptr(step_e.contiguous()),
+                                      _ptr(target.contiguous()), _ptr(out), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(dev))
+    _check("lmhead_logprob_int", st)
     return out
 
 

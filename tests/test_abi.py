@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(lmhead.SIGNATURES)
@@ -173,6 +173,46 @@ def test_sample_validation(lib):
     assert call(nws=ws_need - 1) == E_WORKSPACE
     assert call(V=1) == E_SHAPE
     assert call(mode=1, H=1 << 17) == E_OVERFLOW
+
+
+def test_quantize_validation(lib):
+    def call(x=A, B=4, H=100, q=A2, m=A, e=A):
+        return lib.lmhead_quantize_rows(x, B, H, q, m, e, S)
+
+    assert call(x=None) == E_NULL
+    assert call(q=None) == E_NULL
+    assert call(m=None) == E_NULL
+    assert call(e=None) == E_NULL
+    assert call(B=0) == E_SHAPE
+    assert call(H=0) == E_SHAPE
+    assert call(B=(1 << 24) + 1) == E_SHAPE
+    assert call(x=ODD) == E_ALIGN
+    assert call(m=ODD) == E_ALIGN
+    assert call(e=ODD) == E_ALIGN
+
+
+def test_logprob_int_validation(lib):
+    ws_need = lib.lmhead_workspace_bytes(1, 4, 64, 1000)
+
+    def call(x=A, w=A, B=4, H=64, V=1000, um=1 << 30, ue=-40, sm=A, se=A, tgt=A, out=A2,
+             ws=A2, nws=ws_need):
+        return lib.lmhead_logprob_int(x, w, B, H, V, um, ue, sm, se, tgt, out, ws, nws, S)
+
+    assert call(x=None) == E_NULL
+    assert call(sm=None) == E_NULL
+    assert call(se=None) == E_NULL
+    assert call(tgt=None) == E_NULL
+    assert call(out=None) == E_NULL
+    assert call(V=1) == E_SHAPE
+    assert call(H=65) == E_SHAPE
+    assert call(H=1 << 17) == E_OVERFLOW
+    assert call(x=MIS) == E_ALIGN
+    assert call(sm=ODD) == E_ALIGN
+    assert call(out=ctypes.c_void_p(0x20004)) == E_ALIGN     # int64 output: 8-byte aligned
+    assert call(um=0) == E_VALUE
+    assert call(um=-5) == E_VALUE
+    assert call(ws=None) == E_WORKSPACE
+    assert call(nws=ws_need - 1) == E_WORKSPACE
 
 
 def test_self_check_validation(lib):
