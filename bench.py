@@ -66,7 +66,7 @@ class Caller:
     launch well under the kernel time; torch allocates nothing in the loop)."""
 
     def __init__(self, torch, lmhead, x_list, w_list, B, H, V, mode=0, kind="greedy",
-                 target=None, scale=None, round_bf16=0, tau=0.0):
+                 target=None, scale=None, round_bf16=0, tau=0.0, steps=None, unit=None):
         self.torch = torch
         lib = lmhead.library()
         dev = x_list[0].device
@@ -114,6 +114,22 @@ class Caller:
                 self.calls.append((lib.lmhead_logprob, (
                     mode, P(xx), P(ww), B, H, V, P(scale), P(target), P(out), P(self.ws),
                     ws_bytes, self.stream)))
+        elif kind == "logprob_int":
+            out = torch.empty((B,), dtype=torch.int64, device=dev)
+            sm, se = steps
+            self.keep = (out, sm, se)
+            for xx, ww in zip(x_list, w_list):
+                self.calls.append((lib.lmhead_logprob_int, (
+                    P(xx), P(ww), B, H, V, int(unit[0]), int(unit[1]), P(sm), P(se), P(target),
+                    P(out), P(self.ws), ws_bytes, self.stream)))
+        elif kind == "quantize":
+            q = torch.empty((B, H), dtype=torch.int8, device=dev)
+            sm = torch.empty((B,), dtype=torch.int32, device=dev)
+            se = torch.empty((B,), dtype=torch.int32, device=dev)
+            self.keep = (q, sm, se)
+            for xx in x_list:
+                self.calls.append((lib.lmhead_quantize_rows, (P(xx), B, H, P(q), P(sm), P(se),
+                                                              self.stream)))
         elif kind == "logits":
             out = torch.empty((B, V), dtype=torch.float32 if mode == 0 else torch.int32, device=dev)
             self.keep = (out,)
@@ -408,6 +424,33 @@ def extras(torch, lmhead, synth, bf16, x, w_copies, d):
                                                   mode="int8")}
         r = res[f"int8_b{B}"]["roofline"]
         log(f"int8 B={B}: {tt * 1e6:.1f} us, {r['bound']} {100 * r['frac']:.1f}%")
+
+    # the all-integer path at the same shape: per-token quantisation of int32
+    # hidden rows, then the integer log-softmax (log p in Q.24), and the float
+    # log-prob of the int8 head for comparison
+    hid = torch.from_numpy(synth.hidden_int32(synth.seed_of(5, 6), 512, Hi)).to(x.device)
+    ti = torch.from_numpy(synth.target_ids(synth.seed_of(5, 3), 512, Vi)).to(x.device)
+    cq = Caller(torch, lmhead, [hid], [None], 512, Hi, Vi, mode=1, kind="quantize")
+    tq = time_calls(torch, cq, 50)
+    res["int_quantize_b512"] = {"us_per_call": tq * 1e6,
+                                "gbps": 512 * Hi * 5 / tq / 1e9}
+    log(f"int quantize 512 x {Hi}: {tq * 1e6:.1f} us")
+    qi, smi, sei = cq.keep
+    for B in (1, 512):
+        c = Caller(torch, lmhead, [qi[:B].contiguous()], wi, B, Hi, Vi, mode=1,
+                   kind="logprob_int", target=ti[:B].contiguous(),
+                   steps=(smi[:B].contiguous(), sei[:B].contiguous()), unit=synth.INT_UNIT)
+        tt = time_calls(torch, c, 50)
+        cf = Caller(torch, lmhead, [xi[:B].contiguous()], wi, B, Hi, Vi, mode=1, kind="logprob",
+                    target=ti[:B].contiguous(), scale=si[:B])
+        tf = time_calls(torch, cf, 50)
+        res[f"int_logprob_b{B}"] = {"us_per_call": tt * 1e6, "rows_per_s": B / tt,
+                                    "float_logprob_us": tf * 1e6,
+                                    "roofline": roofline(B, Hi, Vi, tt, esize=1,
+                                                         out_bytes_per_row=20, mode="int8")}
+        r = res[f"int_logprob_b{B}"]["roofline"]
+        log(f"integer log-prob B={B}: {tt * 1e6:.1f} us ({r['bound']} {100 * r['frac']:.1f}%), "
+            f"float log-prob of the int8 head {tf * 1e6:.1f} us")
     return res
 
 

@@ -998,17 +998,20 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
             const uint64_t ctr = 32u * (uint64_t)(col0 >> 7) + (uint64_t)j;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const int row = min(m0 + wm * T::WM * 32 + mt * 32 + acc_row(v, h), p.B - 1);
-              float cr = p.inv_t;
-              if constexpr (MODE == 1) cr = (p.scale ? p.scale[row] : 1.0f) * p.inv_t;
-              uint64_t words[4];
-              philox4x64(ctr, p.seed[row], (uint64_t)p.position[row], words);
+              const int row = m0 + wm * T::WM * 32 + mt * 32 + acc_row(v, h);
+              // rows past B (tile padding) are never ranked: skip their noise
+              if (row < p.B) {
+                float cr = p.inv_t;
+                if constexpr (MODE == 1) cr = (p.scale ? p.scale[row] : 1.0f) * p.inv_t;
+                uint64_t words[4];
+                philox4x64(ctr, p.seed[row], (uint64_t)p.position[row], words);
 #pragma unroll
-              for (int k = 0; k < T::NTB; ++k) {
-                const int nt = b * T::NTB + k;
-                const float y = (float)acc[mt][nt][v] * cr +
-                                gumbel_of(word_of(words, ((col0 >> 5) + k) & 3));
-                acc[mt][nt][v] = vfrom<val_t>(__float_as_int(y));
+                for (int k = 0; k < T::NTB; ++k) {
+                  const int nt = b * T::NTB + k;
+                  const float y = (float)acc[mt][nt][v] * cr +
+                                  gumbel_of(word_of(words, ((col0 >> 5) + k) & 3));
+                  acc[mt][nt][v] = vfrom<val_t>(__float_as_int(y));
+                }
               }
               // one row value at a time: interleaving the 16 Philox chains would
               // buy nothing here and run out of registers
@@ -1154,17 +1157,20 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
               mx[v] = m;
             }
           }
-          // integer exps of (block max - z), summed exactly
+          // integer exps of (block max - z), summed exactly; rows past B (tile
+          // padding) are never written, so their exps are skipped
           LseI part[16];
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             uint64_t e = 0;
+            if (m0 + lbase + acc_row(v, h) < p.B) {
 #pragma unroll
-            for (int k = 0; k < T::NTB; ++k) {
-              const int col = wcol0 + (b * T::NTB + k) * 32 + j;
-              const int z = acc[mt][b * T::NTB + k][v];
-              const uint32_t ek = iexp_q30(int_nats((uint32_t)mx[v] - (uint32_t)z, sc[v]));
-              e += col < p.V ? ek : 0u;
+              for (int k = 0; k < T::NTB; ++k) {
+                const int col = wcol0 + (b * T::NTB + k) * 32 + j;
+                const int z = acc[mt][b * T::NTB + k][v];
+                const uint32_t ek = iexp_q30(int_nats((uint32_t)mx[v] - (uint32_t)z, sc[v]));
+                e += col < p.V ? ek : 0u;
+              }
             }
             part[v] = lse_i(mx[v], e);
           }
