@@ -1467,7 +1467,10 @@ __global__ void reverse_rows_kernel(const char *src, char *dst, int64_t rows, in
 #ifndef LMH_V3_TILE
 #define LMH_V3_TILE 256, 128, 4, 2, BKB, 2, 4
 #endif
-template <int BKB> using V0 = Tile<32, 128, 1, 4, BKB, 2, 4>;
+#ifndef LMH_V0_TILE
+#define LMH_V0_TILE 32, 128, 1, 4, BKB, 2, 3
+#endif
+template <int BKB> using V0 = Tile<LMH_V0_TILE>;
 template <int BKB> using V1 = Tile<64, 128, 2, 2, BKB, 2, 3>;
 template <int BKB> using V2 = Tile<128, 128, 2, 2, BKB, 2, 4>;
 template <int BKB> using V3 = Tile<LMH_V3_TILE>;
