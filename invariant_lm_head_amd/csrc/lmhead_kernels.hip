@@ -1461,9 +1461,15 @@ __global__ void reverse_rows_kernel(const char *src, char *dst, int64_t rows, in
 //   0: 32 x 128  (batch <= 32, fold fused)   1: 64 x 128  (<= 64)
 //   2: 128 x 128 (<= 128)                    3: 256 x 128 (<= 256)
 //   4: 256 x 256 (> 256)
+//   5: 32 x 256, 6: 64 x 256 in place of 0 and 1 when the 128-column grid
+//      would take more than two rounds of the 256 CUs (large vocabularies):
+//      half the workgroups, so half the pipeline fills and tails per CU
 #ifndef LMH_V4_TILE
 #define LMH_V4_TILE 256, 256, 4, 2, 128, 2, 3
 #endif
+template <int BKB> using V0w = Tile<32, 256, 1, 4, BKB, 2, 3>;
+template <int BKB> using V1w = Tile<64, 256, 2, 2, BKB, 2, 3>;
+constexpr int kCUs = 256;  // MI355X compute units
 #ifndef LMH_V3_TILE
 #define LMH_V3_TILE 256, 128, 4, 2, BKB, 2, 4
 #endif
@@ -1471,7 +1477,10 @@ __global__ void reverse_rows_kernel(const char *src, char *dst, int64_t rows, in
 #define LMH_V0_TILE 32, 128, 1, 4, BKB, 2, 3
 #endif
 template <int BKB> using V0 = Tile<LMH_V0_TILE>;
-template <int BKB> using V1 = Tile<64, 128, 2, 2, BKB, 2, 3>;
+#ifndef LMH_V1_TILE
+#define LMH_V1_TILE 64, 128, 2, 2, BKB, 2, 3
+#endif
+template <int BKB> using V1 = Tile<LMH_V1_TILE>;
 template <int BKB> using V2 = Tile<128, 128, 2, 2, BKB, 2, 4>;
 template <int BKB> using V3 = Tile<LMH_V3_TILE>;
 using V4 = Tile<LMH_V4_TILE>;
@@ -1534,6 +1543,12 @@ hipError_t launch_mode(int epi, const Plan &plan, const Params &p, hipStream_t s
     case 3:
       if (plan.bkb == 128) return launch_tile<V3<128>, MODE, false>(epi, p, s);
       return launch_tile<V3<64>, MODE, false>(epi, p, s);
+    case 5:
+      if (plan.bkb == 128) return launch_tile<V0w<128>, MODE, true>(epi, p, s);
+      return launch_tile<V0w<64>, MODE, true>(epi, p, s);
+    case 6:
+      if (plan.bkb == 128) return launch_tile<V1w<128>, MODE, false>(epi, p, s);
+      return launch_tile<V1w<64>, MODE, false>(epi, p, s);
     default:
       if (plan.bkb == V4::BKB) return launch_tile<V4, MODE, false>(epi, p, s);
       return launch_tile<V4s, MODE, false>(epi, p, s);
@@ -1546,10 +1561,15 @@ Plan plan_for(int64_t B, int64_t rowbytes, int64_t V) {
   Plan pl;
   const int bkb256 = rowbytes % 256 == 0 ? 256 : rowbytes % 128 == 0 ? 128 : 64;
   const int bkb128 = rowbytes % 128 == 0 ? 128 : 64;
-  if (B <= 32) {
-    pl.variant = 0; pl.bm = 32; pl.bn = 128; pl.bkb = bkb256;
+  const bool wide = (V + 127) / 128 > 2 * kCUs;  // the 128-column grid takes > 2 rounds
+  if (B <= 32 && wide) {
+    pl.variant = 5; pl.bm = V0w<128>::BM; pl.bn = V0w<128>::BN; pl.bkb = bkb128;
+  } else if (B <= 32) {
+    pl.variant = 0; pl.bm = V0<256>::BM; pl.bn = V0<256>::BN; pl.bkb = bkb256;
+  } else if (B <= 64 && wide) {
+    pl.variant = 6; pl.bm = V1w<128>::BM; pl.bn = V1w<128>::BN; pl.bkb = bkb128;
   } else if (B <= 64) {
-    pl.variant = 1; pl.bm = 64; pl.bn = 128; pl.bkb = bkb256;
+    pl.variant = 1; pl.bm = V1<256>::BM; pl.bn = V1<256>::BN; pl.bkb = bkb256;
   } else if (B <= 128) {
     pl.variant = 2; pl.bm = 128; pl.bn = 128; pl.bkb = bkb128;
   } else if (B <= 256) {
