@@ -755,6 +755,23 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
   }
 }
 
+// Store of one block record.  In a fused launch the records are read by the
+// last workgroup, possibly on another XCD, after the release / acquire pair of
+// the ticket; written through to the agent coherence point (agent-scope atomic
+// stores), they leave the release's L2 writeback next to nothing to do
+// (measured: batch 1 and 8 about 0.6 us faster).  The merge kernel reads them
+// after the launch ends, so there they are plain stores.
+template <bool THROUGH> __device__ __forceinline__ void put_record(uint4 *d, uint4 v) {
+  if constexpr (THROUGH) {
+    __hip_atomic_store((unsigned long long *)d, ((unsigned long long)v.y << 32) | v.x,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store((unsigned long long *)d + 1, ((unsigned long long)v.w << 32) | v.z,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *d = v;
+  }
+}
+
 // ------------------------------------------------------------------ kernel
 template <class T, int MODE, int EPI, bool FUSED>
 __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
@@ -1041,7 +1058,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
               const int row = m0 + lrow;
               const int blk = wcol0 / kBlockCols + b;
               if (!dup && row < p.B && blk < p.nblocks)
-                p.records[(int64_t)row * p.nblocks + blk] = t2_pack(r);
+                put_record<FUSED>(&p.records[(int64_t)row * p.nblocks + blk], t2_pack(r));
             } else {
               if (!dup) xch[lrow * T::WAVES_N + wn] = t2_pack(r);
             }
@@ -1073,7 +1090,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
               const int row = m0 + lrow;
               const int blk = wcol0 / kBlockCols + b;
               if (!dup && row < p.B && blk < p.nblocks)
-                p.records[(int64_t)row * p.nblocks + blk] = t2_pack(r);
+                put_record<FUSED>(&p.records[(int64_t)row * p.nblocks + blk], t2_pack(r));
             } else {
               if (!dup) xch[lrow * T::WAVES_N + wn] = t2_pack(r);
             }
@@ -1093,7 +1110,8 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
           for (int pp = 1; pp < T::PARTS; ++pp)
             t = t2_merge(t, t2_unpack(xch[lrow * T::WAVES_N + wn + pp]));
           const int blk = wcol0 / kBlockCols;
-          if (row < p.B && blk < p.nblocks) p.records[(int64_t)row * p.nblocks + blk] = t2_pack(t);
+          if (row < p.B && blk < p.nblocks)
+            put_record<FUSED>(&p.records[(int64_t)row * p.nblocks + blk], t2_pack(t));
         }
       }
     } else if constexpr (EPI == kLseInt) {
@@ -1187,15 +1205,15 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
                 sum += xsum[(xbase + acc_row(u, h)) * T::WAVES_N + wn + pp];
               const int row = m0 + lrow;
               if (row < p.B && blk < p.nblocks)
-                p.records[(int64_t)row * p.nblocks + blk] =
-                    make_uint4((unsigned)r.m, (unsigned)sum, (unsigned)(sum >> 32), 0u);
+                put_record<FUSED>(&p.records[(int64_t)row * p.nblocks + blk],
+                                  make_uint4((unsigned)r.m, (unsigned)sum, (unsigned)(sum >> 32), 0u));
             }
             __syncthreads();
           } else {
             const int row = m0 + lrow;
             if (!dup && row < p.B && blk < p.nblocks)
-              p.records[(int64_t)row * p.nblocks + blk] =
-                  make_uint4((unsigned)r.m, r.lo, r.hi, 0u);
+              put_record<FUSED>(&p.records[(int64_t)row * p.nblocks + blk],
+                                make_uint4((unsigned)r.m, r.lo, r.hi, 0u));
           }
         }
       });
@@ -1301,8 +1319,8 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
             const int row = m0 + lbase + acc_row(u, h);
             const int blk = wcol0 / kBlockCols + b;
             if (!dup && row < p.B && blk < p.nblocks)
-              p.records[(int64_t)row * p.nblocks + blk] =
-                  make_uint4((unsigned)r.m, __float_as_uint(r.s), 0u, 0u);
+              put_record<FUSED>(&p.records[(int64_t)row * p.nblocks + blk],
+                                make_uint4((unsigned)r.m, __float_as_uint(r.s), 0u, 0u));
           }
           if constexpr (T::PARTS > 1) __syncthreads();
         }
