@@ -157,7 +157,8 @@ def test_int8_extremes_exact(o):
 # ---------------------------------------------------------------- edges
 @pytest.mark.parametrize("mode", ["bf16", "int8"])
 @pytest.mark.parametrize("B,H,V", [(1, 64, 2), (2, 64, 3), (5, 128, 17), (17, 64, 129),
-                                   (70, 192, 130), (300, 64, 1000), (1, 4096, 257)])
+                                   (70, 192, 130), (300, 64, 1000), (1, 4096, 257),
+                                   (5, 64, 70001), (40, 128, 70001)])
 def test_edge_shapes(o, mode, B, H, V):
     rng = np.random.default_rng(B * 1000 + V)
     t = rng.integers(0, V, B).astype(np.int32)
@@ -183,6 +184,31 @@ def test_edge_shapes(o, mode, B, H, V):
         assert np.array_equal(host(margin).view(np.int32), o_margin.view(np.int32))
         lp = host(lmhead.logprob(gx, gw, gpu(t), row_scale=gs))
         assert np.max(np.abs(lp - o.logprob_i8(x, w, t, s))) <= TOL
+
+
+def test_wide_plans_batch_invariant():
+    """A vocabulary of more than 512 blocks (70,001 columns) runs 256-column
+    tiles at batches up to 64 and the usual tiles above: greedy, log-prob and
+    sampled draws of every row have the same bits at batch 1, 17, 40 and 300."""
+    rng = np.random.default_rng(77)
+    B, H, V = 300, 128, 70001
+    x = gpu_bf16(synth.bf16_from_f32(rng.standard_normal((B, H)).astype(np.float32)))
+    w = gpu_bf16(synth.bf16_from_f32((0.1 * rng.standard_normal((V, H))).astype(np.float32)))
+    t = gpu(rng.integers(0, V, B).astype(np.int32))
+    seed = gpu(rng.integers(0, 2 ** 62, B, dtype=np.int64).astype(np.uint64).view(np.int64))
+    pos = gpu(np.arange(B, dtype=np.int64))
+
+    def run(n):
+        ids, vals, margin, _ = lmhead.greedy_top2(x[:n].contiguous(), w)
+        lp = lmhead.logprob(x[:n].contiguous(), w, t[:n].contiguous())
+        tok, val, gap = lmhead.sample_gumbel(x[:n].contiguous(), w, 0.7, seed[:n].contiguous(),
+                                             pos[:n].contiguous())
+        return [host(a).view(np.int32) for a in (ids, vals, margin, lp, tok, val, gap)]
+
+    full = run(B)
+    for n in (1, 17, 40):
+        for got, ref in zip(run(n), full):
+            assert np.array_equal(got, ref[:n]), n
 
 
 def test_exact_ties_go_to_lowest_id():
