@@ -193,9 +193,14 @@ def cpu_baseline():
     t0 = time.perf_counter()
     oracle.greedy_bf16(d["x"], d["w"], nthreads=n)
     dt = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    oracle.greedy_bf16(d["x"][:16], d["w"], nthreads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": 256 / dt, "unit": "rows/s", "cores": n, "kind": "oracle",
             "sample": "float64 greedy top-2 of rows 0..255 of the H=2048, V=32000 head "
-                      f"({dt:.1f} s wall on {n} threads)"}
+                      f"({dt:.1f} s wall on {n} threads)",
+            "single_thread_rows_per_s": 16 / dt1,
+            "single_thread_sample": f"rows 0..15 on one thread ({dt1:.1f} s)"}
 
 
 def main():
