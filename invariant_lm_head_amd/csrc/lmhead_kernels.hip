@@ -556,11 +556,41 @@ template <int P, int R, class T> __device__ __forceinline__ void rs_step(T (&a)[
     a[i] = combine(keep, perm<P>(send));
   }
 }
+// The first step (partners j and j^16, the two 16-lane rows of a wave half)
+// without selects: v_permlane16_swap exchanges the odd rows of its first
+// operand with the even rows of its second.  With x = a[i], y = a[i + 8] it
+// leaves, in an even-row lane, its own a[i] and its partner's a[i]; in an
+// odd-row lane, its partner's a[i + 8] and its own a[i + 8].  combine() is
+// symmetric (an exact top-2 of a union, or a commutative sum), so the result
+// equals rs_step<kX16, 16> bit for bit.
+template <class T> __device__ __forceinline__ void swap_rows16(T &x, T &y) {
+  static_assert(sizeof(T) % 4 == 0, "32-bit words");
+  constexpr int N = sizeof(T) / 4;
+  unsigned xw[N], yw[N];
+  __builtin_memcpy(xw, &x, sizeof(T));
+  __builtin_memcpy(yw, &y, sizeof(T));
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const auto r = __builtin_amdgcn_permlane16_swap(xw[k], yw[k], false, false);
+    xw[k] = r[0];
+    yw[k] = r[1];
+  }
+  __builtin_memcpy(&x, xw, sizeof(T));
+  __builtin_memcpy(&y, yw, sizeof(T));
+}
+template <class T> __device__ __forceinline__ void rs_rows16(T (&a)[16]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    swap_rows16(a[i], a[i + 8]);
+    a[i] = combine(a[i], a[i + 8]);
+  }
+}
+
 // 16 row values on each of the 32 column lanes -> lane j holds row value
 // u(j) = 8 b4 + 4 b3 + 2 b2 + b1 (b = bits of j) combined over all 32 columns,
 // in the pairing order j^16, j^15, j^7, j^2, j^1 (the same for every row).
 template <class T> __device__ __forceinline__ T reduce_scatter(T (&a)[16], int j) {
-  rs_step<kX16, 16>(a, j);
+  rs_rows16(a);
   rs_step<kMirror, 8>(a, j);
   rs_step<kHalfMirror, 4>(a, j);
   rs_step<kQuadX2, 2>(a, j);
