@@ -132,6 +132,7 @@ lmhead_status lmhead_logprob(int mode, const void *x, const void *w, int64_t B, 
  *      them: same MFMA instruction and k order) and re-ranks them, lowest id on
  *      a tie; top_val and margin of that row then hold float32 logits.
  *   gated[b] = 1 for a recomputed row, 0 otherwise.
+ * Step 2 runs inside the fold of step 1 (no extra launch).
  * tau >= 0 (0 recomputes nothing, +inf every row); NaN or negative tau gives
  * LMHEAD_E_VALUE.  ws / ws_bytes as for lmhead_greedy_top2. */
 lmhead_status lmhead_greedy_gated(int mode, const void *x, const void *w, int64_t B, int64_t H,

@@ -108,10 +108,13 @@ static lmhead_status bind_workspace(lmh::Params &p, void *ws, size_t ws_bytes, i
   return LMHEAD_OK;
 }
 
-lmhead_status lmhead_greedy_top2(int mode, int round, const void *x, const void *w, int64_t B,
-                                 int64_t H, int64_t V, const float *row_scale, int32_t *top_id,
-                                 float *top_val, float *margin, int32_t *top_raw, void *ws,
-                                 size_t ws_bytes, void *stream) {
+namespace {
+// greedy top-2; with gated != null (bf16-output head only) the fold re-ranks
+// rows whose margin is below tau on their candidates' float32-head logits
+lmhead_status greedy(int mode, int round, const void *x, const void *w, int64_t B, int64_t H,
+                     int64_t V, const float *row_scale, int32_t *top_id, float *top_val,
+                     float *margin, int32_t *top_raw, float tau, int32_t *gated, void *ws,
+                     size_t ws_bytes, void *stream) {
   lmhead_status st = check_common(mode, round, x, w, B, H, V);
   if (st != LMHEAD_OK) return st;
   if (!top_id || !top_val || !margin) return LMHEAD_E_NULL;
@@ -128,7 +131,18 @@ lmhead_status lmhead_greedy_top2(int mode, int round, const void *x, const void 
   p.top_val = top_val;
   p.margin = margin;
   p.top_raw = mode == LMHEAD_MODE_INT8 ? top_raw : nullptr;
+  p.tau = tau;
+  p.gated = gated;
   return launched(lmh::launch(mode, lmh::kTop2, plan, p, (hipStream_t)stream));
+}
+}  // namespace
+
+lmhead_status lmhead_greedy_top2(int mode, int round, const void *x, const void *w, int64_t B,
+                                 int64_t H, int64_t V, const float *row_scale, int32_t *top_id,
+                                 float *top_val, float *margin, int32_t *top_raw, void *ws,
+                                 size_t ws_bytes, void *stream) {
+  return greedy(mode, round, x, w, B, H, V, row_scale, top_id, top_val, margin, top_raw, 0.0f,
+                nullptr, ws, ws_bytes, stream);
 }
 
 lmhead_status lmhead_logprob(int mode, const void *x, const void *w, int64_t B, int64_t H,
@@ -191,19 +205,8 @@ lmhead_status lmhead_greedy_gated(int mode, const void *x, const void *w, int64_
   if (!gated) return LMHEAD_E_NULL;
   if (!aligned4(gated)) return LMHEAD_E_ALIGN;
   if (!(tau >= 0.0f)) return LMHEAD_E_VALUE;  // NaN or negative
-  st = lmhead_greedy_top2(mode, LMHEAD_ROUND_BF16, x, w, B, H, V, nullptr, top_id, top_val,
-                          margin, nullptr, ws, ws_bytes, stream);
-  if (st != LMHEAD_OK) return st;
-  lmh::GateParams g;
-  g.x = (const char *)x;
-  g.w = (const char *)w;
-  g.rowbytes = row_bytes(mode, H);
-  g.tau = tau;
-  g.top_id = top_id;
-  g.top_val = top_val;
-  g.margin = margin;
-  g.gated = gated;
-  return launched(lmh::launch_gate(g, B, (hipStream_t)stream));
+  return greedy(mode, LMHEAD_ROUND_BF16, x, w, B, H, V, nullptr, top_id, top_val, margin,
+                nullptr, tau, gated, ws, ws_bytes, stream);
 }
 
 lmhead_status lmhead_sample_gumbel(int mode, const void *x, const void *w, int64_t B, int64_t H,

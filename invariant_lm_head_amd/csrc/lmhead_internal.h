@@ -27,6 +27,10 @@ struct Params {
   float *top_val;         // [B, 2]
   float *margin;          // [B]
   int32_t *top_raw;       // [B, 2] int8 only (may be null)
+  // kTop2, bf16-output head: rows with margin < tau are re-ranked on their two
+  // candidates' float32-head logits when gated is not null
+  float tau;
+  int32_t *gated;         // [B] 1 = re-ranked
   float *logprob;         // [B]
   unsigned *tickets;      // [ceil(B/16)] zero on entry and on exit
   int32_t *zt;            // [B] target logit bits (float32 or int32)
@@ -59,17 +63,6 @@ size_t workspace_layout(int64_t B, int64_t V, size_t *off_zt, size_t *off_record
 
 hipError_t launch(int mode, int epilogue, const Plan &plan, const Params &p, hipStream_t s);
 
-// Margin-gated recompute of the two greedy candidates with the float32 head.
-struct GateParams {
-  const char *x, *w;
-  int64_t rowbytes;
-  float tau;
-  int32_t *top_id;  // [B, 2] in: bf16-head candidates; out: re-ranked
-  float *top_val;   // [B, 2]
-  float *margin;    // [B]
-  int32_t *gated;   // [B]
-};
-hipError_t launch_gate(const GateParams &g, int64_t B, hipStream_t s);
 
 // Per-token int8 quantisation of int32 rows (one workgroup per row).
 hipError_t launch_quantize(const int32_t *x, int64_t B, int64_t H, int8_t *q, int32_t *step_m,

@@ -624,6 +624,84 @@ template <int N> __device__ __forceinline__ float tree_sum(const float *e) {
 // Rows [row0, row0 + nrows) of the records, 16 lanes (slots) per row; the
 // caller's threads [0, nthreads) take rows 16 lanes at a time.  Block b goes to
 // slot b mod 16, slots fold ascending, then slots pair j^1, j^2, j^7, j^15.
+// ------------------------------------------------------ gated recompute
+// Margin-gated recompute ("Greedy Decoding Has a Precision Clause", section
+// "Correct the vulnerable token decisions, not every calculation"), run by the
+// fold right after it has written the bf16-output head's top-2 of rows
+// [row0, row0 + nrows), nrows <= 64.  Rows whose margin is below tau are
+// listed; each wave takes up to 16 of them and recomputes their candidates'
+// logits with the float32 head in one MFMA chain: A row i (and i + 16) is
+// listed row i's hidden row, B column 2i / 2i + 1 its first / second
+// candidate's W row, k ascending, the instruction and lane layout of the tile
+// kernel.  An MFMA result depends only on its own A row and B column, so each
+// value equals the float32 head's bits.  The two are then ranked, lowest id on
+// a tie, and the row's outputs replaced.
+__device__ void gate_rows(const Params &p, int row0, int nrows, int tid, int nthreads) {
+  __shared__ int s_rows[64];
+  __shared__ int s_count;
+  __syncthreads();  // the fold's writes of these rows are visible to every wave
+  if (tid < 64) {
+    const bool in = tid < nrows;
+    const int row = row0 + (in ? tid : 0);
+    const bool gate = in && p.margin[row] < p.tau;
+    if (in) p.gated[row] = gate ? 1 : 0;
+    const unsigned long long m = __ballot(gate);
+    if (gate) s_rows[__popcll(m & ((1ull << tid) - 1))] = row;
+    if (tid == 0) s_count = __popcll(m);
+  }
+  __syncthreads();
+  const int G = s_count;
+  const int lane = tid & 63, j = lane & 31, h = lane >> 5;
+  for (int b = tid >> 6; 16 * b < G; b += nthreads >> 6) {
+    const int n = min(16, G - 16 * b);
+    const int ra = s_rows[16 * b + min(j & 15, n - 1)];
+    const int rb = s_rows[16 * b + min(j >> 1, n - 1)];
+    const int cand = p.top_id[2 * rb + (j & 1)];
+    const char *xr = p.x + (int64_t)ra * p.rowbytes + 16 * h;
+    const char *wr = p.w + (int64_t)cand * p.rowbytes + 16 * h;
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+    // the chain is latency-bound: the fragments of GK k-steps are loaded
+    // before their MFMAs, GK = 32 while they last, then 4 (H is a multiple of 64)
+    const int nsteps = (int)(p.rowbytes / 32);
+    auto steps = [&](int k0, auto gk) {
+      constexpr int GK = decltype(gk)::value;
+      i32x4 fa[GK], fb[GK];
+#pragma unroll
+      for (int k = 0; k < GK; ++k) {
+        fa[k] = *(const i32x4 *)(xr + 32 * (k0 + k));
+        fb[k] = *(const i32x4 *)(wr + 32 * (k0 + k));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // every load issued before the first MFMA waits
+#pragma unroll
+      for (int k = 0; k < GK; ++k) acc = Arith<0>::mfma(fa[k], fb[k], acc);
+    };
+    int k0 = 0;
+    for (; k0 + 32 <= nsteps; k0 += 32) steps(k0, std::integral_constant<int, 32>{});
+    for (; k0 < nsteps; k0 += 4) steps(k0, std::integral_constant<int, 4>{});
+    // (A row i, B column c) is value 4 (i >> 3) + (i & 3) of lane 32 ((i >> 2) & 1) + c
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int v = 4 * (i >> 3) + (i & 3), base = 32 * ((i >> 2) & 1) + 2 * i;
+      const float z1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[v]), base));
+      const float z2 =
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[v]), base + 1));
+      if (lane == 0 && i < n) {
+        const int row = s_rows[16 * b + i];
+        const int c1 = p.top_id[2 * row], c2 = p.top_id[2 * row + 1];
+        const bool second = (z2 > z1) | ((z2 == z1) & (c2 < c1));
+        p.top_id[2 * row] = second ? c2 : c1;
+        p.top_id[2 * row + 1] = second ? c1 : c2;
+        const float t1 = second ? z2 : z1, t2 = second ? z1 : z2;
+        p.top_val[2 * row] = t1;
+        p.top_val[2 * row + 1] = t2;
+        p.margin[row] = t1 - t2;
+      }
+    }
+  }
+}
+
 template <int MODE, int EPI>
 __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nthreads) {
   using val_t = typename Arith<MODE>::val_t;
@@ -1372,6 +1450,8 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
       if (!s_last) return;
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       merge_rows<MODE, EPI>(p, m0, min(T::BM, p.B - m0), tid, T::NT);
+      if constexpr (MODE == 0 && EPI == kTop2)
+        if (p.gated) gate_rows(p, m0, min(T::BM, p.B - m0), tid, T::NT);
       if (tid == 0) p.tickets[tm] = 0u;  // leave the workspace zeroed for the next call
     }
   }
@@ -1382,44 +1462,8 @@ template <int MODE, int EPI>
 __global__ __launch_bounds__(256) void lmhead_merge_kernel(Params p) {
   const int row0 = blockIdx.x * (256 / kSlots);
   merge_rows<MODE, EPI>(p, row0, min(256 / kSlots, p.B - row0), threadIdx.x, 256);
-}
-
-// ------------------------------------------------------ gated recompute
-// One wave per row.  A row whose bf16-head margin is below tau recomputes the
-// logits of its two candidates with the float32 head: every k-step feeds the
-// row (A, all 32 MFMA rows) and the candidate W rows (B, MFMA column 0 and 1;
-// the other columns repeat candidate 0) to the same MFMA instruction, with the
-// same k order and lane layout as the contraction kernel, so the values equal
-// the float32 head's bit for bit.  The two are then ranked, lowest id on a tie.
-__global__ __launch_bounds__(64) void lmhead_gate_kernel(GateParams g) {
-  const int row = blockIdx.x;
-  const int lane = threadIdx.x, j = lane & 31, h = lane >> 5;
-  const bool gate = g.margin[row] < g.tau;  // the same in every lane
-  if (lane == 0) g.gated[row] = gate ? 1 : 0;
-  if (!gate) return;
-  const int c1 = g.top_id[2 * row], c2 = g.top_id[2 * row + 1];
-  const char *xr = g.x + (int64_t)row * g.rowbytes + 16 * h;
-  const char *wr = g.w + (int64_t)(j == 1 ? c2 : c1) * g.rowbytes + 16 * h;
-  f32x16 acc;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  const int nsteps = (int)(g.rowbytes / 32);  // a multiple of 4 (H is of 64)
-  for (int k0 = 0; k0 < nsteps; k0 += 4)
-#pragma unroll
-    for (int k = k0; k < k0 + 4; ++k)
-      acc = Arith<0>::mfma(*(const i32x4 *)(xr + 32 * k), *(const i32x4 *)(wr + 32 * k), acc);
-  // MFMA row 0 of column c is value 0 of lane (j = c, h = 0)
-  const float z1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[0]), 0));
-  const float z2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[0]), 1));
-  if (lane == 0) {
-    const bool second = (z2 > z1) | ((z2 == z1) & (c2 < c1));
-    g.top_id[2 * row] = second ? c2 : c1;
-    g.top_id[2 * row + 1] = second ? c1 : c2;
-    const float t1 = second ? z2 : z1, t2 = second ? z1 : z2;
-    g.top_val[2 * row] = t1;
-    g.top_val[2 * row + 1] = t2;
-    g.margin[row] = t1 - t2;
-  }
+  if constexpr (MODE == 0 && EPI == kTop2)
+    if (p.gated) gate_rows(p, row0, min(256 / kSlots, p.B - row0), threadIdx.x, 256);
 }
 
 // ------------------------------------------------ per-token quantisation
@@ -1634,11 +1678,6 @@ Plan plan_for(int64_t B, int64_t rowbytes, int64_t V) {
 
 hipError_t launch(int mode, int epi, const Plan &plan, const Params &p, hipStream_t s) {
   return mode == 0 ? launch_mode<0>(epi, plan, p, s) : launch_mode<1>(epi, plan, p, s);
-}
-
-hipError_t launch_gate(const GateParams &g, int64_t B, hipStream_t s) {
-  hipLaunchKernelGGL(lmhead_gate_kernel, dim3((unsigned)B), dim3(64), 0, s, g);
-  return hipGetLastError();
 }
 
 hipError_t launch_quantize(const int32_t *x, int64_t B, int64_t H, int8_t *q, int32_t *step_m,
