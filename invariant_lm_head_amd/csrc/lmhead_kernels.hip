@@ -702,6 +702,44 @@ __device__ void gate_rows(const Params &p, int row0, int nrows, int tid, int nth
   }
 }
 
+// A row's outputs from its folded top-2 (greedy) or Gumbel top-2 (sampling).
+template <int MODE, int EPI>
+__device__ __forceinline__ void put_top2(const Params &p, int row, const Top2 &t) {
+  using val_t = typename Arith<MODE>::val_t;
+  if constexpr (EPI == kSample) {
+    bool ok = true;
+    if constexpr (MODE == 1) ok = scale_ok(p.scale ? p.scale[row] : 1.0f);
+    const float y1 = okey_value<float>((unsigned)(t.k1 >> 32));
+    const float y2 = okey_value<float>((unsigned)(t.k2 >> 32));
+    const float nan = __builtin_nanf("");
+    p.token[row] = ok ? key_id(t.k1) : -1;
+    if (p.value) p.value[row] = ok ? y1 : nan;
+    if (p.gap) p.gap[row] = ok ? y1 - y2 : nan;
+  } else {
+    const val_t v1 = okey_value<val_t>((unsigned)(t.k1 >> 32));
+    const val_t v2 = okey_value<val_t>((unsigned)(t.k2 >> 32));
+    p.top_id[2 * row] = key_id(t.k1);
+    p.top_id[2 * row + 1] = key_id(t.k2);
+    if constexpr (MODE == 0) {
+      p.top_val[2 * row] = v1;
+      p.top_val[2 * row + 1] = v2;
+      p.margin[row] = v1 - v2;
+    } else {
+      const float s = p.scale ? p.scale[row] : 1.0f;
+      if (p.top_raw) {
+        p.top_raw[2 * row] = v1;
+        p.top_raw[2 * row + 1] = v2;
+      }
+      const bool ok = scale_ok(s);
+      const float nan = __builtin_nanf("");
+      // one rounding of an exact float64 product (|raw| < 2^31, 24-bit scale)
+      p.top_val[2 * row] = ok ? (float)((double)v1 * (double)s) : nan;
+      p.top_val[2 * row + 1] = ok ? (float)((double)v2 * (double)s) : nan;
+      p.margin[row] = ok ? (float)((double)(v1 - v2) * (double)s) : nan;
+    }
+  }
+}
+
 template <int MODE, int EPI>
 __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nthreads) {
   using val_t = typename Arith<MODE>::val_t;
@@ -727,38 +765,7 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
       t = t2_merge(t, perm<kQuadX2>(t));
       t = t2_merge(t, perm<kHalfMirror>(t));
       t = t2_merge(t, perm<kMirror>(t));
-      if (EPI == kSample && slot == 0) {
-        bool ok = true;
-        if constexpr (MODE == 1) ok = scale_ok(p.scale ? p.scale[row] : 1.0f);
-        const float y1 = okey_value<float>((unsigned)(t.k1 >> 32));
-        const float y2 = okey_value<float>((unsigned)(t.k2 >> 32));
-        const float nan = __builtin_nanf("");
-        p.token[row] = ok ? key_id(t.k1) : -1;
-        if (p.value) p.value[row] = ok ? y1 : nan;
-        if (p.gap) p.gap[row] = ok ? y1 - y2 : nan;
-      } else if (EPI == kTop2 && slot == 0) {
-        const val_t v1 = okey_value<val_t>((unsigned)(t.k1 >> 32));
-        const val_t v2 = okey_value<val_t>((unsigned)(t.k2 >> 32));
-        p.top_id[2 * row] = key_id(t.k1);
-        p.top_id[2 * row + 1] = key_id(t.k2);
-        if constexpr (MODE == 0) {
-          p.top_val[2 * row] = v1;
-          p.top_val[2 * row + 1] = v2;
-          p.margin[row] = v1 - v2;
-        } else {
-          const float s = p.scale ? p.scale[row] : 1.0f;
-          if (p.top_raw) {
-            p.top_raw[2 * row] = v1;
-            p.top_raw[2 * row + 1] = v2;
-          }
-          const bool ok = scale_ok(s);
-          const float nan = __builtin_nanf("");
-          // one rounding of an exact float64 product (|raw| < 2^31, 24-bit scale)
-          p.top_val[2 * row] = ok ? (float)((double)v1 * (double)s) : nan;
-          p.top_val[2 * row + 1] = ok ? (float)((double)v2 * (double)s) : nan;
-          p.margin[row] = ok ? (float)((double)(v1 - v2) * (double)s) : nan;
-        }
-      }
+      if (slot == 0) put_top2<MODE, EPI>(p, row, t);
     } else if constexpr (EPI == kLseInt) {
       // pass 1: the row max (exact); pass 2: the exact sum of the rescaled
       // block sums (integers: the order does not matter)
@@ -1457,13 +1464,43 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   }
 }
 
-// the row-parallel fold for larger batches: 16 rows per workgroup
+// the row-parallel log-prob fold for larger batches: 16 rows per workgroup, in
+// the slot order of merge_rows (the same order as the fused fold)
 template <int MODE, int EPI>
 __global__ __launch_bounds__(256) void lmhead_merge_kernel(Params p) {
+  static_assert(EPI == kLse || EPI == kLseInt, "top-2 folds use lmhead_merge_top2_kernel");
   const int row0 = blockIdx.x * (256 / kSlots);
   merge_rows<MODE, EPI>(p, row0, min(256 / kSlots, p.B - row0), threadIdx.x, 256);
+}
+
+// The top-2 fold for larger batches (greedy and sampling): one wave per row,
+// four rows per workgroup, so a batch of 512 spreads over 128 workgroups.  A
+// top-2 of a union is exact in any order, so the lane count does not change a
+// bit (the log-prob folds keep their fixed slot order in merge_rows).
+template <int MODE, int EPI>
+__global__ __launch_bounds__(256) void lmhead_merge_top2_kernel(Params p) {
+  constexpr int kRowsPerWg = 4, kPerLane = 4;  // records per lane in flight per round
+  const int row0 = blockIdx.x * kRowsPerWg;
+  const int row = row0 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int nb = p.nblocks;
+  if (row < p.B) {
+    const uint4 *rec = p.records + (int64_t)row * nb;
+    Top2 t{0, 0};
+    for (int b0 = lane; b0 < nb; b0 += 64 * kPerLane) {
+      uint4 r[kPerLane];  // all issued (a clamped index stays in bounds), then merged
+#pragma unroll
+      for (int q = 0; q < kPerLane; ++q) r[q] = rec[min(b0 + 64 * q, nb - 1)];
+#pragma unroll
+      for (int q = 0; q < kPerLane; ++q)
+        if (b0 + 64 * q < nb) t = t2_merge(t, t2_unpack(r[q]));
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) t = t2_merge(t, Top2{__shfl_xor(t.k1, m), __shfl_xor(t.k2, m)});
+    if (lane == 0) put_top2<MODE, EPI>(p, row, t);
+  }
   if constexpr (MODE == 0 && EPI == kTop2)
-    if (p.gated) gate_rows(p, row0, min(256 / kSlots, p.B - row0), threadIdx.x, 256);
+    if (p.gated) gate_rows(p, row0, min(kRowsPerWg, p.B - row0), threadIdx.x, 256);
 }
 
 // ------------------------------------------------ per-token quantisation
@@ -1606,10 +1643,11 @@ hipError_t launch_tile(int epi, const Params &p, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 mgrid((p.B + 256 / kSlots - 1) / (256 / kSlots));
+    const dim3 tgrid((p.B + 3) / 4);  // lmhead_merge_top2_kernel: four rows per workgroup
     if (epi == kTop2)
-      hipLaunchKernelGGL((lmhead_merge_kernel<MODE, kTop2>), mgrid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((lmhead_merge_top2_kernel<MODE, kTop2>), tgrid, dim3(256), 0, s, p);
     else if (epi == kSample)
-      hipLaunchKernelGGL((lmhead_merge_kernel<MODE, kSample>), mgrid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((lmhead_merge_top2_kernel<MODE, kSample>), tgrid, dim3(256), 0, s, p);
     else if (MODE == 1 && epi == kLseInt)
       hipLaunchKernelGGL((lmhead_merge_kernel<1, kLseInt>), mgrid, dim3(256), 0, s, p);
     else
