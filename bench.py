@@ -289,7 +289,7 @@ def main():
     traffic = traffic_from_profile(f"greedy_tinyllama_b{dom['batch']}")
     rf["traffic"] = traffic
     rf["kernel"] = (f"one greedy top-2 call at batch {dom['batch']} "
-                    f"({'tile kernel with fused fold' if dom['batch'] <= 32 else 'tile kernel + merge kernel'})")
+                    f"({'tile kernel with fused fold' if dom['batch'] <= 32 else 'tile kernel + fold kernel'})")
 
     out = {
         "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1,

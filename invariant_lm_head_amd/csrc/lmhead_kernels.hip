@@ -8,9 +8,11 @@
 //   kSample per-row top-2 of z / T + Gumbel noise (seeded Gumbel-max draw);
 //   kLseInt (int8) per-row block max and the exact sum of integer exps, for
 //           the all-integer log-softmax (see "integer front and back").
-// The block partials of a row are then folded into the outputs by merge_rows(),
-// either by the last workgroup of the launch (atomic ticket, small batches) or
-// by a second, row-parallel kernel (larger batches); both run the same code.
+// The block partials of a row are then folded into the outputs, either by the
+// last workgroup of the launch (atomic ticket, small batches: merge_rows) or by
+// a second, row-parallel kernel (larger batches: merge_rows again for the
+// log-prob folds, whose slot order it fixes; one wave per row for the top-2
+// folds, which are exact in any order).
 //
 // Batch invariance (one reduction order per logit, fixed by H only):
 //   * every logit is acc = 0; for s = 0 .. H*esize/32 - 1: acc = MFMA(A_s, B_s, acc)
@@ -37,7 +39,8 @@
 // (no register round trip), NS stages in flight, 16-byte chunks XOR-swizzled by
 // row so the MFMA fragment reads (ds_read_b128) are bank-conflict free.  The
 // workgroup -> tile map is XCD-aware: workgroups that share operand tiles run
-// on the same XCD (same L2).  Cross-lane reductions use DPP and ds_swizzle.
+// on the same XCD (same L2).  Cross-lane reductions use v_permlane16_swap, DPP
+// and ds_swizzle.
 #include <hip/hip_runtime.h>
 #include <limits.h>
 #include <stdint.h>
@@ -874,7 +877,7 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
 // last workgroup, possibly on another XCD, after the release / acquire pair of
 // the ticket; written through to the agent coherence point (agent-scope atomic
 // stores), they leave the release's L2 writeback next to nothing to do
-// (measured: batch 1 and 8 about 0.6 us faster).  The merge kernel reads them
+// (measured: batch 1 and 8 about 0.6 us faster).  The fold kernels read them
 // after the launch ends, so there they are plain stores.
 template <bool THROUGH> __device__ __forceinline__ void put_record(uint4 *d, uint4 v) {
   if constexpr (THROUGH) {
