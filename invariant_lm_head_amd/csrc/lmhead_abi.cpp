@@ -89,7 +89,7 @@ lmhead_status lmhead_logits(int mode, int round, const void *x, const void *w, i
   if (st != LMHEAD_OK) return st;
   if (!logits) return LMHEAD_E_NULL;
   if (((uintptr_t)logits & (round == LMHEAD_ROUND_BF16 ? 1u : 3u)) != 0) return LMHEAD_E_ALIGN;
-  const lmh::Plan plan = lmh::plan_for(B, row_bytes(mode, H), V);
+  const lmh::Plan plan = lmh::plan_for(mode, B, row_bytes(mode, H), V);
   lmh::Params p = base_params(mode, x, w, B, H, V, plan);
   p.round_bf16 = round == LMHEAD_ROUND_BF16;
   p.logits = logits;
@@ -121,7 +121,7 @@ lmhead_status greedy(int mode, int round, const void *x, const void *w, int64_t 
   if (!aligned4(top_id) || !aligned4(top_val) || !aligned4(margin) ||
       (top_raw && !aligned4(top_raw)) || (row_scale && !aligned4(row_scale)))
     return LMHEAD_E_ALIGN;
-  const lmh::Plan plan = lmh::plan_for(B, row_bytes(mode, H), V);
+  const lmh::Plan plan = lmh::plan_for(mode, B, row_bytes(mode, H), V);
   lmh::Params p = base_params(mode, x, w, B, H, V, plan);
   st = bind_workspace(p, ws, ws_bytes, B, V);
   if (st != LMHEAD_OK) return st;
@@ -153,7 +153,7 @@ lmhead_status lmhead_logprob(int mode, const void *x, const void *w, int64_t B, 
   if (!target || !logprob) return LMHEAD_E_NULL;
   if (!aligned4(target) || !aligned4(logprob) || (row_scale && !aligned4(row_scale)))
     return LMHEAD_E_ALIGN;
-  const lmh::Plan plan = lmh::plan_for(B, row_bytes(mode, H), V);
+  const lmh::Plan plan = lmh::plan_for(mode, B, row_bytes(mode, H), V);
   lmh::Params p = base_params(mode, x, w, B, H, V, plan);
   st = bind_workspace(p, ws, ws_bytes, B, V);
   if (st != LMHEAD_OK) return st;
@@ -183,7 +183,7 @@ lmhead_status lmhead_logprob_int(const void *x, const void *w, int64_t B, int64_
       ((uintptr_t)logprob_q & 7) != 0)
     return LMHEAD_E_ALIGN;
   if (unit_m <= 0) return LMHEAD_E_VALUE;
-  const lmh::Plan plan = lmh::plan_for(B, row_bytes(mode, H), V);
+  const lmh::Plan plan = lmh::plan_for(mode, B, row_bytes(mode, H), V);
   lmh::Params p = base_params(mode, x, w, B, H, V, plan);
   st = bind_workspace(p, ws, ws_bytes, B, V);
   if (st != LMHEAD_OK) return st;
@@ -222,7 +222,7 @@ lmhead_status lmhead_sample_gumbel(int mode, const void *x, const void *w, int64
       (row_scale && !aligned4(row_scale)))
     return LMHEAD_E_ALIGN;
   if (!(temperature > 0.0f) || !(temperature <= 3.4e38f)) return LMHEAD_E_VALUE;
-  const lmh::Plan plan = lmh::plan_for(B, row_bytes(mode, H), V);
+  const lmh::Plan plan = lmh::plan_for(mode, B, row_bytes(mode, H), V);
   lmh::Params p = base_params(mode, x, w, B, H, V, plan);
   st = bind_workspace(p, ws, ws_bytes, B, V);
   if (st != LMHEAD_OK) return st;

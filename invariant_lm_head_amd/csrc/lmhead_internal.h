@@ -56,7 +56,7 @@ struct Plan {
   int grid_m, grid_n;
 };
 
-Plan plan_for(int64_t B, int64_t rowbytes, int64_t V);
+Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V);
 
 // Byte offsets of the workspace regions; returns the total size.
 size_t workspace_layout(int64_t B, int64_t V, size_t *off_zt, size_t *off_records);

@@ -151,18 +151,25 @@ struct Tile {
   static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "tile shape");
   static_assert(XSTAGE % 1024 == 0 && WSTAGE % 1024 == 0, "1 KB load spans");
   static_assert(BN % kBlockCols == 0 && (WN % TPB == 0 || TPB % WN == 0), "blocks");
-  static_assert(BKB == 64 || BKB == 128 || BKB == 256, "stage width");
-  static_assert(NSX >= 2 && NSW > NSX, "ring depths: W loads lead X loads");
+  static_assert(BKB == 64 || BKB == 128 || BKB == 256 || BKB == 512, "stage width");
+  static_assert(NSX >= 2 && NSW >= NSX, "ring depths");
+  // NSW > NSX: W stage b + NSW is issued spread over the k-steps after boundary
+  // b, ahead of the X stage it is consumed with.  NSW == NSX: both are issued at
+  // the boundary, and each boundary waits for every load of the next stage.
+  static constexpr bool WSPREAD = NSW > NSX;
   static_assert(LDS <= 160 * 1024, "LDS budget");
   // loads of one wave in flight at once (after a boundary's issue) stay below
   // the 6-bit vmcnt counter
   static_assert((NSX - 1) * SPWX_MAX + (NSW - 1) * SPWW_MAX < 64, "vmcnt range");
   // this wave's loads issued after X stage s by the time stage s is awaited
   // (steady state; fewer near the last stages)
-  static constexpr int AFTER_MAX = SPWW_MIN + (NSX - 2) * (SPWX_MIN + SPWW_MIN);
+  static constexpr int AFTER_MAX = WSPREAD ? SPWW_MIN + (NSX - 2) * (SPWX_MIN + SPWW_MIN) : 0;
   static_assert(STEPS % 2 == 0, "fragment double buffer parity");
   // epilogue exchange areas (one 32-row tile per wave row at a time) fit in LDS
-  static_assert(WAVES_M * 32 * WAVES_N * (4 + 32 * 4) <= LDS && BM * WAVES_N * 16 <= LDS,
+  // below the fold's flag and row list, which take its top 288 bytes
+  static constexpr int FOLD_LDS = 288;
+  static_assert(WAVES_M * 32 * WAVES_N * (4 + 32 * 4) + FOLD_LDS <= LDS &&
+                    BM * WAVES_N * 16 + FOLD_LDS <= LDS,
                 "exchange");
 };
 
@@ -639,9 +646,12 @@ template <int N> __device__ __forceinline__ float tree_sum(const float *e) {
 // kernel.  An MFMA result depends only on its own A row and B column, so each
 // value equals the float32 head's bits.  The two are then ranked, lowest id on
 // a tie, and the row's outputs replaced.
-__device__ void gate_rows(const Params &p, int row0, int nrows, int tid, int nthreads) {
-  __shared__ int s_rows[64];
-  __shared__ int s_count;
+// lds: kGateLdsInts ints of LDS the caller's workgroup does not otherwise use
+// meanwhile (the listed rows, then their count)
+constexpr int kGateLdsInts = 65;
+__device__ void gate_rows(const Params &p, int row0, int nrows, int tid, int nthreads, int *lds) {
+  int *s_rows = lds;
+  int &s_count = lds[64];
   __syncthreads();  // the fold's writes of these rows are visible to every wave
   if (tid < 64) {
     const bool in = tid < nrows;
@@ -897,7 +907,11 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   using acc_t = typename A::acc_t;
   using val_t = typename A::val_t;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
-  __shared__ int s_last;
+  // the fold's flag and the gated recompute's row list sit at the top of the
+  // stage rings, which are free by then (the epilogue exchange uses the bottom)
+  static_assert(16 + 4 * 68 <= T::FOLD_LDS && kGateLdsInts <= 68, "fold LDS");
+  int &s_last = *(int *)(smem + T::LDS - 16);
+  int *s_gate = (int *)(smem + T::LDS - T::FOLD_LDS);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -931,7 +945,8 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   // stage t holds bytes [koff(t), koff(t) + BKB) of every row: the k order of
   // this tile's columns (a tile never straddles a rotation group, and the
   // rotation is a whole number of stages)
-  static_assert((1LL << LMH_ROT_SHIFT) % T::BN == 0 && 256 % T::BKB == 0, "tile within one rotation group");
+  static_assert(MODE != 1 || ((1LL << LMH_ROT_SHIFT) % T::BN == 0 && 256 % T::BKB == 0),
+                "tile within one rotation group");
   const int64_t rot = MODE == 1 ? k_rotation(p.rowbytes, n0) : 0;
   auto koff = [&](int stage) -> int64_t {
     const int64_t o = (int64_t)stage * T::BKB + rot;
@@ -1027,7 +1042,9 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
     if (sw < nst) issue_w(sw, sw % T::NSW);
   };
   // loads this wave issued after X stage s, once boundaries <= s - 2 are issued
+  // (with W issued at the boundary, after X: wait for everything)
   auto after = [&](int s) {
+    if constexpr (!T::WSPREAD) return 0;
     int n = s - T::NSX + T::NSW < nst ? T::SPWW_MIN : 0;
     const int lo = s - T::NSX + 1, hi = s - 2;  // whole boundaries after X stage s
     n += T::SPWX_MIN * max(0, min(hi, nst - 1 - T::NSX) - lo + 1);
@@ -1074,6 +1091,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
       wait_vm_le<T::AFTER_MAX>(after(t + 1));  // stage t + 1 has landed
       lds_barrier();
       if (t + T::NSX < nst) issue_x(t + T::NSX, t % T::NSX);
+      if (!T::WSPREAD && t + T::NSW < nst) issue_w(t + T::NSW, t % T::NSW);
       read_frags(smem + ((t + 1) % T::NSX) * T::XSTAGE,
                  smem + T::WRING + ((t + 1) % T::NSW) * T::WSTAGE, 0, fa[last ^ 1], fb[last ^ 1]);
     }
@@ -1082,7 +1100,8 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   // loads of the boundary before them (W stages NSW .. nst - 1)
   stage(0, std::false_type{});
   int t = 1;
-  for (; t <= nst - T::NSW; ++t) stage(t, std::true_type{});
+  if constexpr (T::WSPREAD)
+    for (; t <= nst - T::NSW; ++t) stage(t, std::true_type{});
   for (; t < nst; ++t) stage(t, std::false_type{});
 
   // lane (j, h) of MFMA tile (mt, nt) holds Z[row0 + acc_row(v, h)][col0 + j], v = 0..15
@@ -1461,7 +1480,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       merge_rows<MODE, EPI>(p, m0, min(T::BM, p.B - m0), tid, T::NT);
       if constexpr (MODE == 0 && EPI == kTop2)
-        if (p.gated) gate_rows(p, m0, min(T::BM, p.B - m0), tid, T::NT);
+        if (p.gated) gate_rows(p, m0, min(T::BM, p.B - m0), tid, T::NT, s_gate);
       if (tid == 0) p.tickets[tm] = 0u;  // leave the workspace zeroed for the next call
     }
   }
@@ -1503,7 +1522,10 @@ __global__ __launch_bounds__(256) void lmhead_merge_top2_kernel(Params p) {
     if (lane == 0) put_top2<MODE, EPI>(p, row, t);
   }
   if constexpr (MODE == 0 && EPI == kTop2)
-    if (p.gated) gate_rows(p, row0, min(kRowsPerWg, p.B - row0), threadIdx.x, 256);
+    if (p.gated) {
+      __shared__ int s_gate[kGateLdsInts];
+      gate_rows(p, row0, min(kRowsPerWg, p.B - row0), threadIdx.x, 256, s_gate);
+    }
 }
 
 // ------------------------------------------------ per-token quantisation
@@ -1596,6 +1618,7 @@ __global__ void reverse_rows_kernel(const char *src, char *dst, int64_t rows, in
 //   5: 32 x 256, 6: 64 x 256 in place of 0 and 1 when the 128-column grid
 //      would take more than two rounds of the 256 CUs (large vocabularies):
 //      half the workgroups, so half the pipeline fills and tails per CU
+//   0 with 512-byte stages (V0d) for the float head when rows allow it
 #ifndef LMH_V4_TILE
 #define LMH_V4_TILE 256, 256, 4, 2, 128, 2, 3
 #endif
@@ -1609,6 +1632,13 @@ constexpr int kCUs = 256;  // MI355X compute units
 #define LMH_V0_TILE 32, 128, 1, 4, BKB, 2, 3
 #endif
 template <int BKB> using V0 = Tile<LMH_V0_TILE>;
+// V0 with 512 bytes of each row per stage and the W ring as deep as the X ring
+// (2 x 16 KB + 2 x 64 KB of LDS): each W row is read 512 contiguous bytes at a
+// time.  Measured on MI355X for the 131 MB W stream alone (same pattern, eight
+// separately allocated copies): 25.3 us against 28.2 us with 256-byte pieces,
+// whose rate also varied from copy to copy (23-31 us).  Float head only: the
+// int8 head's rotated k order works in 256-byte units.
+using V0d = Tile<32, 128, 1, 4, 512, 2, 2>;
 #ifndef LMH_V1_TILE
 #define LMH_V1_TILE 64, 128, 2, 2, BKB, 2, 3
 #endif
@@ -1663,6 +1693,8 @@ template <int MODE>
 hipError_t launch_mode(int epi, const Plan &plan, const Params &p, hipStream_t s) {
   switch (plan.variant) {
     case 0:
+      if constexpr (MODE == 0)
+        if (plan.bkb == V0d::BKB) return launch_tile<V0d, MODE, true>(epi, p, s);
       if (plan.bkb == 256) return launch_tile<V0<256>, MODE, true>(epi, p, s);
       if (plan.bkb == 128) return launch_tile<V0<128>, MODE, true>(epi, p, s);
       return launch_tile<V0<64>, MODE, true>(epi, p, s);
@@ -1690,7 +1722,7 @@ hipError_t launch_mode(int epi, const Plan &plan, const Params &p, hipStream_t s
 
 }  // namespace
 
-Plan plan_for(int64_t B, int64_t rowbytes, int64_t V) {
+Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V) {
   Plan pl;
   const int bkb256 = rowbytes % 256 == 0 ? 256 : rowbytes % 128 == 0 ? 128 : 64;
   const int bkb128 = rowbytes % 128 == 0 ? 128 : 64;
@@ -1699,6 +1731,7 @@ Plan plan_for(int64_t B, int64_t rowbytes, int64_t V) {
     pl.variant = 5; pl.bm = V0w<128>::BM; pl.bn = V0w<128>::BN; pl.bkb = bkb128;
   } else if (B <= 32) {
     pl.variant = 0; pl.bm = V0<256>::BM; pl.bn = V0<256>::BN; pl.bkb = bkb256;
+    if (mode == 0 && rowbytes % V0d::BKB == 0) pl.bkb = V0d::BKB;
   } else if (B <= 64 && wide) {
     pl.variant = 6; pl.bm = V1w<128>::BM; pl.bn = V1w<128>::BN; pl.bkb = bkb128;
   } else if (B <= 64) {
