@@ -1008,13 +1008,15 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   // ---- main loop: stages in k order (koff), one MFMA chain per logit.
   // Loads: boundary b (after stage b; boundaries -NSW..-1 before the loop)
   // loads, in this order, X stage b + NSX into X buffer b mod NSX and W stage
-  // b + NSW into W buffer b mod NSW.  In the loop the X loads are issued at the
-  // boundary and the W loads are spread over the next stage's k-steps, so the
-  // address unit is not handed a whole stage at once.  Stage s is awaited at
-  // boundary s - 1, before that boundary's loads: loads complete in issue order
-  // and W stage s was issued before X stage s (NSW > NSX), so it suffices that
-  // this wave has at most after(s) loads in flight, the number it issued after
-  // X stage s.
+  // b + NSW into W buffer b mod NSW.  With NSW > NSX, in the loop the X loads
+  // are issued at the boundary and the W loads are spread over the next
+  // stage's k-steps, so the address unit is not handed a whole stage at once.
+  // Stage s is awaited at boundary s - 1, before that boundary's loads: loads
+  // complete in issue order and W stage s was issued before X stage s, so it
+  // suffices that this wave has at most after(s) loads in flight, the number it
+  // issued after X stage s.  With NSW == NSX both stages are issued at the
+  // boundary (X, then W) and boundary s - 1 waits for every load in flight,
+  // which are exactly stage s's.
   // Compute: within a stage, the fragments of k-step s + 1 are read while the
   // MFMAs of step s issue (one read per MFMA, so LDS latency hides behind the
   // matrix pipe); after the stage's last MFMAs every wave waits for stage t + 1,
