@@ -54,7 +54,9 @@ extern "C" {
 typedef enum {
   LMHEAD_OK = 0,
   LMHEAD_E_NULL = 1,      /* a required pointer is NULL */
-  LMHEAD_E_SHAPE = 2,     /* B < 1, V < 2, H not a positive multiple of 64, or too large */
+  LMHEAD_E_SHAPE = 2,     /* B < 1, V < 2, H not a positive multiple of 64, or too large:
+                             B > 2^24, V > 2^30, H > 2^20, or B and V together beyond
+                             one launch grid (2^32 threads; about B * V > 2^38) */
   LMHEAD_E_ALIGN = 3,     /* x, w or workspace not 16-byte aligned, or another array
                              not aligned to its element size */
   LMHEAD_E_MODE = 4,      /* unknown mode / rounding, or rounding not valid for the mode */

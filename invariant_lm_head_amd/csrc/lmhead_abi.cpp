@@ -20,6 +20,8 @@ constexpr int64_t kMaxVocab = (int64_t)1 << 30;  // V bound
 constexpr int64_t kMaxHidden = (int64_t)1 << 20; // H bound
 constexpr int64_t kInt8MaxHidden = 131071;       // H * 128^2 < 2^31
 
+int64_t row_bytes(int mode, int64_t H) { return mode == LMHEAD_MODE_BF16 ? 2 * H : H; }
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
@@ -33,6 +35,10 @@ lmhead_status check_common(int mode, int round, const void *x, const void *w, in
       H > kMaxHidden)
     return LMHEAD_E_SHAPE;
   if (mode == LMHEAD_MODE_INT8 && H > kInt8MaxHidden) return LMHEAD_E_OVERFLOW;
+  // the tile grid is one x dimension of at most 2^32 - 1 threads (up to 512 per
+  // workgroup), which bounds B x V jointly
+  const lmh::Plan pl = lmh::plan_for(mode, B, row_bytes(mode, H), V);
+  if ((uint64_t)pl.grid_m * (uint64_t)pl.grid_n * 512u > 0xFFFFFFFFull) return LMHEAD_E_SHAPE;
   if (!aligned16(x) || !aligned16(w)) return LMHEAD_E_ALIGN;
   return LMHEAD_OK;
 }
@@ -57,8 +63,6 @@ lmh::Params base_params(int mode, const void *x, const void *w, int64_t B, int64
   p.grid_n = plan.grid_n;
   return p;
 }
-
-int64_t row_bytes(int mode, int64_t H) { return mode == LMHEAD_MODE_BF16 ? 2 * H : H; }
 
 }  // namespace
 
@@ -294,8 +298,9 @@ const char *lmhead_status_string(int status) {
   switch (status) {
     case LMHEAD_OK: return "ok";
     case LMHEAD_E_NULL: return "a required pointer is NULL";
-    case LMHEAD_E_SHAPE: return "invalid shape (need B >= 1, V >= 2, H a positive multiple of 64)";
-    case LMHEAD_E_ALIGN: return "a pointer is not 16-byte aligned";
+    case LMHEAD_E_SHAPE:
+      return "invalid shape (need B >= 1, V >= 2, H a positive multiple of 64, sizes within bounds)";
+    case LMHEAD_E_ALIGN: return "a pointer is not aligned as required";
     case LMHEAD_E_MODE: return "unknown mode or rounding, or rounding not valid for the mode";
     case LMHEAD_E_OVERFLOW: return "int8 head: H too large for exact int32 accumulation";
     case LMHEAD_E_WORKSPACE: return "workspace missing or too small";

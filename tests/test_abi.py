@@ -62,6 +62,11 @@ def test_workspace_bytes_layout(lib):
     assert lib.lmhead_workspace_bytes(0, 0, 2048, 32000) == 0
     assert lib.lmhead_workspace_bytes(0, 1, 100, 32000) == 0
     assert lib.lmhead_workspace_bytes(2, 1, 2048, 32000) == 0
+    # B and V each within bounds but together beyond one launch grid (2^32 threads)
+    assert lib.lmhead_workspace_bytes(0, 1 << 24, 64, 151936) == 0
+    assert lib.lmhead_workspace_bytes(0, 1 << 24, 64, 32000) > 0      # 2^32 - 2^24 threads: fits
+    assert lib.lmhead_workspace_bytes(0, 512, 64, 1 << 30) == 0
+    assert lib.lmhead_workspace_bytes(0, 32, 64, 1 << 30) > 0
 
 
 def logits_status(lib, mode=0, rnd=0, x=A, w=A, B=4, H=64, V=1000, out=A2):
@@ -109,6 +114,7 @@ def test_greedy_validation(lib):
     assert call(nws=ws_need - 1) == E_WORKSPACE
     assert call(ws=MIS) == E_ALIGN
     assert call(mode=1, H=1 << 17) == E_OVERFLOW
+    assert call(B=1 << 24, V=151936) == E_SHAPE        # grid beyond 2^32 threads
 
 
 def test_logprob_validation(lib):
