@@ -87,7 +87,26 @@ def _dims(x: torch.Tensor, w: torch.Tensor):
         raise ValueError(f"x must be [B, H] and w [V, H], got {tuple(x.shape)}, {tuple(w.shape)}")
     if not (x.is_cuda and w.is_cuda and x.is_contiguous() and w.is_contiguous()):
         raise ValueError("x and w must be contiguous device tensors")
+    if x.device != w.device:
+        raise ValueError(f"x and w must be on one device, got {x.device}, {w.device}")
     return x.shape[0], x.shape[1], w.shape[0]
+
+
+def _vec(t, name: str, B: int, dtype, dev):
+    """A caller's per-row array: None, or a contiguous [B] tensor of dtype on dev
+    (the kernels read B elements of it)."""
+    if t is None:
+        return None
+    if t.dtype != dtype or t.shape != (B,) or t.device != dev or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape ({B},) on {dev}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+    return t
+
+
+def _ws(ws, dev):
+    if ws is not None and (ws.device != dev or not ws.is_contiguous()):
+        raise ValueError(f"ws must be a contiguous tensor on {dev}")
+    return ws
 
 
 def _ptr(t):
@@ -129,6 +148,8 @@ def logits(x: torch.Tensor, w: torch.Tensor, round_bf16: bool = False,
     dt = torch.int32 if mode == MODE_INT8 else (torch.bfloat16 if round_bf16 else torch.float32)
     if out is None:
         out = torch.empty((B, V), dtype=dt, device=x.device)
+    elif out.dtype != dt or out.shape != (B, V) or out.device != x.device or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {dt} tensor of shape ({B}, {V}) on {x.device}")
     st = library().lmhead_logits(mode, ROUND_BF16 if round_bf16 else ROUND_F32, _ptr(x), _ptr(w),
                                  B, H, V, _ptr(out), _stream(x.device))
     _check("lmhead_logits", st)
@@ -146,11 +167,12 @@ def greedy_top2(x: torch.Tensor, w: torch.Tensor, row_scale: torch.Tensor | None
     vals = torch.empty((B, 2), dtype=torch.float32, device=dev)
     margin = torch.empty((B,), dtype=torch.float32, device=dev)
     raw = torch.empty((B, 2), dtype=torch.int32, device=dev) if mode == MODE_INT8 else None
+    rs = _vec(row_scale, "row_scale", B, torch.float32, dev)
     need = workspace_bytes(mode, B, H, V)
-    if ws is None:
+    if _ws(ws, dev) is None:
         ws = workspace(need, dev)
     st = library().lmhead_greedy_top2(mode, ROUND_BF16 if round_bf16 else ROUND_F32,
-                                      _ptr(x), _ptr(w), B, H, V, _ptr(row_scale), _ptr(ids),
+                                      _ptr(x), _ptr(w), B, H, V, _ptr(rs), _ptr(ids),
                                       _ptr(vals), _ptr(margin), _ptr(raw), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(dev))
     _check("lmhead_greedy_top2", st)
@@ -163,13 +185,14 @@ def logprob(x: torch.Tensor, w: torch.Tensor, target: torch.Tensor,
     mode = _mode_of(x, w)
     B, H, V = _dims(x, w)
     dev = x.device
-    if target.dtype != torch.int32 or target.numel() != B or not target.is_cuda:
-        raise ValueError("target must be a device int32 tensor of B ids")
+    if target.dtype != torch.int32 or target.numel() != B or target.device != dev:
+        raise ValueError(f"target must be an int32 tensor of B ids on {dev}")
+    rs = _vec(row_scale, "row_scale", B, torch.float32, dev)
     out = torch.empty((B,), dtype=torch.float32, device=dev)
     need = workspace_bytes(mode, B, H, V)
-    if ws is None:
+    if _ws(ws, dev) is None:
         ws = workspace(need, dev)
-    st = library().lmhead_logprob(mode, _ptr(x), _ptr(w), B, H, V, _ptr(row_scale),
+    st = library().lmhead_logprob(mode, _ptr(x), _ptr(w), B, H, V, _ptr(rs),
                                   _ptr(target.contiguous()), _ptr(out), _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(dev))
     _check("lmhead_logprob", st)
@@ -206,11 +229,11 @@ def logprob_int(x: torch.Tensor, w: torch.Tensor, unit: tuple, step_m: torch.Ten
     B, H, V = _dims(x, w)
     dev = x.device
     for name, t in (("step_m", step_m), ("step_e", step_e), ("target", target)):
-        if t.dtype != torch.int32 or t.numel() != B or not t.is_cuda:
-            raise ValueError(f"{name} must be a device int32 tensor of B values")
+        if t.dtype != torch.int32 or t.numel() != B or t.device != dev:
+            raise ValueError(f"{name} must be an int32 tensor of B values on {dev}")
     out = torch.empty((B,), dtype=torch.int64, device=dev)
     need = workspace_bytes(MODE_INT8, B, H, V)
-    if ws is None:
+    if _ws(ws, dev) is None:
         ws = workspace(need, dev)
     st = library().lmhead_logprob_int(_ptr(x), _ptr(w), B, H, V, int(unit[0]), int(unit[1]),
                                       _ptr(step_m.contiguous()), _ptr(step_e.contiguous()),
@@ -233,7 +256,7 @@ def greedy_gated(x: torch.Tensor, w: torch.Tensor, tau: float,
     margin = torch.empty((B,), dtype=torch.float32, device=dev)
     gated = torch.empty((B,), dtype=torch.int32, device=dev)
     need = workspace_bytes(mode, B, H, V)
-    if ws is None:
+    if _ws(ws, dev) is None:
         ws = workspace(need, dev)
     st = library().lmhead_greedy_gated(mode, _ptr(x), _ptr(w), B, H, V, float(tau), _ptr(ids),
                                        _ptr(vals), _ptr(margin), _ptr(gated), _ptr(ws),
@@ -252,16 +275,17 @@ def sample_gumbel(x: torch.Tensor, w: torch.Tensor, temperature: float, seed: to
     B, H, V = _dims(x, w)
     dev = x.device
     for name, t in (("seed", seed), ("position", position)):
-        if t.numel() != B or not t.is_cuda or t.element_size() != 8:
-            raise ValueError(f"{name} must be a device tensor of B 64-bit integers")
+        if t.numel() != B or t.device != dev or t.element_size() != 8:
+            raise ValueError(f"{name} must be a tensor of B 64-bit integers on {dev}")
+    rs = _vec(row_scale, "row_scale", B, torch.float32, dev)
     token = torch.empty((B,), dtype=torch.int32, device=dev)
     value = torch.empty((B,), dtype=torch.float32, device=dev)
     gap = torch.empty((B,), dtype=torch.float32, device=dev)
     need = workspace_bytes(mode, B, H, V)
-    if ws is None:
+    if _ws(ws, dev) is None:
         ws = workspace(need, dev)
     st = library().lmhead_sample_gumbel(mode, _ptr(x), _ptr(w), B, H, V, float(temperature),
-                                        _ptr(row_scale), _ptr(seed.contiguous()),
+                                        _ptr(rs), _ptr(seed.contiguous()),
                                         _ptr(position.contiguous()), _ptr(token), _ptr(value),
                                         _ptr(gap), _ptr(ws), ws.numel() * ws.element_size(),
                                         _stream(dev))

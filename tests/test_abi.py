@@ -236,3 +236,19 @@ def test_binding_refuses_mixed_dtypes():
     import torch
     with pytest.raises(TypeError):
         lmhead._mode_of(torch.zeros(1, 64, dtype=torch.bfloat16), torch.zeros(2, 64, dtype=torch.int8))
+
+
+def test_binding_checks_caller_arrays():
+    """Per-row arrays and workspaces the kernels would read past are refused
+    before any call (CPU tensors stand in for device ones here)."""
+    import torch
+    cpu = torch.device("cpu")
+    assert lmhead._vec(None, "row_scale", 4, torch.float32, cpu) is None
+    ok = torch.ones(4)
+    assert lmhead._vec(ok, "row_scale", 4, torch.float32, cpu) is ok
+    for bad in (torch.ones(3), torch.ones(4, dtype=torch.float64), torch.ones(8)[::2]):
+        with pytest.raises(ValueError):
+            lmhead._vec(bad, "row_scale", 4, torch.float32, cpu)
+    with pytest.raises(ValueError):
+        lmhead._ws(torch.zeros(2, 64, dtype=torch.uint8)[:, ::2], cpu)
+    assert lmhead._ws(None, cpu) is None

@@ -281,3 +281,15 @@ def test_bad_arguments_raise_before_launch(tl):
     with pytest.raises(lmhead.LMHeadError) as e:
         lmhead.logits(x[:, :100].contiguous(), w[:, :100].contiguous())
     assert e.value.status == 2
+    # caller buffers the kernels would overrun are refused by the binding
+    with pytest.raises(ValueError):
+        lmhead.logits(x, w, out=torch.empty((4, 100), dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError):
+        lmhead.logits(x, w, out=torch.empty((4, w.shape[0]), dtype=torch.bfloat16, device=DEV))
+    xi, wi = torch.zeros((4, 64), dtype=torch.int8, device=DEV), torch.zeros((8, 64), dtype=torch.int8, device=DEV)
+    with pytest.raises(ValueError):
+        lmhead.greedy_top2(xi, wi, row_scale=torch.ones(3, device=DEV))
+    with pytest.raises(ValueError):
+        lmhead.greedy_top2(xi, wi, row_scale=torch.ones(4, dtype=torch.float64, device=DEV))
+    with pytest.raises(ValueError):
+        lmhead.greedy_top2(x, w, ws=torch.zeros((2, 1 << 20), dtype=torch.uint8, device=DEV)[:, ::2])
