@@ -22,8 +22,9 @@
  * alone (one MFMA shape, one accumulator; k ascending in MODE_BF16, and in
  * MODE_INT8 from a start fixed by the column, which cannot change an exact
  * integer sum), never by the number of rows or a row's position in the batch;
- * the softmax partial sums are fixed by V alone.  A row's outputs are therefore bitwise identical at every batch
- * size.  ("12 Exactness", section 12.2: every matrix-product kernel fixes its
+ * the softmax partial sums are fixed by V alone.  A row's outputs are
+ * therefore bitwise identical at every batch size.  ("12 Exactness", section
+ * 12.2: every matrix-product kernel fixes its
  * reduction order by the weight's shape and never by the row count;
  * "Integer-Only Arithmetic", section "Why kernels don't always add in the same
  * order": split reductions chosen by batch size break batch invariance.)
@@ -37,9 +38,11 @@
  * asynchronous on `stream` (a hipStream_t; NULL = the default stream).
  *
  * Errors.  Arguments are validated on the host, synchronously, before any work
- * is queued; on any error nothing is queued and the status says why.  A failed
- * launch returns LMHEAD_E_HIP (lmhead_last_error() has the HIP message).  No
- * exception or abort crosses this interface.  Inputs are assumed finite.
+ * is queued; on a validation error nothing is queued and the status says why.
+ * A failed launch returns LMHEAD_E_HIP (lmhead_last_error() has the HIP
+ * message); where a call launches two kernels and the second launch fails,
+ * the first may already be queued.  No exception or abort crosses this
+ * interface.  Inputs are assumed finite.
  */
 #ifndef LMHEAD_H_
 #define LMHEAD_H_
