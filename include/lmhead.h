@@ -24,8 +24,8 @@
  * integer sum), never by the number of rows or a row's position in the batch;
  * the softmax partial sums are fixed by V alone.  A row's outputs are
  * therefore bitwise identical at every batch size.  ("12 Exactness", section
- * 12.2: every matrix-product kernel fixes its
- * reduction order by the weight's shape and never by the row count;
+ * 12.2: every matrix-product kernel fixes its reduction order by the weight's
+ * shape and never by the row count;
  * "Integer-Only Arithmetic", section "Why kernels don't always add in the same
  * order": split reductions chosen by batch size break batch invariance.)
  *
