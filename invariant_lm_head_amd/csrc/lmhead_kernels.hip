@@ -126,10 +126,12 @@ template <int P, class V> __device__ __forceinline__ V perm(V x) {
 // every row at a time, in two LDS rings: NSX stages of the X rows (read from
 // L2: every vocabulary tile re-reads them) and NSW > NSX stages of the W rows
 // (streamed from HBM once), so W loads are issued NSW - 1 stages ahead of use.
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BKB_, int NSX_, int NSW_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BKB_, int NSX_, int NSW_,
+          bool WPAIR_ = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int BKB = BKB_, NSX = NSX_, NSW = NSW_;
+  static constexpr bool WPAIR = WPAIR_;
   static constexpr int NW = WAVES_M * WAVES_N, NT = NW * 64;
   static constexpr int WM = BM / WAVES_M / 32;  // 32-row MFMA tiles per wave
   static constexpr int WN = BN / WAVES_N / 32;  // 32-column MFMA tiles per wave
@@ -156,14 +158,19 @@ struct Tile {
   // NSW > NSX: W stage b + NSW is issued spread over the k-steps after boundary
   // b, ahead of the X stage it is consumed with.  NSW == NSX: both are issued at
   // the boundary, and each boundary waits for every load of the next stage.
-  static constexpr bool WSPREAD = NSW > NSX;
+  // WPAIR (NSX 2, NSW 4): W stages are issued two at a time at every other
+  // boundary, span by span (span i of stage s, then span i of stage s + 1), so
+  // the two halves of each row's 2 x BKB bytes reach memory back to back.
+  static constexpr bool WSPREAD = NSW > NSX && !WPAIR;
+  static_assert(!WPAIR || (NSX == 2 && NSW == 4), "paired W stages: rings of 2 and 4");
   static_assert(LDS <= 160 * 1024, "LDS budget");
   // loads of one wave in flight at once (after a boundary's issue) stay below
   // the 6-bit vmcnt counter
   static_assert((NSX - 1) * SPWX_MAX + (NSW - 1) * SPWW_MAX < 64, "vmcnt range");
   // this wave's loads issued after X stage s by the time stage s is awaited
   // (steady state; fewer near the last stages)
-  static constexpr int AFTER_MAX = WSPREAD ? SPWW_MIN + (NSX - 2) * (SPWX_MIN + SPWW_MIN) : 0;
+  static constexpr int AFTER_MAX =
+      WSPREAD ? SPWW_MIN + (NSX - 2) * (SPWX_MIN + SPWW_MIN) : WPAIR ? 2 * SPWW_MIN : 0;
   static_assert(STEPS % 2 == 0, "fragment double buffer parity");
   // epilogue exchange areas (one 32-row tile per wave row at a time) fit in LDS
   // below the fold's flag and row list, which take its top 288 bytes
@@ -948,6 +955,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   static_assert(MODE != 1 || ((1LL << LMH_ROT_SHIFT) % T::BN == 0 && 256 % T::BKB == 0),
                 "tile within one rotation group");
   const int64_t rot = MODE == 1 ? k_rotation(p.rowbytes, n0) : 0;
+  const int nst = (int)(p.rowbytes / T::BKB);  // stages per row
   auto koff = [&](int stage) -> int64_t {
     const int64_t o = (int64_t)stage * T::BKB + rot;
     return o >= p.rowbytes ? o - p.rowbytes : o;
@@ -984,6 +992,20 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
       if (T::WSPANS % T::NW == 0 || span < T::WSPANS)
         dma16(woff[i], base,
               __builtin_amdgcn_readfirstlane(lds0 + T::WRING + buf * T::WSTAGE + span * 1024));
+    }
+  };
+  // W stages s and s + 1 (those below nst), span by span
+  auto issue_w_pair = [&](int s) {
+    const char *base0 = wtile + koff(s), *base1 = wtile + koff(s + 1 < nst ? s + 1 : s);
+    const unsigned buf0 = lds0 + T::WRING + (s % T::NSW) * T::WSTAGE;
+    const unsigned buf1 = lds0 + T::WRING + ((s + 1) % T::NSW) * T::WSTAGE;
+#pragma unroll
+    for (int i = 0; i < T::SPWW_MAX; ++i) {
+      const int span = wave + i * T::NW;
+      if (T::WSPANS % T::NW == 0 || span < T::WSPANS) {
+        if (s < nst) dma16(woff[i], base0, __builtin_amdgcn_readfirstlane(buf0 + span * 1024));
+        if (s + 1 < nst) dma16(woff[i], base1, __builtin_amdgcn_readfirstlane(buf1 + span * 1024));
+      }
     }
   };
 
@@ -1037,15 +1059,21 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
 #pragma unroll
       for (int nt = 0; nt < T::WN; ++nt) acc[mt][nt] = A::mfma(af[mt], bfr[nt], acc[mt][nt]);
   };
-  const int nst = (int)(p.rowbytes / T::BKB);
   auto boundary = [&](int b) {  // b >= -NSW; buffers of stages b + NSX, b + NSW
     const int sx = b + T::NSX, sw = b + T::NSW;
     if (sx >= 0 && sx < nst) issue_x(sx, sx % T::NSX);
-    if (sw < nst) issue_w(sw, sw % T::NSW);
+    if constexpr (T::WPAIR) {
+      if (b & 1) issue_w_pair(b + T::NSW - 1);  // odd boundary b: W stages b + 3, b + 4
+    } else {
+      if (sw < nst) issue_w(sw, sw % T::NSW);
+    }
   };
   // loads this wave issued after X stage s, once boundaries <= s - 2 are issued
   // (with W issued at the boundary, after X: wait for everything)
+  // (paired W: boundary s - 2, which issued X stage s, then issued W stages
+  // s + 1 and s + 2 when s is odd; W stage s went out at boundary s - 3 or s - 4)
   auto after = [&](int s) {
+    if constexpr (T::WPAIR) return (s & 1) ? T::SPWW_MIN * ((s + 1 < nst) + (s + 2 < nst)) : 0;
     if constexpr (!T::WSPREAD) return 0;
     int n = s - T::NSX + T::NSW < nst ? T::SPWW_MIN : 0;
     const int lo = s - T::NSX + 1, hi = s - 2;  // whole boundaries after X stage s
@@ -1093,7 +1121,11 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
       wait_vm_le<T::AFTER_MAX>(after(t + 1));  // stage t + 1 has landed
       lds_barrier();
       if (t + T::NSX < nst) issue_x(t + T::NSX, t % T::NSX);
-      if (!T::WSPREAD && t + T::NSW < nst) issue_w(t + T::NSW, t % T::NSW);
+      if constexpr (T::WPAIR) {
+        if (t & 1) issue_w_pair(t + T::NSW - 1);
+      } else if constexpr (!T::WSPREAD) {
+        if (t + T::NSW < nst) issue_w(t + T::NSW, t % T::NSW);
+      }
       read_frags(smem + ((t + 1) % T::NSX) * T::XSTAGE,
                  smem + T::WRING + ((t + 1) % T::NSW) * T::WSTAGE, 0, fa[last ^ 1], fb[last ^ 1]);
     }
@@ -1650,8 +1682,12 @@ template <int BKB> using V0 = Tile<LMH_V0_TILE>;
 // whose rate also varied from copy to copy (23-31 us).  Float head only: the
 // int8 head's rotated k order works in 256-byte units.
 using V0d = Tile<32, 128, 1, 4, 512, 2, 2>;
+// V1 pairs its W stages (WPAIR): each row's 2 x BKB bytes go out back to back.
+// Measured on MI355X (TinyLlama head, W from HBM): batch 33 and 64 in 33.1-33.8
+// us against 34.2-35.0 us with a 3-deep spread W ring; the same pairing in
+// V3 was 4.5 us slower at batch 256 (its loads are limited by issue, not HBM).
 #ifndef LMH_V1_TILE
-#define LMH_V1_TILE 64, 128, 2, 2, BKB, 2, 3
+#define LMH_V1_TILE 64, 128, 2, 2, BKB, 2, 4, true
 #endif
 template <int BKB> using V1 = Tile<LMH_V1_TILE>;
 template <int BKB> using V2 = Tile<128, 128, 2, 2, BKB, 2, 4>;

@@ -158,7 +158,8 @@ def test_int8_extremes_exact(o):
 @pytest.mark.parametrize("mode", ["bf16", "int8"])
 @pytest.mark.parametrize("B,H,V", [(1, 64, 2), (2, 64, 3), (5, 128, 17), (17, 64, 129),
                                    (70, 192, 130), (300, 64, 1000), (1, 4096, 257),
-                                   (5, 64, 70001), (40, 128, 70001)])
+                                   (5, 64, 70001), (40, 128, 70001), (48, 192, 1000),
+                                   (64, 256, 1000)])
 def test_edge_shapes(o, mode, B, H, V):
     rng = np.random.default_rng(B * 1000 + V)
     t = rng.integers(0, V, B).astype(np.int32)
