@@ -1658,8 +1658,14 @@ __global__ void reverse_rows_kernel(const char *src, char *dst, int64_t rows, in
 #ifndef LMH_V4_TILE
 #define LMH_V4_TILE 256, 256, 4, 2, 128, 2, 3
 #endif
-template <int BKB> using V0w = Tile<32, 256, 1, 4, BKB, 2, 3>;
-template <int BKB> using V1w = Tile<64, 256, 2, 2, BKB, 2, 3>;
+#ifndef LMH_V0W_TILE
+#define LMH_V0W_TILE 32, 256, 1, 4, BKB, 2, 3
+#endif
+#ifndef LMH_V1W_TILE
+#define LMH_V1W_TILE 64, 256, 2, 2, BKB, 2, 3
+#endif
+template <int BKB> using V0w = Tile<LMH_V0W_TILE>;
+template <int BKB> using V1w = Tile<LMH_V1W_TILE>;
 // int8 head, large vocabularies: 512-column tiles with rings of equal depth
 // (2 x 64 KB of W), so the grid takes one round of the CUs where 256-column
 // tiles would take two.  Measured on MI355X (4096 x 128256, W from HBM): batch
