@@ -36,8 +36,10 @@
 // kernels don't always add in the same order": split-K chosen by batch size.)
 //
 // Data movement: operand tiles are staged HBM -> LDS with global_load_lds_dwordx4
-// (no register round trip), NS stages in flight, 16-byte chunks XOR-swizzled by
-// row so the MFMA fragment reads (ds_read_b128) are bank-conflict free.  The
+// (no register round trip), in rings of stages whose W loads are spread over
+// the k-steps, issued at the boundary, or issued in pairs (Tile), with 16-byte
+// chunks XOR-swizzled by row so the MFMA fragment reads (ds_read_b128) are
+// bank-conflict free.  The
 // workgroup -> tile map is XCD-aware: workgroups that share operand tiles run
 // on the same XCD (same L2).  Cross-lane reductions use v_permlane16_swap, DPP
 // and ds_swizzle.
@@ -1038,7 +1040,10 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   // suffices that this wave has at most after(s) loads in flight, the number it
   // issued after X stage s.  With NSW == NSX both stages are issued at the
   // boundary (X, then W) and boundary s - 1 waits for every load in flight,
-  // which are exactly stage s's.
+  // which are exactly stage s's.  With paired W stages (NSX 2, NSW 4) each
+  // odd boundary b issues X stage b + 2, then W stages b + 3 and b + 4; W stage
+  // s leaves before X stage s, and at most the pair issued after X stage s (s
+  // odd) may still be in flight at boundary s - 1.
   // Compute: within a stage, the fragments of k-step s + 1 are read while the
   // MFMAs of step s issue (one read per MFMA, so LDS latency hides behind the
   // matrix pipe); after the stage's last MFMAs every wave waits for stage t + 1,
