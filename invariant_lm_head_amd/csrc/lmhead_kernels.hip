@@ -39,10 +39,9 @@
 // (no register round trip), in rings of stages whose W loads are spread over
 // the k-steps, issued at the boundary, or issued in pairs (Tile), with 16-byte
 // chunks XOR-swizzled by row so the MFMA fragment reads (ds_read_b128) are
-// bank-conflict free.  The
-// workgroup -> tile map is XCD-aware: workgroups that share operand tiles run
-// on the same XCD (same L2).  Cross-lane reductions use v_permlane16_swap, DPP
-// and ds_swizzle.
+// bank-conflict free.  The workgroup -> tile map is XCD-aware: workgroups that
+// share operand tiles run on the same XCD (same L2).  Cross-lane reductions use
+// v_permlane16_swap, DPP and ds_swizzle.
 #include <hip/hip_runtime.h>
 #include <limits.h>
 #include <stdint.h>
