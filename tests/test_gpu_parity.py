@@ -212,6 +212,28 @@ def test_wide_plans_batch_invariant():
             assert np.array_equal(got, ref[:n]), n
 
 
+def test_wide_plans_batch_invariant_int8():
+    """The int8 head at 70,001 columns runs 512-column tiles at batches up to
+    64 and the usual tiles above: every row's top-2 ids, exact raw values and
+    log-prob have the same bits at batch 1, 17, 40 and 300."""
+    rng = np.random.default_rng(78)
+    B, H, V = 300, 128, 70001
+    x = gpu(rng.integers(-127, 128, (B, H)).astype(np.int8))
+    w = gpu(rng.integers(-127, 128, (V, H)).astype(np.int8))
+    s = gpu((2.0 ** -12 * rng.uniform(0.5, 2, B)).astype(np.float32))
+    t = gpu(rng.integers(0, V, B).astype(np.int32))
+
+    def run(n):
+        ids, vals, margin, raw = lmhead.greedy_top2(x[:n].contiguous(), w, row_scale=s[:n].contiguous())
+        lp = lmhead.logprob(x[:n].contiguous(), w, t[:n].contiguous(), row_scale=s[:n].contiguous())
+        return [host(a).view(np.int32) for a in (ids, raw, vals, margin, lp)]
+
+    full = run(B)
+    for n in (1, 17, 40):
+        for got, ref in zip(run(n), full):
+            assert np.array_equal(got, ref[:n]), n
+
+
 def test_exact_ties_go_to_lowest_id():
     """Identical W rows tie exactly on the GPU too (same arithmetic wherever the
     column sits): the lowest id wins and the margin is exactly 0."""
