@@ -1811,7 +1811,11 @@ Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V) {
     pl.variant = 1; pl.bm = V1<256>::BM; pl.bn = V1<256>::BN; pl.bkb = bkb256;
   } else if (B <= 128) {
     pl.variant = 2; pl.bm = 128; pl.bn = 128; pl.bkb = bkb128;
-  } else if (B <= 256) {
+  } else if (B <= 256 && (V + 255) / 256 < kCUs) {
+    // 256-column tiles would leave CUs idle: 256 x 128.  Where they fill the
+    // CUs (V >= 65281) the 256 x 256 tile below reads X half as often; measured
+    // on MI355X at 4096 x 128256, batch 129-256: 10-15% faster (float head),
+    // 11-14% (int8).  At batch 65-128 it was 13-30% slower (padded rows).
     pl.variant = 3; pl.bm = V3<128>::BM; pl.bn = V3<128>::BN; pl.bkb = bkb128;
   } else if (rowbytes % V4::BKB == 0) {
     pl.variant = 4; pl.bm = V4::BM; pl.bn = V4::BN; pl.bkb = V4::BKB;
