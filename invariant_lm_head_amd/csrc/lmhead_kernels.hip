@@ -1659,6 +1659,8 @@ __global__ void reverse_rows_kernel(const char *src, char *dst, int64_t rows, in
 //   0 with 512-byte stages (V0d) for the float head when rows allow it
 //   7: 32 x 512, 8: 64 x 512 in place of 5 and 6 for the int8 head when the
 //      512-column grid fits one round of the CUs
+//   9: 128 x 256 in place of 2 when ceil(V / 256) >= 256; 10: 128 x 512 for
+//      the int8 head where 7 and 8 apply
 #ifndef LMH_V4_TILE
 #define LMH_V4_TILE 256, 256, 4, 2, 128, 2, 3
 #endif
@@ -1701,6 +1703,14 @@ using V0d = Tile<32, 128, 1, 4, 512, 2, 2>;
 #endif
 template <int BKB> using V1 = Tile<LMH_V1_TILE>;
 template <int BKB> using V2 = Tile<128, 128, 2, 2, BKB, 2, 4>;
+// batches 65-128 at large vocabularies (ceil(V / 256) >= 256): 256-column
+// tiles (and 512-column ones for the int8 head where their grid fits one
+// round of the CUs) halve or quarter the X re-reads and the rounds.  Measured
+// on MI355X at 4096 x 128256, batch 65-128, bitwise identical: float head
+// 183-200 us (65-72% of HBM) against 202-239 us; int8 103-105 us (63%) against
+// 128-131 us (51%), 115-117 us with 256-column tiles.
+template <int BKB> using V2w = Tile<128, 256, 4, 2, BKB, 2, 3>;
+template <int BKB> using V2x = Tile<128, 512, 4, 2, BKB, 2, 2>;
 template <int BKB> using V3 = Tile<LMH_V3_TILE>;
 using V4 = Tile<LMH_V4_TILE>;
 // V4 when the row is not a whole number of its stages
@@ -1782,6 +1792,15 @@ hipError_t launch_mode(int epi, const Plan &plan, const Params &p, hipStream_t s
         return launch_tile<V1x<64>, MODE, false>(epi, p, s);
       }
       return hipErrorInvalidValue;  // int8 plans only
+    case 9:
+      if (plan.bkb == 128) return launch_tile<V2w<128>, MODE, false>(epi, p, s);
+      return launch_tile<V2w<64>, MODE, false>(epi, p, s);
+    case 10:
+      if constexpr (MODE == 1) {
+        if (plan.bkb == 128) return launch_tile<V2x<128>, MODE, false>(epi, p, s);
+        return launch_tile<V2x<64>, MODE, false>(epi, p, s);
+      }
+      return hipErrorInvalidValue;  // int8 plan only
     default:
       if (plan.bkb == V4::BKB) return launch_tile<V4, MODE, false>(epi, p, s);
       return launch_tile<V4s, MODE, false>(epi, p, s);
@@ -1809,6 +1828,10 @@ Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V) {
     pl.variant = 6; pl.bm = V1w<128>::BM; pl.bn = V1w<128>::BN; pl.bkb = bkb128;
   } else if (B <= 64) {
     pl.variant = 1; pl.bm = V1<256>::BM; pl.bn = V1<256>::BN; pl.bkb = bkb256;
+  } else if (B <= 128 && wide512) {
+    pl.variant = 10; pl.bm = V2x<128>::BM; pl.bn = V2x<128>::BN; pl.bkb = bkb128;
+  } else if (B <= 128 && (V + 255) / 256 >= kCUs) {
+    pl.variant = 9; pl.bm = V2w<128>::BM; pl.bn = V2w<128>::BN; pl.bkb = bkb128;
   } else if (B <= 128) {
     pl.variant = 2; pl.bm = 128; pl.bn = 128; pl.bkb = bkb128;
   } else if (B <= 256 && (V + 255) / 256 < kCUs) {

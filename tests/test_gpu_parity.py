@@ -190,8 +190,9 @@ def test_edge_shapes(o, mode, B, H, V):
 def test_wide_plans_batch_invariant():
     """A vocabulary of more than 512 blocks (70,001 columns) runs 256-column
     tiles at batches up to 64 and the usual tiles above: greedy, log-prob and
-    sampled draws of every row have the same bits at batch 1, 17, 40, 200 and
-    300 (batch 200 takes 256-column tiles too at this vocabulary)."""
+    sampled draws of every row have the same bits at batch 1, 17, 40, 100, 200
+    and 300 (batches 100 and 200 take 256-column tiles too at this
+    vocabulary)."""
     rng = np.random.default_rng(77)
     B, H, V = 300, 128, 70001
     x = gpu_bf16(synth.bf16_from_f32(rng.standard_normal((B, H)).astype(np.float32)))
@@ -208,7 +209,7 @@ def test_wide_plans_batch_invariant():
         return [host(a).view(np.int32) for a in (ids, vals, margin, lp, tok, val, gap)]
 
     full = run(B)
-    for n in (1, 17, 40, 200):
+    for n in (1, 17, 40, 100, 200):
         for got, ref in zip(run(n), full):
             assert np.array_equal(got, ref[:n]), n
 
@@ -216,7 +217,7 @@ def test_wide_plans_batch_invariant():
 def test_wide_plans_batch_invariant_int8():
     """The int8 head at 70,001 columns runs 512-column tiles at batches up to
     64 and the usual tiles above: every row's top-2 ids, exact raw values and
-    log-prob have the same bits at batch 1, 17, 40, 200 and 300."""
+    log-prob have the same bits at batch 1, 17, 40, 100, 200 and 300."""
     rng = np.random.default_rng(78)
     B, H, V = 300, 128, 70001
     x = gpu(rng.integers(-127, 128, (B, H)).astype(np.int8))
@@ -230,7 +231,7 @@ def test_wide_plans_batch_invariant_int8():
         return [host(a).view(np.int32) for a in (ids, raw, vals, margin, lp)]
 
     full = run(B)
-    for n in (1, 17, 40, 200):
+    for n in (1, 17, 40, 100, 200):
         for got, ref in zip(run(n), full):
             assert np.array_equal(got, ref[:n]), n
 
