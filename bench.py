@@ -367,6 +367,19 @@ def extras(torch, lmhead, synth, bf16, x, w_copies, d):
         f"{res['tinyllama_logprob_b512']['us_per_call']:.1f} / "
         f"{res['tinyllama_logits_b512']['us_per_call']:.1f} us")
 
+    # the tiny workload (H=64, V=1000, batch 4; W stays in L2): latency per call
+    dt = synth.make_inputs("tiny")
+    xt, wt = bf16(dt["x"]), bf16(dt["w"])
+    tt_t = torch.from_numpy(dt["target"]).to(x.device)
+    tiny = {}
+    for kind in ("greedy", "logprob", "logits"):
+        c = Caller(torch, lmhead, [xt], [wt], 4, 64, 1000, kind=kind, target=tt_t)
+        tiny[f"{kind}_us_per_call"] = time_calls(torch, c, 200) * 1e6
+    res["tiny_b4"] = tiny
+    log("tiny 4 x 64 x 1000: greedy / logprob / logits "
+        f"{tiny['greedy_us_per_call']:.1f} / {tiny['logprob_us_per_call']:.1f} / "
+        f"{tiny['logits_us_per_call']:.1f} us")
+
     # margin-gated float32 recompute (tau = 1e-3) against the plain bf16-output head
     for B in (1, 512):
         xb = [x[:B].contiguous()] * NCOPIES
@@ -420,14 +433,14 @@ def extras(torch, lmhead, synth, bf16, x, w_copies, d):
     log(f"log-prob 16384x151936x4096: {tt * 1e3:.2f} ms = "
         f"{100 * res['logprob_16384x151936x4096']['roofline']['frac']:.1f}% of MFMA peak")
 
-    # int8 head, 4096 x 128256, batch 1 and 512
+    # int8 head, 4096 x 128256, batch 1 .. 512
     i8 = synth.make_inputs("int8")
     Hi, Vi = i8["H"], i8["V"]
     xi = torch.from_numpy(i8["x"]).to(x.device)
     wi = [torch.from_numpy(i8["w"]).to(x.device)]
     si = torch.from_numpy(i8["scale"]).to(x.device)
     del i8
-    for B in (1, 512):
+    for B in (1, 8, 64, 256, 512):
         c = Caller(torch, lmhead, [xi[:B].contiguous()], wi, B, Hi, Vi, mode=1, scale=si[:B])
         tt = time_calls(torch, c, 50)
         res[f"int8_b{B}"] = {"us_per_call": tt * 1e6, "rows_per_s": B / tt,
