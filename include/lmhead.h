@@ -79,9 +79,9 @@ typedef enum { LMHEAD_MODE_BF16 = 0, LMHEAD_MODE_INT8 = 1 } lmhead_mode;
 typedef enum { LMHEAD_ROUND_F32 = 0, LMHEAD_ROUND_BF16 = 1 } lmhead_round;
 
 /* Bytes of device workspace lmhead_greedy_top2 / lmhead_logprob need for this
- * shape (0 if the shape is invalid).  The workspace must be zero-filled ONCE by
- * the caller before its first use; every call leaves it zero-filled again.  One
- * workspace must not be shared by two calls that can run at the same time. */
+ * shape (0 if the shape is invalid).  Its contents on entry do not matter (no
+ * clearing is needed); each call overwrites what it uses.  One workspace must
+ * not be shared by two calls that can run at the same time. */
 size_t lmhead_workspace_bytes(int mode, int64_t B, int64_t H, int64_t V);
 
 /* Full logits.  logits[b, v] = sum_k x[b, k] * w[v, k], stored row-major [B, V]

@@ -69,13 +69,12 @@ lmh::Params base_params(int mode, const void *x, const void *w, int64_t B, int64
 namespace lmh {
 size_t workspace_layout(int64_t B, int64_t V, size_t *off_zt, size_t *off_records) {
   auto up = [](size_t n) { return (n + 255) & ~(size_t)255; };
-  const size_t tickets = up(sizeof(unsigned) * (size_t)((B + 15) / 16));
   const size_t zt = up(sizeof(int32_t) * (size_t)B);
   const size_t nblocks = (size_t)((V + kBlockCols - 1) / kBlockCols);
   const size_t records = 16 * (size_t)B * nblocks;
-  if (off_zt) *off_zt = tickets;
-  if (off_records) *off_records = tickets + zt;
-  return tickets + zt + records;
+  if (off_zt) *off_zt = 0;
+  if (off_records) *off_records = zt;
+  return zt + records;
 }
 }  // namespace lmh
 
@@ -106,7 +105,6 @@ static lmhead_status bind_workspace(lmh::Params &p, void *ws, size_t ws_bytes, i
   const size_t need = lmh::workspace_layout(B, V, &off_zt, &off_rec);
   if (!ws || ws_bytes < need) return LMHEAD_E_WORKSPACE;
   if (!aligned16(ws)) return LMHEAD_E_ALIGN;
-  p.tickets = (unsigned *)ws;
   p.zt = (int32_t *)((char *)ws + off_zt);
   p.records = (uint4 *)((char *)ws + off_rec);
   return LMHEAD_OK;

@@ -32,7 +32,6 @@ struct Params {
   float tau;
   int32_t *gated;         // [B] 1 = re-ranked
   float *logprob;         // [B]
-  unsigned *tickets;      // [ceil(B/16)] zero on entry and on exit
   int32_t *zt;            // [B] target logit bits (float32 or int32)
   uint4 *records;         // [B][nblocks] per-block partials
   // kSample: seeded Gumbel-max draw of every row

@@ -8,11 +8,9 @@
 //   kSample per-row top-2 of z / T + Gumbel noise (seeded Gumbel-max draw);
 //   kLseInt (int8) per-row block max and the exact sum of integer exps, for
 //           the all-integer log-softmax (see "integer front and back").
-// The block partials of a row are then folded into the outputs, either by the
-// last workgroup of the launch (atomic ticket, small batches: merge_rows) or by
-// a second, row-parallel kernel (larger batches: merge_rows again for the
-// log-prob folds, whose slot order it fixes; one wave per row for the top-2
-// folds, which are exact in any order).
+// The block partials of a row are then folded into the outputs by a second,
+// row-parallel kernel (merge_rows for the log-prob folds, whose slot order it
+// fixes; one wave per row for the top-2 folds, which are exact in any order).
 //
 // Batch invariance (one reduction order per logit, fixed by H only):
 //   * every logit is acc = 0; for s = 0 .. H*esize/32 - 1: acc = MFMA(A_s, B_s, acc)
@@ -174,10 +172,7 @@ struct Tile {
       WSPREAD ? SPWW_MIN + (NSX - 2) * (SPWX_MIN + SPWW_MIN) : WPAIR ? 2 * SPWW_MIN : 0;
   static_assert(STEPS % 2 == 0, "fragment double buffer parity");
   // epilogue exchange areas (one 32-row tile per wave row at a time) fit in LDS
-  // below the fold's flag and row list, which take its top 288 bytes
-  static constexpr int FOLD_LDS = 288;
-  static_assert(WAVES_M * 32 * WAVES_N * (4 + 32 * 4) + FOLD_LDS <= LDS &&
-                    BM * WAVES_N * 16 + FOLD_LDS <= LDS,
+  static_assert(WAVES_M * 32 * WAVES_N * (4 + 32 * 4) <= LDS && BM * WAVES_N * 16 <= LDS,
                 "exchange");
 };
 
@@ -761,54 +756,47 @@ __device__ __forceinline__ void put_top2(const Params &p, int row, const Top2 &t
   }
 }
 
+// The log-prob fold of rows row0 .. row0 + nrows - 1: kSlots threads per row.
 template <int MODE, int EPI>
 __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nthreads) {
+  static_assert(EPI == kLse || EPI == kLseInt, "top-2 folds use lmhead_merge_top2_kernel");
   using val_t = typename Arith<MODE>::val_t;
   const int slot = tid & (kSlots - 1);
   const int nb = p.nblocks;
   for (int g = tid / kSlots; g < nrows; g += nthreads / kSlots) {
     const int row = row0 + g;
     const uint4 *rec = p.records + (int64_t)row * nb;
-    if constexpr (EPI == kTop2 || EPI == kSample) {
-      Top2 t{0, 0};
-      // 16 records per slot in flight per round (one memory latency per round)
+    // The row max (exact), then the sum of the rescaled block sums in slot
+    // order.  16 records per slot are in flight per round of loads (one
+    // memory latency per round).  When one round covers the row (nb <= 256),
+    // its records stay in registers for the sum; otherwise they are read
+    // again.  The row's own inputs are loaded first, so their latency
+    // overlaps the records'.
+    const int tgt = p.target[row];
+    const int zt = p.zt[row];  // meaningful only for a target in range
+    const bool one_round = nb <= kChunk * kSlots;
+    if constexpr (EPI == kLseInt) {
+      const IntScale sc = int_row_scale(p.unit_m, p.unit_e, p.step_m[row], p.step_e[row]);
+      uint4 r[kChunk];
+      int mx = INT_MIN;
       for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
-        // every load is issued (a clamped index stays in bounds), so all 16 are
-        // in flight at once; blocks past the row's end are replaced afterwards
-        uint4 r[kChunk];
 #pragma unroll
         for (int q = 0; q < kChunk; ++q) r[q] = rec[min(b0 + q * kSlots, nb - 1)];
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q)
-          if (b0 + q * kSlots < nb) t = t2_merge(t, t2_unpack(r[q]));
-      }
-      t = t2_merge(t, perm<kQuadX1>(t));
-      t = t2_merge(t, perm<kQuadX2>(t));
-      t = t2_merge(t, perm<kHalfMirror>(t));
-      t = t2_merge(t, perm<kMirror>(t));
-      if (slot == 0) put_top2<MODE, EPI>(p, row, t);
-    } else if constexpr (EPI == kLseInt) {
-      // pass 1: the row max (exact); pass 2: the exact sum of the rescaled
-      // block sums (integers: the order does not matter)
-      int mx = INT_MIN;
-      for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
-        int m[kChunk];
-#pragma unroll
-        for (int q = 0; q < kChunk; ++q) m[q] = (int)rec[min(b0 + q * kSlots, nb - 1)].x;
-#pragma unroll
-        for (int q = 0; q < kChunk; ++q) mx = m[q] > mx ? m[q] : mx;
+        for (int q = 0; q < kChunk; ++q) mx = (int)r[q].x > mx ? (int)r[q].x : mx;
       }
       int o;
       o = perm<kQuadX1>(mx); mx = o > mx ? o : mx;
       o = perm<kQuadX2>(mx); mx = o > mx ? o : mx;
       o = perm<kHalfMirror>(mx); mx = o > mx ? o : mx;
       o = perm<kMirror>(mx); mx = o > mx ? o : mx;
-      const IntScale sc = int_row_scale(p.unit_m, p.unit_e, p.step_m[row], p.step_e[row]);
+      // integer terms: the order does not matter
       uint64_t S = 0;
       for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
-        uint4 r[kChunk];
+        if (!one_round) {
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q) r[q] = rec[min(b0 + q * kSlots, nb - 1)];
+          for (int q = 0; q < kChunk; ++q) r[q] = rec[min(b0 + q * kSlots, nb - 1)];
+        }
 #pragma unroll
         for (int q = 0; q < kChunk; ++q) {
           if (b0 + q * kSlots < nb) {
@@ -823,10 +811,9 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
       S += perm64<kHalfMirror>(S);
       S += perm64<kMirror>(S);
       if (slot == 0) {
-        const int tgt = p.target[row];
         int64_t lp = INT64_MIN;
         if (tgt >= 0 && tgt < p.V && sc.m != 0u) {
-          const uint64_t Tt = int_nats((uint32_t)mx - (uint32_t)p.zt[row], sc);
+          const uint64_t Tt = int_nats((uint32_t)mx - (uint32_t)zt, sc);
           const uint64_t L = rnd64((uint64_t)iln_q30(S), kExpFrac - kNatsFrac);
           const uint64_t nl = Tt + L;  // < 2^63 + 2^40: no wrap
           lp = nl > (uint64_t)INT64_MAX ? -INT64_MAX : -(int64_t)nl;
@@ -834,15 +821,19 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
         p.logprob_q[row] = lp;
       }
     } else {
-      // pass 1: the row max (exact); pass 2: the sum in slot order
+      float cr = kLog2e, sr = 1.0f;
+      if constexpr (MODE == 1) {
+        sr = p.scale ? p.scale[row] : 1.0f;
+        cr = sr * kLog2e;
+      }
+      uint2 r[kChunk];
       val_t mx = lowest_of<val_t>();
       for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
-        int m[kChunk];
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q) m[q] = (int)rec[min(b0 + q * kSlots, nb - 1)].x;
+        for (int q = 0; q < kChunk; ++q) r[q] = *(const uint2 *)&rec[min(b0 + q * kSlots, nb - 1)];
 #pragma unroll
         for (int q = 0; q < kChunk; ++q) {
-          const val_t o = vfrom<val_t>(m[q]);  // a repeated last block cannot change a max
+          const val_t o = vfrom<val_t>((int)r[q].x);  // a repeated last block cannot change a max
           mx = o > mx ? o : mx;
         }
       }
@@ -851,16 +842,12 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
       o = perm<kQuadX2>(mx); mx = o > mx ? o : mx;
       o = perm<kHalfMirror>(mx); mx = o > mx ? o : mx;
       o = perm<kMirror>(mx); mx = o > mx ? o : mx;
-      float cr = kLog2e, sr = 1.0f;
-      if constexpr (MODE == 1) {
-        sr = p.scale ? p.scale[row] : 1.0f;
-        cr = sr * kLog2e;
-      }
       float s = 0.0f;
       for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
-        uint2 r[kChunk];
+        if (!one_round) {
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q) r[q] = *(const uint2 *)&rec[min(b0 + q * kSlots, nb - 1)];
+          for (int q = 0; q < kChunk; ++q) r[q] = *(const uint2 *)&rec[min(b0 + q * kSlots, nb - 1)];
+        }
 #pragma unroll
         for (int q = 0; q < kChunk; ++q) {
           if (b0 + q * kSlots < nb) {
@@ -876,13 +863,12 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
       s = s + perm<kHalfMirror>(s);
       s = s + perm<kMirror>(s);
       if (slot == 0) {
-        const int tgt = p.target[row];
         float lp = __builtin_nanf("");
         if (tgt >= 0 && tgt < p.V) {
           if constexpr (MODE == 0) {
-            lp = (__int_as_float(p.zt[row]) - mx) - kLn2 * log2_hw(s);
+            lp = (__int_as_float(zt) - mx) - kLn2 * log2_hw(s);
           } else {
-            if (scale_ok(sr)) lp = (float)(p.zt[row] - mx) * sr - kLn2 * log2_hw(s);
+            if (scale_ok(sr)) lp = (float)(zt - mx) * sr - kLn2 * log2_hw(s);
           }
         }
         p.logprob[row] = lp;
@@ -891,35 +877,16 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
   }
 }
 
-// Store of one block record.  In a fused launch the records are read by the
-// last workgroup, possibly on another XCD, after the release / acquire pair of
-// the ticket; written through to the agent coherence point (agent-scope atomic
-// stores), they leave the release's L2 writeback next to nothing to do
-// (measured: batch 1 and 8 about 0.6 us faster).  The fold kernels read them
-// after the launch ends, so there they are plain stores.
-template <bool THROUGH> __device__ __forceinline__ void put_record(uint4 *d, uint4 v) {
-  if constexpr (THROUGH) {
-    __hip_atomic_store((unsigned long long *)d, ((unsigned long long)v.y << 32) | v.x,
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store((unsigned long long *)d + 1, ((unsigned long long)v.w << 32) | v.z,
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-    *d = v;
-  }
-}
+// one block record (read by the fold kernel after the tile launch ends)
+__device__ __forceinline__ void put_record(uint4 *d, uint4 v) { *d = v; }
 
 // ------------------------------------------------------------------ kernel
-template <class T, int MODE, int EPI, bool FUSED>
+template <class T, int MODE, int EPI>
 __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   using A = Arith<MODE>;
   using acc_t = typename A::acc_t;
   using val_t = typename A::val_t;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
-  // the fold's flag and the gated recompute's row list sit at the top of the
-  // stage rings, which are free by then (the epilogue exchange uses the bottom)
-  static_assert(16 + 4 * 68 <= T::FOLD_LDS && kGateLdsInts <= 68, "fold LDS");
-  int &s_last = *(int *)(smem + T::LDS - 16);
-  int *s_gate = (int *)(smem + T::LDS - T::FOLD_LDS);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1233,7 +1200,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
               const int row = m0 + lrow;
               const int blk = wcol0 / kBlockCols + b;
               if (!dup && row < p.B && blk < p.nblocks)
-                put_record<FUSED>(&p.records[(int64_t)row * p.nblocks + blk], t2_pack(r));
+                put_record(&p.records[(int64_t)row * p.nblocks + blk], t2_pack(r));
             } else {
               if (!dup) xch[lrow * T::WAVES_N + wn] = t2_pack(r);
             }
@@ -1265,7 +1232,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
               const int row = m0 + lrow;
               const int blk = wcol0 / kBlockCols + b;
               if (!dup && row < p.B && blk < p.nblocks)
-                put_record<FUSED>(&p.records[(int64_t)row * p.nblocks + blk], t2_pack(r));
+                put_record(&p.records[(int64_t)row * p.nblocks + blk], t2_pack(r));
             } else {
               if (!dup) xch[lrow * T::WAVES_N + wn] = t2_pack(r);
             }
@@ -1286,7 +1253,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
             t = t2_merge(t, t2_unpack(xch[lrow * T::WAVES_N + wn + pp]));
           const int blk = wcol0 / kBlockCols;
           if (row < p.B && blk < p.nblocks)
-            put_record<FUSED>(&p.records[(int64_t)row * p.nblocks + blk], t2_pack(t));
+            put_record(&p.records[(int64_t)row * p.nblocks + blk], t2_pack(t));
         }
       }
     } else if constexpr (EPI == kLseInt) {
@@ -1380,15 +1347,15 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
                 sum += xsum[(xbase + acc_row(u, h)) * T::WAVES_N + wn + pp];
               const int row = m0 + lrow;
               if (row < p.B && blk < p.nblocks)
-                put_record<FUSED>(&p.records[(int64_t)row * p.nblocks + blk],
-                                  make_uint4((unsigned)r.m, (unsigned)sum, (unsigned)(sum >> 32), 0u));
+                put_record(&p.records[(int64_t)row * p.nblocks + blk],
+                           make_uint4((unsigned)r.m, (unsigned)sum, (unsigned)(sum >> 32), 0u));
             }
             __syncthreads();
           } else {
             const int row = m0 + lrow;
             if (!dup && row < p.B && blk < p.nblocks)
-              put_record<FUSED>(&p.records[(int64_t)row * p.nblocks + blk],
-                                make_uint4((unsigned)r.m, r.lo, r.hi, 0u));
+              put_record(&p.records[(int64_t)row * p.nblocks + blk],
+                         make_uint4((unsigned)r.m, r.lo, r.hi, 0u));
           }
         }
       });
@@ -1494,47 +1461,26 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
             const int row = m0 + lbase + acc_row(u, h);
             const int blk = wcol0 / kBlockCols + b;
             if (!dup && row < p.B && blk < p.nblocks)
-              put_record<FUSED>(&p.records[(int64_t)row * p.nblocks + blk],
-                                make_uint4((unsigned)r.m, __float_as_uint(r.s), 0u, 0u));
+              put_record(&p.records[(int64_t)row * p.nblocks + blk],
+                         make_uint4((unsigned)r.m, __float_as_uint(r.s), 0u, 0u));
           }
           if constexpr (T::PARTS > 1) __syncthreads();
         }
       }
     }
-
-    if constexpr (FUSED) {
-      // ---- the last workgroup of this row tile folds every block of its rows.
-      // Every wave's record stores are complete (vmcnt 0) before the barrier;
-      // one agent-scope release then publishes them to the other XCDs.
-      wait_vm<0>();
-      __syncthreads();
-      if (tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const unsigned prev = atomicAdd(&p.tickets[tm], 1u);
-        s_last = prev == (unsigned)(p.grid_n - 1);
-      }
-      __syncthreads();
-      if (!s_last) return;
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      merge_rows<MODE, EPI>(p, m0, min(T::BM, p.B - m0), tid, T::NT);
-      if constexpr (MODE == 0 && EPI == kTop2)
-        if (p.gated) gate_rows(p, m0, min(T::BM, p.B - m0), tid, T::NT, s_gate);
-      if (tid == 0) p.tickets[tm] = 0u;  // leave the workspace zeroed for the next call
-    }
   }
 }
 
-// the row-parallel log-prob fold for larger batches: 16 rows per workgroup, in
-// the slot order of merge_rows (the same order as the fused fold)
+// the row-parallel log-prob fold: 16 rows per workgroup, in the slot order of
+// merge_rows
 template <int MODE, int EPI>
 __global__ __launch_bounds__(256) void lmhead_merge_kernel(Params p) {
-  static_assert(EPI == kLse || EPI == kLseInt, "top-2 folds use lmhead_merge_top2_kernel");
   const int row0 = blockIdx.x * (256 / kSlots);
   merge_rows<MODE, EPI>(p, row0, min(256 / kSlots, p.B - row0), threadIdx.x, 256);
 }
 
-// The top-2 fold for larger batches (greedy and sampling): one wave per row,
-// four rows per workgroup, so a batch of 512 spreads over 128 workgroups.  A
+// The top-2 fold (greedy and sampling): one wave per row, four rows per
+// workgroup, so a batch of 512 spreads over 128 workgroups.  A
 // top-2 of a union is exact in any order, so the lane count does not change a
 // bit (the log-prob folds keep their fixed slot order in merge_rows).
 template <int MODE, int EPI>
@@ -1650,7 +1596,7 @@ __global__ void reverse_rows_kernel(const char *src, char *dst, int64_t rows, in
 
 // ------------------------------------------------------------ dispatch
 // tile shapes, indexed by Plan::variant
-//   0: 32 x 128  (batch <= 32, fold fused)   1: 64 x 128  (<= 64)
+//   0: 32 x 128  (batch <= 32)   1: 64 x 128  (<= 64)
 //   2: 128 x 128 (<= 128)                    3: 256 x 128 (<= 256)
 //   4: 256 x 256 (> 256)
 //   5: 32 x 256, 6: 64 x 256 in place of 0 and 1 when the 128-column grid
@@ -1716,43 +1662,41 @@ using V4 = Tile<LMH_V4_TILE>;
 // V4 when the row is not a whole number of its stages
 using V4s = Tile<256, 256, 4, 2, 64, 2, 6>;
 
-template <class T, int MODE, bool FUSED>
+template <class T, int MODE>
 hipError_t launch_tile(int epi, const Params &p, hipStream_t s) {
   const dim3 grid(p.grid_m * p.grid_n), block(T::NT);
   switch (epi) {
     case kStore:
-      hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kStore, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kStore>), grid, block, 0, s, p);
       return hipGetLastError();
     case kTop2:
-      hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kTop2, FUSED>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kTop2>), grid, block, 0, s, p);
       break;
     case kSample:
-      hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kSample, FUSED>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kSample>), grid, block, 0, s, p);
       break;
     case kLseInt:
       if constexpr (MODE == 1)
-        hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kLseInt, FUSED>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kLseInt>), grid, block, 0, s, p);
       else
         return hipErrorInvalidValue;
       break;
     default:
-      hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kLse, FUSED>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((lmhead_tile_kernel<T, MODE, kLse>), grid, block, 0, s, p);
       break;
   }
-  if constexpr (!FUSED) {
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const dim3 mgrid((p.B + 256 / kSlots - 1) / (256 / kSlots));
-    const dim3 tgrid((p.B + 3) / 4);  // lmhead_merge_top2_kernel: four rows per workgroup
-    if (epi == kTop2)
-      hipLaunchKernelGGL((lmhead_merge_top2_kernel<MODE, kTop2>), tgrid, dim3(256), 0, s, p);
-    else if (epi == kSample)
-      hipLaunchKernelGGL((lmhead_merge_top2_kernel<MODE, kSample>), tgrid, dim3(256), 0, s, p);
-    else if (MODE == 1 && epi == kLseInt)
-      hipLaunchKernelGGL((lmhead_merge_kernel<1, kLseInt>), mgrid, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL((lmhead_merge_kernel<MODE, kLse>), mgrid, dim3(256), 0, s, p);
-  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 mgrid((p.B + 256 / kSlots - 1) / (256 / kSlots));
+  const dim3 tgrid((p.B + 3) / 4);  // lmhead_merge_top2_kernel: four rows per workgroup
+  if (epi == kTop2)
+    hipLaunchKernelGGL((lmhead_merge_top2_kernel<MODE, kTop2>), tgrid, dim3(256), 0, s, p);
+  else if (epi == kSample)
+    hipLaunchKernelGGL((lmhead_merge_top2_kernel<MODE, kSample>), tgrid, dim3(256), 0, s, p);
+  else if (MODE == 1 && epi == kLseInt)
+    hipLaunchKernelGGL((lmhead_merge_kernel<1, kLseInt>), mgrid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((lmhead_merge_kernel<MODE, kLse>), mgrid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1761,49 +1705,49 @@ hipError_t launch_mode(int epi, const Plan &plan, const Params &p, hipStream_t s
   switch (plan.variant) {
     case 0:
       if constexpr (MODE == 0)
-        if (plan.bkb == V0d::BKB) return launch_tile<V0d, MODE, true>(epi, p, s);
-      if (plan.bkb == 256) return launch_tile<V0<256>, MODE, true>(epi, p, s);
-      if (plan.bkb == 128) return launch_tile<V0<128>, MODE, true>(epi, p, s);
-      return launch_tile<V0<64>, MODE, true>(epi, p, s);
+        if (plan.bkb == V0d::BKB) return launch_tile<V0d, MODE>(epi, p, s);
+      if (plan.bkb == 256) return launch_tile<V0<256>, MODE>(epi, p, s);
+      if (plan.bkb == 128) return launch_tile<V0<128>, MODE>(epi, p, s);
+      return launch_tile<V0<64>, MODE>(epi, p, s);
     case 1:
-      if (plan.bkb == 256) return launch_tile<V1<256>, MODE, false>(epi, p, s);
-      if (plan.bkb == 128) return launch_tile<V1<128>, MODE, false>(epi, p, s);
-      return launch_tile<V1<64>, MODE, false>(epi, p, s);
+      if (plan.bkb == 256) return launch_tile<V1<256>, MODE>(epi, p, s);
+      if (plan.bkb == 128) return launch_tile<V1<128>, MODE>(epi, p, s);
+      return launch_tile<V1<64>, MODE>(epi, p, s);
     case 2:
-      if (plan.bkb == 128) return launch_tile<V2<128>, MODE, false>(epi, p, s);
-      return launch_tile<V2<64>, MODE, false>(epi, p, s);
+      if (plan.bkb == 128) return launch_tile<V2<128>, MODE>(epi, p, s);
+      return launch_tile<V2<64>, MODE>(epi, p, s);
     case 3:
-      if (plan.bkb == 128) return launch_tile<V3<128>, MODE, false>(epi, p, s);
-      return launch_tile<V3<64>, MODE, false>(epi, p, s);
+      if (plan.bkb == 128) return launch_tile<V3<128>, MODE>(epi, p, s);
+      return launch_tile<V3<64>, MODE>(epi, p, s);
     case 5:
-      if (plan.bkb == 128) return launch_tile<V0w<128>, MODE, true>(epi, p, s);
-      return launch_tile<V0w<64>, MODE, true>(epi, p, s);
+      if (plan.bkb == 128) return launch_tile<V0w<128>, MODE>(epi, p, s);
+      return launch_tile<V0w<64>, MODE>(epi, p, s);
     case 6:
-      if (plan.bkb == 128) return launch_tile<V1w<128>, MODE, false>(epi, p, s);
-      return launch_tile<V1w<64>, MODE, false>(epi, p, s);
+      if (plan.bkb == 128) return launch_tile<V1w<128>, MODE>(epi, p, s);
+      return launch_tile<V1w<64>, MODE>(epi, p, s);
     case 7:
     case 8:
       if constexpr (MODE == 1) {
         if (plan.variant == 7) {
-          if (plan.bkb == 128) return launch_tile<V0x<128>, MODE, true>(epi, p, s);
-          return launch_tile<V0x<64>, MODE, true>(epi, p, s);
+          if (plan.bkb == 128) return launch_tile<V0x<128>, MODE>(epi, p, s);
+          return launch_tile<V0x<64>, MODE>(epi, p, s);
         }
-        if (plan.bkb == 128) return launch_tile<V1x<128>, MODE, false>(epi, p, s);
-        return launch_tile<V1x<64>, MODE, false>(epi, p, s);
+        if (plan.bkb == 128) return launch_tile<V1x<128>, MODE>(epi, p, s);
+        return launch_tile<V1x<64>, MODE>(epi, p, s);
       }
       return hipErrorInvalidValue;  // int8 plans only
     case 9:
-      if (plan.bkb == 128) return launch_tile<V2w<128>, MODE, false>(epi, p, s);
-      return launch_tile<V2w<64>, MODE, false>(epi, p, s);
+      if (plan.bkb == 128) return launch_tile<V2w<128>, MODE>(epi, p, s);
+      return launch_tile<V2w<64>, MODE>(epi, p, s);
     case 10:
       if constexpr (MODE == 1) {
-        if (plan.bkb == 128) return launch_tile<V2x<128>, MODE, false>(epi, p, s);
-        return launch_tile<V2x<64>, MODE, false>(epi, p, s);
+        if (plan.bkb == 128) return launch_tile<V2x<128>, MODE>(epi, p, s);
+        return launch_tile<V2x<64>, MODE>(epi, p, s);
       }
       return hipErrorInvalidValue;  // int8 plan only
     default:
-      if (plan.bkb == V4::BKB) return launch_tile<V4, MODE, false>(epi, p, s);
-      return launch_tile<V4s, MODE, false>(epi, p, s);
+      if (plan.bkb == V4::BKB) return launch_tile<V4, MODE>(epi, p, s);
+      return launch_tile<V4s, MODE>(epi, p, s);
   }
 }
 

@@ -126,15 +126,13 @@ def workspace_bytes(mode: int, B: int, H: int, V: int) -> int:
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
-    """A zero-filled workspace of at least nbytes for the current stream.
-
-    The library leaves it zeroed after every call, so it is reused by all calls
-    ordered on that stream (calls on one stream never overlap)."""
+    """A workspace of at least nbytes for the current stream, reused by all
+    calls ordered on that stream (calls on one stream never overlap)."""
     dev = torch.device(device)
     key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(nbytes, 1 << 16), dtype=torch.uint8, device=dev)
         _ws_cache[key] = ws
     return ws
 

@@ -50,13 +50,13 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes_layout(lib):
-    # tickets (ceil(B/16) x 4 B) | target logits (B x 4 B) | B x ceil(V/128) 16-byte records,
-    # every region rounded up to 256 bytes
+    # target logits (B x 4 B) | B x ceil(V/128) 16-byte records, the first
+    # region rounded up to 256 bytes
     def up(n):
         return (n + 255) // 256 * 256
 
     for (B, H, V) in [(1, 2048, 32000), (512, 2048, 32000), (4, 64, 1000), (16384, 4096, 151936)]:
-        want = up(4 * ((B + 15) // 16)) + up(4 * B) + 16 * B * ((V + 127) // 128)
+        want = up(4 * B) + 16 * B * ((V + 127) // 128)
         assert lib.lmhead_workspace_bytes(0, B, H, V) == want
         assert lib.lmhead_workspace_bytes(1, B, H, V) == want
     assert lib.lmhead_workspace_bytes(0, 0, 2048, 32000) == 0

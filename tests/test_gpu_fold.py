@@ -1,8 +1,8 @@
 """The top-2 fold over many blocks (through the C-ABI): a vocabulary of 70,001
 columns has 547 blocks of 128, so each lane of the fold takes its records in
 several rounds.  Greedy and sampled draws against the CPU oracle, and the gated
-head against the GPU's own bf16 and float32 heads, at batches that use the
-fused fold (5) and the separate fold kernel (40, 100, 300)."""
+head against the GPU's own bf16 and float32 heads, at batches of four tile
+shapes (5, 40, 100, 300)."""
 import math
 
 import numpy as np

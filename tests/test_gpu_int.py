@@ -56,7 +56,8 @@ def _oracle_rows(o, i8, hid, rows, t):  # noqa: F811
 @pytest.mark.parametrize("B", [1, 5, 33])
 def test_logprob_int_bit_exact(i8, hid, o, B):  # noqa: F811
     """The 4096 x 128256 head on the GPU-quantised rows: log p in Q.24 equals
-    the oracle's bit for bit (fused fold at B <= 32, merge kernel above)."""
+    the oracle's bit for bit (32- and 64-row tiles; the fold reads each row's
+    1002 block records in four rounds)."""
     t = i8["target"][:B]
     got = host(lmhead.logprob_int(hid["q"][:B].contiguous(), i8["gw"], hid["unit"],
                                   hid["sm"][:B].contiguous(), hid["se"][:B].contiguous(),

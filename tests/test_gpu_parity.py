@@ -278,17 +278,22 @@ def test_invalid_target_and_scale_give_nan(o):
     assert np.isnan(lp[1:5]).all() and np.isfinite(lp[[0, 5]]).all()
 
 
-def test_workspace_reused_across_calls(tl):
-    """One workspace serves consecutive calls of different sizes (the library
-    leaves it zeroed); results equal those of a fresh workspace."""
-    ws = torch.zeros(lmhead.workspace_bytes(0, 512, 2048, 32000), dtype=torch.uint8, device=DEV)
+def test_workspace_contents_do_not_matter(tl):
+    """One workspace, filled with junk first, serves consecutive greedy and
+    log-prob calls of different sizes; results equal those of a fresh zeroed
+    workspace."""
+    n = lmhead.workspace_bytes(0, 512, 2048, 32000)
+    ws = torch.randint(0, 256, (n,), dtype=torch.uint8, generator=torch.Generator().manual_seed(5)).to(DEV)
+    t = torch.from_numpy(np.arange(512, dtype=np.int32) * 61 % 32000).to(DEV)
     runs = []
     for B in (512, 7, 512, 1, 300):
-        runs.append(lmhead.greedy_top2(tl["gx"][:B].contiguous(), tl["gw"], ws=ws))
-        assert int(ws[:256].count_nonzero()) == 0      # tickets back to zero
+        g = lmhead.greedy_top2(tl["gx"][:B].contiguous(), tl["gw"], ws=ws)
+        lp = lmhead.logprob(tl["gx"][:B].contiguous(), tl["gw"], t[:B].contiguous(), ws=ws)
+        runs.append((*g[:3], lp))
     fresh = lmhead.greedy_top2(tl["gx"], tl["gw"], ws=torch.zeros_like(ws))
+    fresh_lp = lmhead.logprob(tl["gx"], tl["gw"], t, ws=torch.zeros_like(ws))
     for B, r in zip((512, 7, 512, 1, 300), runs):
-        for a, b in zip(r[:3], fresh[:3]):
+        for a, b in zip(r, (*fresh[:3], fresh_lp)):
             assert torch.equal(a, b[:B])
 
 
