@@ -125,12 +125,15 @@ template <int P, class V> __device__ __forceinline__ V perm(V x) {
 // every row at a time, in two LDS rings: NSX stages of the X rows (read from
 // L2: every vocabulary tile re-reads them) and NSW > NSX stages of the W rows
 // (streamed from HBM once), so W loads are issued NSW - 1 stages ahead of use.
+// WSHARED: the plan's row tiles can share W tiles (batches above BM), the later
+// workgroups reading them from L2; otherwise each W byte is read by one
+// workgroup, and W is loaded with the non-temporal policy (WNT).
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BKB_, int NSX_, int NSW_,
-          bool WPAIR_ = false>
+          bool WPAIR_ = false, bool WSHARED_ = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int BKB = BKB_, NSX = NSX_, NSW = NSW_;
-  static constexpr bool WPAIR = WPAIR_;
+  static constexpr bool WPAIR = WPAIR_, WNT = !WSHARED_;
   static constexpr int NW = WAVES_M * WAVES_N, NT = NW * 64;
   static constexpr int WM = BM / WAVES_M / 32;  // 32-row MFMA tiles per wave
   static constexpr int WN = BN / WAVES_N / 32;  // 32-column MFMA tiles per wave
@@ -212,18 +215,31 @@ __device__ __forceinline__ void wait_lgkm0() {
 // so the compiler does not guard every later LDS read with a full vmcnt(0)
 // drain; completion is tracked by the pipeline's explicit vmcnt waits instead.
 // m0 (the copy's LDS base) is saved and restored around it; the s_nop is the
-// one wait state required between an SALU write of m0 and its use.
+// one wait state required between an SALU write of m0 and its use.  NT: the
+// non-temporal cache policy, for bytes that no other workgroup reads again.
+template <bool NT = false>
 __device__ __forceinline__ void dma16(unsigned voff, const void *sbase, unsigned lds) {
   unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(lds)
-      : "memory");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds)
+        : "memory");
 }
 
 __device__ __forceinline__ unsigned lds_addr(const void *p) {
@@ -958,8 +974,8 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
     for (int i = 0; i < T::SPWW_MAX; ++i) {
       const int span = wave + i * T::NW;
       if (T::WSPANS % T::NW == 0 || span < T::WSPANS)
-        dma16(woff[i], base,
-              __builtin_amdgcn_readfirstlane(lds0 + T::WRING + buf * T::WSTAGE + span * 1024));
+        dma16<T::WNT>(woff[i], base,
+                      __builtin_amdgcn_readfirstlane(lds0 + T::WRING + buf * T::WSTAGE + span * 1024));
     }
   };
   // W stages s and s + 1 (those below nst), span by span
@@ -971,8 +987,9 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
     for (int i = 0; i < T::SPWW_MAX; ++i) {
       const int span = wave + i * T::NW;
       if (T::WSPANS % T::NW == 0 || span < T::WSPANS) {
-        if (s < nst) dma16(woff[i], base0, __builtin_amdgcn_readfirstlane(buf0 + span * 1024));
-        if (s + 1 < nst) dma16(woff[i], base1, __builtin_amdgcn_readfirstlane(buf1 + span * 1024));
+        if (s < nst) dma16<T::WNT>(woff[i], base0, __builtin_amdgcn_readfirstlane(buf0 + span * 1024));
+        if (s + 1 < nst)
+          dma16<T::WNT>(woff[i], base1, __builtin_amdgcn_readfirstlane(buf1 + span * 1024));
       }
     }
   };
@@ -1068,8 +1085,8 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
       const int i = i0 + q;
       const int span = wave + i * T::NW;
       if (i < T::SPWW_MAX && (T::WSPANS % T::NW == 0 || span < T::WSPANS))
-        dma16(woff[i < T::SPWW_MAX ? i : 0], base,
-              __builtin_amdgcn_readfirstlane(lds0 + T::WRING + buf * T::WSTAGE + span * 1024));
+        dma16<T::WNT>(woff[i < T::SPWW_MAX ? i : 0], base,
+                      __builtin_amdgcn_readfirstlane(lds0 + T::WRING + buf * T::WSTAGE + span * 1024));
     }
   };
   // one stage; PEND: this stage carries the W loads of boundary t - 1
@@ -1608,7 +1625,7 @@ __global__ void reverse_rows_kernel(const char *src, char *dst, int64_t rows, in
 //   9: 128 x 256 in place of 2 when ceil(V / 256) >= 256; 10: 128 x 512 for
 //      the int8 head where 7 and 8 apply
 #ifndef LMH_V4_TILE
-#define LMH_V4_TILE 256, 256, 4, 2, 128, 2, 3
+#define LMH_V4_TILE 256, 256, 4, 2, 128, 2, 3, false, true
 #endif
 #ifndef LMH_V0W_TILE
 #define LMH_V0W_TILE 32, 256, 1, 4, BKB, 2, 3
@@ -1660,7 +1677,7 @@ template <int BKB> using V2x = Tile<128, 512, 4, 2, BKB, 2, 2>;
 template <int BKB> using V3 = Tile<LMH_V3_TILE>;
 using V4 = Tile<LMH_V4_TILE>;
 // V4 when the row is not a whole number of its stages
-using V4s = Tile<256, 256, 4, 2, 64, 2, 6>;
+using V4s = Tile<256, 256, 4, 2, 64, 2, 6, false, true>;
 
 template <class T, int MODE>
 hipError_t launch_tile(int epi, const Params &p, hipStream_t s) {
