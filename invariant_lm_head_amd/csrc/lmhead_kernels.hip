@@ -1676,6 +1676,9 @@ template <int BKB> using V2w = Tile<128, 256, 4, 2, BKB, 2, 3>;
 template <int BKB> using V2x = Tile<128, 512, 4, 2, BKB, 2, 2>;
 template <int BKB> using V3 = Tile<LMH_V3_TILE>;
 using V4 = Tile<LMH_V4_TILE>;
+// V4 with one row tile (batches 129-256 at large vocabularies): no W tile is
+// shared, so W takes the non-temporal policy
+using V4n = Tile<256, 256, 4, 2, 128, 2, 3>;
 // V4 when the row is not a whole number of its stages
 using V4s = Tile<256, 256, 4, 2, 64, 2, 6, false, true>;
 
@@ -1763,7 +1766,10 @@ hipError_t launch_mode(int epi, const Plan &plan, const Params &p, hipStream_t s
       }
       return hipErrorInvalidValue;  // int8 plan only
     default:
-      if (plan.bkb == V4::BKB) return launch_tile<V4, MODE>(epi, p, s);
+      if (plan.bkb == V4::BKB) {
+        if (p.grid_m == 1) return launch_tile<V4n, MODE>(epi, p, s);
+        return launch_tile<V4, MODE>(epi, p, s);
+      }
       return launch_tile<V4s, MODE>(epi, p, s);
   }
 }

@@ -1,8 +1,9 @@
 """The top-2 fold over many blocks (through the C-ABI): a vocabulary of 70,001
 columns has 547 blocks of 128, so each lane of the fold takes its records in
 several rounds.  Greedy and sampled draws against the CPU oracle, and the gated
-head against the GPU's own bf16 and float32 heads, at batches of four tile
-shapes (5, 40, 100, 300)."""
+head against the GPU's own bf16 and float32 heads, at batches of five plans
+(5, 40, 100, 200 and 300; 200 and 300 both take 256 x 256 tiles, with one row
+tile and with two)."""
 import math
 
 import numpy as np
@@ -27,14 +28,14 @@ def big():
     return {"x": x, "w": w, "gx": gpu_bf16(x), "gw": gpu_bf16(w)}
 
 
-@pytest.mark.parametrize("B", [5, 40, 100, 300])
+@pytest.mark.parametrize("B", [5, 40, 100, 200, 300])
 def test_greedy_many_blocks(big, o, B):
     ids, vals, margin, _ = lmhead.greedy_top2(big["gx"][:B].contiguous(), big["gw"])
     ex = check_greedy_bf16(ids, vals, margin, *o.greedy_bf16(big["x"][:B], big["w"]))
     print(f"B={B}: {ex} exempt rows", flush=True)
 
 
-@pytest.mark.parametrize("B", [5, 40, 100, 300])
+@pytest.mark.parametrize("B", [5, 40, 100, 200, 300])
 def test_sample_many_blocks(big, o, B):
     rng = np.random.default_rng(B)
     sd = rng.integers(0, 2 ** 63, B, dtype=np.uint64) * np.uint64(2) + np.uint64(1)
@@ -55,7 +56,7 @@ def _bits(a):
     return np.ascontiguousarray(a, dtype=np.float32).view(np.int32)
 
 
-@pytest.mark.parametrize("B", [5, 40, 100, 300])
+@pytest.mark.parametrize("B", [5, 40, 100, 200, 300])
 def test_gated_many_blocks(big, B):
     """Bit for bit against the GPU's own heads: a row is recomputed iff its
     bf16-head margin is below tau; an ungated row is the bf16 head's result; a
