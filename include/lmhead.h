@@ -40,9 +40,10 @@
  * Errors.  Arguments are validated on the host, synchronously, before any work
  * is queued; on a validation error nothing is queued and the status says why.
  * A failed launch returns LMHEAD_E_HIP (lmhead_last_error() has the HIP
- * message); where a call launches two kernels and the second launch fails,
- * the first may already be queued.  No exception or abort crosses this
- * interface.  Inputs are assumed finite.
+ * message).  The reducing calls (greedy, gated, sampling, log-prob) launch two
+ * kernels, the tiled contraction and then the per-row fold; if the second
+ * launch fails, the first may already be queued.  No exception or abort
+ * crosses this interface.  Inputs are assumed finite.
  */
 #ifndef LMHEAD_H_
 #define LMHEAD_H_
