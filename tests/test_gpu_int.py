@@ -112,11 +112,14 @@ def test_logprob_int_close_to_float(i8, hid, o):  # noqa: F811
         assert abs(got[r] - want) <= 1e-6, (r, got[r], want)
 
 
-@pytest.mark.parametrize("B,H,V", [(3, 64, 2), (40, 192, 1000), (300, 128, 333), (7, 64, 129)])
+@pytest.mark.parametrize("B,H,V", [(3, 64, 2), (40, 192, 1000), (300, 128, 333), (7, 64, 129),
+                                   (5, 64, 32768), (5, 64, 32769)])
 def test_logprob_int_edges(o, B, H, V):  # noqa: F811
     """Ragged V (blocks of 128 cut short), V = 2, a zero hidden row (every logit
     0: log p = -ln V), an invalid target and an invalid step: bit-exact
-    against the oracle, sentinels where the header says."""
+    against the oracle, sentinels where the header says.  V = 32768 and 32769
+    give 256 and 257 blocks: the fold's last single-round row and its first
+    row read in two rounds."""
     rng = np.random.default_rng(B * 1000 + V)
     x = rng.integers(-127, 128, (B, H)).astype(np.int8)
     x[0] = 0
