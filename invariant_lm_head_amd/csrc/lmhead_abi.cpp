@@ -35,10 +35,11 @@ lmhead_status check_common(int mode, int round, const void *x, const void *w, in
       H > kMaxHidden)
     return LMHEAD_E_SHAPE;
   if (mode == LMHEAD_MODE_INT8 && H > kInt8MaxHidden) return LMHEAD_E_OVERFLOW;
-  // the tile grid is one x dimension of at most 2^32 - 1 threads (up to 512 per
-  // workgroup), which bounds B x V jointly
+  // the tile grid is one x dimension of at most 2^32 - 1 threads (256 or 512
+  // per workgroup, by plan), which bounds B x V jointly
   const lmh::Plan pl = lmh::plan_for(mode, B, row_bytes(mode, H), V);
-  if ((uint64_t)pl.grid_m * (uint64_t)pl.grid_n * 512u > 0xFFFFFFFFull) return LMHEAD_E_SHAPE;
+  if ((uint64_t)pl.grid_m * (uint64_t)pl.grid_n * (uint64_t)pl.nt > 0xFFFFFFFFull)
+    return LMHEAD_E_SHAPE;
   if (!aligned16(x) || !aligned16(w)) return LMHEAD_E_ALIGN;
   return LMHEAD_OK;
 }

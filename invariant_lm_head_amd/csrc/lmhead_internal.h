@@ -52,6 +52,7 @@ struct Plan {
   int variant;  // tile shape index (see lmhead_kernels.hip)
   int bkb;      // bytes of every row staged per pipeline stage
   int bm, bn;   // rows and vocabulary columns per workgroup
+  int nt;       // threads per workgroup
   int grid_m, grid_n;
 };
 

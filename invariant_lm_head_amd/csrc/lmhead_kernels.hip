@@ -1616,9 +1616,10 @@ __global__ void reverse_rows_kernel(const char *src, char *dst, int64_t rows, in
 //   0: 32 x 128  (batch <= 32)   1: 64 x 128  (<= 64)
 //   2: 128 x 128 (<= 128)                    3: 256 x 128 (<= 256)
 //   4: 256 x 256 (> 256)
-//   5: 32 x 256, 6: 64 x 256 in place of 0 and 1 when the 128-column grid
-//      would take more than two rounds of the 256 CUs (large vocabularies):
-//      half the workgroups, so half the pipeline fills and tails per CU
+//   5: 32 x 256, 6: 64 x 256 in place of 0 and 1 for the int8 head when the
+//      128-column grid would take more than two rounds of the 256 CUs (large
+//      vocabularies): half the workgroups, so half the pipeline fills and
+//      tails per CU
 //   0 with 512-byte stages (V0d) for the float head when rows allow it
 //   7: 32 x 512, 8: 64 x 512 in place of 5 and 6 for the int8 head when the
 //      512-column grid fits one round of the CUs
@@ -1638,8 +1639,7 @@ template <int BKB> using V1w = Tile<LMH_V1W_TILE>;
 // int8 head, large vocabularies: 512-column tiles with rings of equal depth
 // (2 x 64 KB of W), so the grid takes one round of the CUs where 256-column
 // tiles would take two.  Measured on MI355X (4096 x 128256, W from HBM): batch
-// 1, 33 and 64 in 98 us against 108-111 us; the float head measured 1-3%
-// slower with them and keeps V0w / V1w.
+// 1, 33 and 64 in 98 us against 108-111 us.
 template <int BKB> using V0x = Tile<32, 512, 1, 4, BKB, 2, 2>;
 template <int BKB> using V1x = Tile<64, 512, 2, 2, BKB, 2, 2>;
 constexpr int kCUs = 256;  // MI355X compute units
@@ -1740,11 +1740,16 @@ hipError_t launch_mode(int epi, const Plan &plan, const Params &p, hipStream_t s
       if (plan.bkb == 128) return launch_tile<V3<128>, MODE>(epi, p, s);
       return launch_tile<V3<64>, MODE>(epi, p, s);
     case 5:
-      if (plan.bkb == 128) return launch_tile<V0w<128>, MODE>(epi, p, s);
-      return launch_tile<V0w<64>, MODE>(epi, p, s);
     case 6:
-      if (plan.bkb == 128) return launch_tile<V1w<128>, MODE>(epi, p, s);
-      return launch_tile<V1w<64>, MODE>(epi, p, s);
+      if constexpr (MODE == 1) {
+        if (plan.variant == 5) {
+          if (plan.bkb == 128) return launch_tile<V0w<128>, MODE>(epi, p, s);
+          return launch_tile<V0w<64>, MODE>(epi, p, s);
+        }
+        if (plan.bkb == 128) return launch_tile<V1w<128>, MODE>(epi, p, s);
+        return launch_tile<V1w<64>, MODE>(epi, p, s);
+      }
+      return hipErrorInvalidValue;  // int8 plans only
     case 7:
     case 8:
       if constexpr (MODE == 1) {
@@ -1780,37 +1785,41 @@ Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V) {
   Plan pl;
   const int bkb256 = rowbytes % 256 == 0 ? 256 : rowbytes % 128 == 0 ? 128 : 64;
   const int bkb128 = rowbytes % 128 == 0 ? 128 : 64;
-  const bool wide = (V + 127) / 128 > 2 * kCUs;  // the 128-column grid takes > 2 rounds
+  // int8 head: the 128-column grid takes > 2 rounds.  The float head keeps
+  // 128-column tiles at batches up to 64: with W streamed non-temporally they
+  // measured as fast at 4096 x 128256 and 16% faster at 4096 x 151936, whose
+  // 256-column grid fills only a third of its last round.
+  const bool wide = mode == 1 && (V + 127) / 128 > 2 * kCUs;
   const bool wide512 = mode == 1 && wide && (V + 511) / 512 <= kCUs;
   if (B <= 32 && wide512) {
-    pl.variant = 7; pl.bm = V0x<128>::BM; pl.bn = V0x<128>::BN; pl.bkb = bkb128;
+    pl.variant = 7; pl.bm = V0x<128>::BM; pl.bn = V0x<128>::BN; pl.nt = V0x<128>::NT; pl.bkb = bkb128;
   } else if (B <= 64 && wide512) {
-    pl.variant = 8; pl.bm = V1x<128>::BM; pl.bn = V1x<128>::BN; pl.bkb = bkb128;
+    pl.variant = 8; pl.bm = V1x<128>::BM; pl.bn = V1x<128>::BN; pl.nt = V1x<128>::NT; pl.bkb = bkb128;
   } else if (B <= 32 && wide) {
-    pl.variant = 5; pl.bm = V0w<128>::BM; pl.bn = V0w<128>::BN; pl.bkb = bkb128;
+    pl.variant = 5; pl.bm = V0w<128>::BM; pl.bn = V0w<128>::BN; pl.nt = V0w<128>::NT; pl.bkb = bkb128;
   } else if (B <= 32) {
-    pl.variant = 0; pl.bm = V0<256>::BM; pl.bn = V0<256>::BN; pl.bkb = bkb256;
+    pl.variant = 0; pl.bm = V0<256>::BM; pl.bn = V0<256>::BN; pl.nt = V0<256>::NT; pl.bkb = bkb256;
     if (mode == 0 && rowbytes % V0d::BKB == 0) pl.bkb = V0d::BKB;
   } else if (B <= 64 && wide) {
-    pl.variant = 6; pl.bm = V1w<128>::BM; pl.bn = V1w<128>::BN; pl.bkb = bkb128;
+    pl.variant = 6; pl.bm = V1w<128>::BM; pl.bn = V1w<128>::BN; pl.nt = V1w<128>::NT; pl.bkb = bkb128;
   } else if (B <= 64) {
-    pl.variant = 1; pl.bm = V1<256>::BM; pl.bn = V1<256>::BN; pl.bkb = bkb256;
+    pl.variant = 1; pl.bm = V1<256>::BM; pl.bn = V1<256>::BN; pl.nt = V1<256>::NT; pl.bkb = bkb256;
   } else if (B <= 128 && wide512) {
-    pl.variant = 10; pl.bm = V2x<128>::BM; pl.bn = V2x<128>::BN; pl.bkb = bkb128;
+    pl.variant = 10; pl.bm = V2x<128>::BM; pl.bn = V2x<128>::BN; pl.nt = V2x<128>::NT; pl.bkb = bkb128;
   } else if (B <= 128 && (V + 255) / 256 >= kCUs) {
-    pl.variant = 9; pl.bm = V2w<128>::BM; pl.bn = V2w<128>::BN; pl.bkb = bkb128;
+    pl.variant = 9; pl.bm = V2w<128>::BM; pl.bn = V2w<128>::BN; pl.nt = V2w<128>::NT; pl.bkb = bkb128;
   } else if (B <= 128) {
-    pl.variant = 2; pl.bm = 128; pl.bn = 128; pl.bkb = bkb128;
+    pl.variant = 2; pl.bm = V2<128>::BM; pl.bn = V2<128>::BN; pl.nt = V2<128>::NT; pl.bkb = bkb128;
   } else if (B <= 256 && (V + 255) / 256 < kCUs) {
     // 256-column tiles would leave CUs idle: 256 x 128.  Where they fill the
     // CUs (V >= 65281) the 256 x 256 tile below reads X half as often; measured
     // on MI355X at 4096 x 128256, batch 129-256: 10-15% faster (float head),
     // 11-14% (int8).  At batch 65-128 it was 13-30% slower (padded rows).
-    pl.variant = 3; pl.bm = V3<128>::BM; pl.bn = V3<128>::BN; pl.bkb = bkb128;
+    pl.variant = 3; pl.bm = V3<128>::BM; pl.bn = V3<128>::BN; pl.nt = V3<128>::NT; pl.bkb = bkb128;
   } else if (rowbytes % V4::BKB == 0) {
-    pl.variant = 4; pl.bm = V4::BM; pl.bn = V4::BN; pl.bkb = V4::BKB;
+    pl.variant = 4; pl.bm = V4::BM; pl.bn = V4::BN; pl.nt = V4::NT; pl.bkb = V4::BKB;
   } else {
-    pl.variant = 4; pl.bm = V4s::BM; pl.bn = V4s::BN; pl.bkb = V4s::BKB;
+    pl.variant = 4; pl.bm = V4s::BM; pl.bn = V4s::BN; pl.nt = V4s::NT; pl.bkb = V4s::BKB;
   }
   pl.grid_m = (int)((B + pl.bm - 1) / pl.bm);
   pl.grid_n = (int)((V + pl.bn - 1) / pl.bn);

@@ -191,11 +191,11 @@ def test_edge_shapes(o, mode, B, H, V):
 
 
 def test_wide_plans_batch_invariant():
-    """A vocabulary of more than 512 blocks (70,001 columns) runs 256-column
-    tiles at batches up to 64 and the usual tiles above: greedy, log-prob and
-    sampled draws of every row have the same bits at batch 1, 17, 40, 100, 200
-    and 300 (batches 100 and 200 take 256-column tiles too at this
-    vocabulary)."""
+    """At 70,001 columns (more than 256 blocks of 256) the float head runs
+    32- and 64-row tiles of 128 columns at batches up to 64, 128 x 256 tiles at
+    100 and 256 x 256 tiles at 200 (one row tile) and 300 (two): greedy,
+    log-prob and sampled draws of every row have the same bits at batch 1, 17,
+    40, 100, 200 and 300."""
     rng = np.random.default_rng(77)
     B, H, V = 300, 128, 70001
     x = gpu_bf16(synth.bf16_from_f32(rng.standard_normal((B, H)).astype(np.float32)))
