@@ -1785,12 +1785,20 @@ Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V) {
   Plan pl;
   const int bkb256 = rowbytes % 256 == 0 ? 256 : rowbytes % 128 == 0 ? 128 : 64;
   const int bkb128 = rowbytes % 128 == 0 ? 128 : 64;
-  // int8 head: the 128-column grid takes > 2 rounds.  The float head keeps
-  // 128-column tiles at batches up to 64: with W streamed non-temporally they
-  // measured as fast at 4096 x 128256 and 16% faster at 4096 x 151936, whose
-  // 256-column grid fills only a third of its last round.
-  const bool wide = mode == 1 && (V + 127) / 128 > 2 * kCUs;
-  const bool wide512 = mode == 1 && wide && (V + 511) / 512 <= kCUs;
+  // Wide tiles (int8 head only) where the 128-column grid takes more than two
+  // rounds of the CUs.  256-column tiles are taken only where their grid fills
+  // its rounds at least as well as the 128-column one: at 4096 x 151936 (2.32
+  // against 4.64 rounds) 128-column tiles measured 10% faster at batches up to
+  // 32.  The float head keeps 128-column tiles at batches up to 64: with W
+  // streamed non-temporally they measured as fast at 4096 x 128256 and 16%
+  // faster at 4096 x 151936.
+  auto fill = [](int64_t n) {  // busy share of the CU slots over a grid's rounds
+    return (double)n / (double)(((n + kCUs - 1) / kCUs) * kCUs);
+  };
+  const int64_t n128 = (V + 127) / 128, n256 = (V + 255) / 256;
+  const bool big = mode == 1 && n128 > 2 * kCUs;
+  const bool wide = big && fill(n256) >= fill(n128);
+  const bool wide512 = big && (V + 511) / 512 <= kCUs;
   if (B <= 32 && wide512) {
     pl.variant = 7; pl.bm = V0x<128>::BM; pl.bn = V0x<128>::BN; pl.nt = V0x<128>::NT; pl.bkb = bkb128;
   } else if (B <= 64 && wide512) {
