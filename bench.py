@@ -427,10 +427,19 @@ def extras(torch, lmhead, synth, bf16, x, w_copies, d):
     res["logprob_16384x151936x4096"] = {"ms_per_call": tt * 1e3, "rows_per_s": Bl / tt,
                                         "roofline": roofline(Bl, Hl, Vl, tt, out_bytes_per_row=8),
                                         "exp_per_s": Bl * Vl / tt}
-    del c, xl, wl_, tl
-    torch.cuda.empty_cache()
     log(f"log-prob 16384x151936x4096: {tt * 1e3:.2f} ms = "
         f"{100 * res['logprob_16384x151936x4096']['roofline']['frac']:.1f}% of MFMA peak")
+    # greedy on the same 1.24 GB head (five times the Infinity Cache, so W
+    # comes from HBM on every call) at batch 1 and 64
+    for B in (1, 64):
+        c = Caller(torch, lmhead, [xl[:B].contiguous()], [wl_], B, Hl, Vl)
+        tt = time_calls(torch, c, 30)
+        key = f"greedy_4096x151936_b{B}"
+        res[key] = {"us_per_call": tt * 1e6, "rows_per_s": B / tt, "roofline": roofline(B, Hl, Vl, tt)}
+        log(f"greedy 4096x151936 B={B}: {tt * 1e6:.1f} us, "
+            f"{res[key]['roofline']['bound']} {100 * res[key]['roofline']['frac']:.1f}%")
+    del c, xl, wl_, tl
+    torch.cuda.empty_cache()
 
     # int8 head, 4096 x 128256, batch 1 .. 512
     i8 = synth.make_inputs("int8")
