@@ -25,7 +25,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -164,10 +163,9 @@ def time_calls(torch, caller, n, warmup=3):
 
 
 def source_digest() -> str:
-    h = hashlib.sha256()
-    for p in sorted((ROOT / "invariant_lm_head_amd" / "csrc").glob("*")):
-        h.update(p.read_bytes())
-    return h.hexdigest()[:16]
+    """Digest of the library's sources (the one the library records at build)."""
+    from invariant_lm_head_amd import _build
+    return _build.source_digest()
 
 
 def traffic_from_profile(kernel_tag: str):

@@ -217,9 +217,9 @@ lmhead_status lmhead_logprob_int(const void *x, const void *w, int64_t B, int64_
  * load-time self-check proves on the device that every row gets the same bits
  * whatever the number of rows).  Computes the logits of x[0..B) as one batch,
  * of every row alone, and of the rows in reverse order, and adds the number of
- * logits whose bits differ to *mismatches (a device uint64 the caller zeroes).
- * scratch: device memory of lmhead_self_check_bytes() bytes, 16-byte aligned;
- * it is overwritten. */
+ * logits whose bits differ to *mismatches (a device uint64 the caller zeroes,
+ * 8-byte aligned; LMHEAD_E_ALIGN otherwise).  scratch: device memory of
+ * lmhead_self_check_bytes() bytes, 16-byte aligned; it is overwritten. */
 size_t lmhead_self_check_bytes(int mode, int64_t B, int64_t H, int64_t V);
 lmhead_status lmhead_self_check(int mode, const void *x, const void *w, int64_t B, int64_t H,
                                 int64_t V, void *scratch, size_t scratch_bytes,
@@ -228,6 +228,11 @@ lmhead_status lmhead_self_check(int mode, const void *x, const void *w, int64_t 
 /* Text of a status code, and of the last HIP error seen by this thread. */
 const char *lmhead_status_string(int status);
 const char *lmhead_last_error(void);
+
+/* The first 16 hex digits of the SHA-256 of the sources this library was built
+ * from (a static string), so a caller can refuse a library built from other
+ * sources. */
+const char *lmhead_source_digest(void);
 
 #ifdef __cplusplus
 }

@@ -13,6 +13,10 @@
 
 namespace {
 
+#ifndef LMH_SOURCE_DIGEST
+#error "the build passes the sources' digest as LMH_SOURCE_DIGEST"
+#endif
+
 thread_local char g_last_error[256] = "no HIP error";
 
 constexpr int64_t kMaxRows = (int64_t)1 << 24;   // B bound (int indexing of rows)
@@ -266,7 +270,7 @@ lmhead_status lmhead_self_check(int mode, const void *x, const void *w, int64_t 
   if (!scratch || !mismatches) return LMHEAD_E_NULL;
   size_t off[4];
   if (scratch_bytes < self_check_layout(mode, B, H, V, off)) return LMHEAD_E_WORKSPACE;
-  if (!aligned16(scratch) || !aligned4(mismatches)) return LMHEAD_E_ALIGN;
+  if (!aligned16(scratch) || ((uintptr_t)mismatches & 7u) != 0) return LMHEAD_E_ALIGN;
   char *sc = (char *)scratch;
   hipStream_t s = (hipStream_t)stream;
   const int64_t rb = row_bytes(mode, H);
@@ -310,5 +314,7 @@ const char *lmhead_status_string(int status) {
 }
 
 const char *lmhead_last_error(void) { return g_last_error; }
+
+const char *lmhead_source_digest(void) { return LMH_SOURCE_DIGEST; }
 
 }  // extern "C"

@@ -1,5 +1,5 @@
 // Internal interface between the C-ABI layer (lmhead_abi.cpp) and the gfx950
-// kernels (lmhead_kernels.hip).  Not installed; not part of the public ABI.
+// kernels (lmhead_kernels.hip, lmhead_tiles.hip).  Not installed; not part of the public ABI.
 #pragma once
 #include <hip/hip_runtime_api.h>
 #include <stddef.h>
@@ -62,6 +62,11 @@ Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V);
 size_t workspace_layout(int64_t B, int64_t V, size_t *off_zt, size_t *off_records);
 
 hipError_t launch(int mode, int epilogue, const Plan &plan, const Params &p, hipStream_t s);
+
+// The tile and fold kernels of one (mode, epilogue) pair for a plan (one
+// instance per object file of lmhead_tiles.hip).
+template <int MODE, int EPI>
+hipError_t launch_epi(const Plan &plan, const Params &p, hipStream_t s);
 
 
 // Per-token int8 quantisation of int32 rows (one workgroup per row).

@@ -38,6 +38,7 @@ SIGNATURES = {
     "lmhead_self_check": ([_I, _P, _P, _I64, _I64, _I64, _P, _SZ, _P, _P], _I),
     "lmhead_status_string": ([_I], ctypes.c_char_p),
     "lmhead_last_error": ([], ctypes.c_char_p),
+    "lmhead_source_digest": ([], ctypes.c_char_p),
 }
 
 
@@ -54,8 +55,16 @@ _lib = None
 _lock = threading.Lock()
 
 
+class StaleLibraryError(RuntimeError):
+    pass
+
+
 def library():
-    """Load liblmhead.so (building it first only if it does not exist)."""
+    """Load liblmhead.so, building it first only if it does not exist.
+
+    A library built from other sources than the ones beside it (its
+    lmhead_source_digest() differs from the sources' digest) is refused: run
+    the build again (``python -m invariant_lm_head_amd._build``)."""
     global _lib
     with _lock:
         if _lib is None:
@@ -65,6 +74,11 @@ def library():
             for name, (args, res) in SIGNATURES.items():
                 fn = getattr(lib, name)
                 fn.argtypes, fn.restype = args, res
+            built, now = lib.lmhead_source_digest().decode(), _build.source_digest()
+            if built != now:
+                raise StaleLibraryError(
+                    f"{_build.LIBRARY} was built from sources with digest {built}, but the "
+                    f"sources now hash to {now}: rebuild it (python -m invariant_lm_head_amd._build)")
             _lib = lib
     return _lib
 

@@ -31,10 +31,24 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(lmhead.SIGNATURES)
+
+
+def test_library_matches_its_sources(lib):
+    """The loaded library was built from the sources beside it (the binding
+    refuses a library whose recorded digest differs)."""
+    assert lib.lmhead_source_digest().decode() == _build.source_digest()
+
+
+def test_stale_library_is_refused(monkeypatch):
+    """A library whose recorded digest is not the sources' is not loaded."""
+    monkeypatch.setattr(lmhead, "_lib", None)
+    monkeypatch.setattr(_build, "source_digest", lambda: "0" * 16)
+    with pytest.raises(lmhead.StaleLibraryError):
+        lmhead.library()
 
 
 def test_library_is_gfx950_only():
@@ -230,6 +244,9 @@ def test_self_check_validation(lib):
     assert lib.lmhead_self_check(0, A, A, 4, 64, 1000, A2, need, None, S) == E_NULL
     assert lib.lmhead_self_check(0, A, A, 4, 64, 1000, A2, need - 1, A, S) == E_WORKSPACE
     assert lib.lmhead_self_check(0, A, A, 4, 64, 1000, MIS, need, A, S) == E_ALIGN
+    # the mismatch counter is a 64-bit device atomic: 4-byte alignment is refused
+    assert lib.lmhead_self_check(0, A, A, 4, 64, 1000, A2, need, ctypes.c_void_p(0x20004),
+                                 S) == E_ALIGN
 
 
 def test_binding_refuses_mixed_dtypes():

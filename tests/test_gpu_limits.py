@@ -59,22 +59,50 @@ def test_max_hidden_float_exact(o):
     assert np.max(np.abs(lp - o.logprob_bf16(xb, wb, t))) <= TOL
 
 
-def test_max_hidden_int8_exact(o):
-    """H = 131008 int8: all-127 and all--128 rows push the int32 sums to
-    within 0.05% of 2^31 (16384 H = 2,146,435,072); logits, ids and raw top
-    values bit-exact."""
-    B, H, V = 2, 131008, 129
+# H = 131008 int8 rows and vocabulary rows whose sums reach both ends of int32
+H_I8_MAX = 131008
+S_I8_MAX = np.float32(2.0 ** -26)   # scale that maps a 2^32 logit span to about 64 nats
+
+
+def _int8_extremes(V):
+    """Row 0 all -128 against vocabulary row 0 all -128 (z = 16384 H =
+    2,146,435,072) and row 1 all +127 (z = -16256 H = -2,129,666,048); the
+    other entries random.  Row 1 of x random."""
     rng = np.random.default_rng(14)
-    x = rng.integers(-128, 128, (B, H)).astype(np.int8)
+    x = rng.integers(-128, 128, (2, H_I8_MAX)).astype(np.int8)
     x[0] = -128
-    w = rng.integers(-128, 128, (V, H)).astype(np.int8)
-    w[5] = -128
-    w[77] = 127
+    w = rng.integers(-128, 128, (V, H_I8_MAX)).astype(np.int8)
+    w[0] = -128
+    w[1] = 127
+    return x, w
+
+
+@pytest.mark.parametrize("V", [2, 129])
+def test_max_hidden_int8_exact(o, V):
+    """H = 131008 int8: the logits of row 0 reach +2^31 - 2^20 and -2^31 + 2^24,
+    so their differences exceed the int32 range (V = 2: the margin is 32640 H =
+    4,276,101,120).  Logits, ids, raw and scaled top values and the margin
+    bit-exact; the float log-prob of every target within 1e-4 (scale 2^-26)."""
+    x, w = _int8_extremes(V)
+    B = x.shape[0]
     gx, gw = gpu(x), gpu(w)
     z = host(lmhead.logits(gx, gw)).astype(np.int64)
     zo = o.logits_i8(x, w)
-    assert zo[0, 5] == 16384 * H and np.array_equal(z, zo)
-    s = np.ones(B, dtype=np.float32)
-    ids, vals, margin, raw = lmhead.greedy_top2(gx, gw, row_scale=gpu(s))
-    o_ids, o_raw, o_vals, o_margin = o.greedy_i8(x, w, s)
-    assert np.array_equal(host(ids), o_ids) and np.array_equal(host(raw), o_raw)
+    assert zo[0, 0] == 16384 * H_I8_MAX and zo[0, 1] == -16256 * H_I8_MAX
+    assert np.array_equal(z, zo)
+    for s in (np.ones(B, dtype=np.float32), np.full(B, S_I8_MAX, dtype=np.float32)):
+        ids, vals, margin, raw = lmhead.greedy_top2(gx, gw, row_scale=gpu(s))
+        o_ids, o_raw, o_vals, o_margin = o.greedy_i8(x, w, s)
+        assert np.array_equal(host(ids), o_ids) and np.array_equal(host(raw), o_raw)
+        assert np.array_equal(host(vals).view(np.int32), o_vals.view(np.int32))
+        assert np.array_equal(host(margin).view(np.int32), o_margin.view(np.int32))
+        if V == 2:
+            assert o_raw[0, 0] - o_raw[0, 1] == 32640 * H_I8_MAX > 2 ** 32 - 2 ** 25
+            assert host(margin)[0] > 0
+    s = np.full(B, S_I8_MAX, dtype=np.float32)
+    for t in range(min(V, 4)):
+        tgt = np.full(B, t, dtype=np.int32)
+        lp = host(lmhead.logprob(gx, gw, gpu(tgt), row_scale=gpu(s)))
+        lo = o.logprob_i8(x, w, tgt, s)
+        assert np.all(np.isfinite(lp)), lp
+        assert np.max(np.abs(lp - lo)) <= TOL, (t, lp, lo)
