@@ -215,8 +215,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
     ap.add_argument("--counters", action="store_true",
-                    help="only launch what the HBM counter runs read: a 512 MiB device copy "
-                         "(calibration) and the greedy top-2 call at batch 1 and 512")
+                    help="only launch what the counter runs read: a 512 MiB device copy "
+                         "(calibration), greedy top-2 at batch 1, 256 and 512 and the int8 "
+                         "head at batch 512")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -320,16 +321,18 @@ def main():
 
 
 def counters_run(torch, lmhead, synth, dev):
-    """Launch sequence for the rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE):
-    3 copies of 512 MiB (read 512 MiB + write 512 MiB each: the calibration),
-    then 5 greedy top-2 calls at batch 512 and 5 at batch 1 (H=2048, V=32000,
-    four rotating W copies)."""
+    """Launch sequence for the rocprofv3 --pmc runs (one counter set per run):
+    3 copies of 512 MiB (read 512 MiB + write 512 MiB each: the calibration of
+    the HBM byte counters), then 5 greedy top-2 calls at each batch 1, 256 and
+    512 of the H=2048, V=32000 head (four rotating W copies), then 5 greedy
+    top-2 calls of the int8 head H=4096, V=128256 at batch 512."""
     src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     src.fill_(1)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
+    del src, dst
     d = synth.make_inputs("tinyllama")
 
     def bf16(a):
@@ -337,12 +340,22 @@ def counters_run(torch, lmhead, synth, dev):
 
     x = bf16(d["x"])
     w = [bf16(d["w"]) for _ in range(NCOPIES)]
-    for B in (512, 1):
+    for B in (1, 256, 512):
         c = Caller(torch, lmhead, [x[:B].contiguous()] * NCOPIES, w, B, 2048, 32000)
         for _ in range(5):
             c()
         torch.cuda.synchronize()
-    log("counter launches done")
+        log(f"counter launches: greedy 2048 x 32000 batch {B} done")
+    del x, w, c
+    i8 = synth.make_inputs("int8", rows=512)
+    xi = torch.from_numpy(i8["x"]).to(dev)
+    wi = torch.from_numpy(i8["w"]).to(dev)
+    si = torch.from_numpy(i8["scale"]).to(dev)
+    c = Caller(torch, lmhead, [xi], [wi], 512, i8["H"], i8["V"], mode=1, scale=si)
+    for _ in range(5):
+        c()
+    torch.cuda.synchronize()
+    log("counter launches: int8 greedy 4096 x 128256 batch 512 done")
 
 
 def extras(torch, lmhead, synth, bf16, x, w_copies, d):

@@ -66,6 +66,8 @@ lmh::Params base_params(int mode, const void *x, const void *w, int64_t B, int64
   p.nblocks = (int)((V + lmh::kBlockCols - 1) / lmh::kBlockCols);
   p.grid_m = plan.grid_m;
   p.grid_n = plan.grid_n;
+  p.div_group = lmh::div_magic((uint64_t)lmh::kTileGroup * (uint64_t)plan.grid_n);
+  p.div_units = lmh::div_magic(p.rowbytes >= 256 ? (uint64_t)(p.rowbytes >> 8) : 1);
   return p;
 }
 

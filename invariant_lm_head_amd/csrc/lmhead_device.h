@@ -257,6 +257,18 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// floor(n / d) for 0 <= n < 2^31, 1 <= d <= 2^31, from m = ceil(2^63 / d) (see
+// div_magic): q = floor(2n m / 2^64) = floor(n / d + n e / 2^63) with
+// 0 <= e < 1, and n e / 2^63 < 2^-32 < 1/d - frac(n/d) unless frac(n/d) = 0,
+// so q is the exact quotient.  Integer instructions only (a runtime division
+// would be lowered through a float32 reciprocal estimate).
+__device__ __forceinline__ uint32_t div_exact(uint32_t n, uint64_t m) {
+  return (uint32_t)__umul64hi((uint64_t)n << 1, m);
+}
+// m of div_exact for the divisors 1..8 (compile-time)
+constexpr uint64_t kDivSmall[9] = {0, div_magic(1), div_magic(2), div_magic(3), div_magic(4),
+                                   div_magic(5), div_magic(6), div_magic(7), div_magic(8)};
+
 // Start of the int8 head's k order for vocabulary column `col`: the row is
 // streamed in 256-byte units in ascending order from unit ((col >> 10) mod
 // units), wrapping round.  Workgroups of different column groups then read
@@ -269,9 +281,10 @@ __device__ __forceinline__ void lds_barrier() {
 // and their exact tie would no longer go to the lower id.  Rows that are not a
 // whole number of 256-byte units start at byte 0.
 constexpr int kRotShift = 10;  // columns per rotation group: 2^kRotShift
-__device__ __forceinline__ int64_t k_rotation(int64_t rowbytes, int col) {
-  if (rowbytes % 256 != 0) return 0;
-  return (int64_t)(((unsigned)col >> kRotShift) % (unsigned)(rowbytes >> 8)) << 8;
+__device__ __forceinline__ int64_t k_rotation(const Params &p, int col) {
+  if (p.rowbytes % 256 != 0) return 0;
+  const uint32_t g = (uint32_t)col >> kRotShift, units = (uint32_t)(p.rowbytes >> 8);
+  return (int64_t)(g - units * div_exact(g, p.div_units)) << 8;
 }
 
 // Scheduling hint for one k-step: NR fragment reads (of the next step) spread
@@ -489,6 +502,21 @@ __device__ __forceinline__ uint32_t iexp_q30(uint64_t T) {
   return zero ? 0u : e;
 }
 
+// floor(n / d) by restoring binary division, for a quotient below 2^31 (n <
+// 2^31 d, d < 2^62): integer instructions only, one step per quotient bit
+__device__ __forceinline__ uint64_t udiv_small_quotient(uint64_t n, uint64_t d) {
+  uint64_t q = 0;
+#pragma unroll 1
+  for (int b = 30; b >= 0; --b) {
+    const uint64_t t = d << b;
+    if (n >= t) {
+      n -= t;
+      q |= (uint64_t)1 << b;
+    }
+  }
+  return q;
+}
+
 // ln(S / 2^30) in Q.30 for S >= 2^30
 __device__ int64_t iln_q30(uint64_t S) {
   int l = 63 - __clzll((long long)S);
@@ -499,7 +527,8 @@ __device__ int64_t iln_q30(uint64_t S) {
   }
   const uint64_t f = mant - (1ull << kExpFrac);
   const uint64_t den = (2ull << kExpFrac) + f;
-  const uint64_t u = (2 * (f << kExpFrac) + den) / (2 * den);
+  // round(f 2^30 / den): the quotient is below 2^29 (f < 2^30 < den)
+  const uint64_t u = udiv_small_quotient(2 * (f << kExpFrac) + den, 2 * den);
   const uint64_t u2 = rnd64(u * u, kExpFrac);
   uint64_t t = u, acc = u;
   for (int j = 1; j <= kAtanhTerms; ++j) {
@@ -921,14 +950,17 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   {
     const int G = gridDim.x, bid = blockIdx.x, per = G >> 3;
     const int nb = bid < (per << 3) ? (bid & 7) * per + (bid >> 3) : bid;
-    constexpr int GROUP_M = 8;
+    constexpr int GROUP_M = kTileGroup;
     const int in_group = GROUP_M * p.grid_n;
-    const int group = nb / in_group;
+    const int group = (int)div_exact((uint32_t)nb, p.div_group);  // nb / in_group
     const int first_m = group * GROUP_M;
     const int gsz = min(p.grid_m - first_m, GROUP_M);
     const int rem = nb - group * in_group;
-    tm = first_m + rem % gsz;
-    tn = rem / gsz;
+    uint64_t mg = kDivSmall[1];
+#pragma unroll
+    for (int d = 2; d <= GROUP_M; ++d) mg = gsz == d ? kDivSmall[d] : mg;
+    tn = (int)div_exact((uint32_t)rem, mg);  // rem / gsz
+    tm = first_m + (rem - tn * gsz);
   }
   const int m0 = tm * T::BM, n0 = tn * T::BN;
 
@@ -942,7 +974,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   // rotation is a whole number of stages)
   static_assert(MODE != 1 || ((1LL << kRotShift) % T::BN == 0 && 256 % T::BKB == 0),
                 "tile within one rotation group");
-  const int64_t rot = MODE == 1 ? k_rotation(p.rowbytes, n0) : 0;
+  const int64_t rot = MODE == 1 ? k_rotation(p, n0) : 0;
   const int nst = (int)(p.rowbytes / T::BKB);  // stages per row
   auto koff = [&](int stage) -> int64_t {
     const int64_t o = (int64_t)stage * T::BKB + rot;

@@ -13,12 +13,22 @@ enum Epilogue { kStore = 0, kTop2 = 1, kLse = 2, kSample = 3, kLseInt = 4 };
 // vocabulary columns; the block grid depends on V only.
 constexpr int kBlockCols = 128;
 
+// m = ceil(2^63 / d) for an exact division of n < 2^31 by 1 <= d <= 2^31 with
+// a multiply-high (div_exact in lmhead_device.h)
+constexpr uint64_t div_magic(uint64_t d) { return ((uint64_t)1 << 63) / d + (((uint64_t)1 << 63) % d != 0); }
+
+// Workgroups per group of the tile raster: kTileGroup row tiles are walked per
+// vocabulary tile.
+constexpr int kTileGroup = 8;
+
 struct Params {
   const char *x;      // [B, H] row-major (bf16 bits or int8)
   const char *w;      // [V, H] row-major
   int64_t rowbytes;   // H * element size
   int B, V, nblocks;  // nblocks = ceil(V / kBlockCols)
   int grid_m, grid_n; // workgroup tiles over rows and vocabulary columns
+  uint64_t div_group; // div_magic(kTileGroup * grid_n)
+  uint64_t div_units; // div_magic(rowbytes / 256) (int8 k rotation; 1 if rowbytes < 256)
   int round_bf16;     // 1: round logits to bf16 before storing / ranking
   void *logits;       // kStore output [B, V]
   const float *scale;     // int8 per-row scale (may be null)

@@ -39,8 +39,9 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const int32_t *x, in
     if (E <= 0) {
       mm = (((uint64_t)a << (-E)) + 126u) / 127u;  // ceil(a 2^-E / 127)
     } else {
-      const uint64_t d = (uint64_t)127 << E;
-      mm = ((uint64_t)a + d - 1) / d;
+      // ceil(a / (127 2^E)) = ceil(ceil(a / 2^E) / 127): a shift and a
+      // division by a constant (no runtime divisor)
+      mm = ((((uint64_t)a + ((uint64_t)1 << E) - 1) >> E) + 126u) / 127u;
     }
     if (mm == (1u << 15)) {
       mm = 1u << 14;

@@ -3,10 +3,18 @@
 Argument marshalling only: every step of the head runs in the HIP kernels.
 PyTorch provides device memory and the current stream.  There is no CPU or
 PyTorch fallback: if the library cannot be loaded, every call raises.
+
+Before the first call on a device the binding runs the library's device
+self-check (lmhead_self_check) in both arithmetic modes on a fixed synthetic
+batch: every row's logits alone, in the batch and in the reversed batch must
+have the same bits, or every call on that device raises SelfCheckError
+("12 Exactness", section 12.8: a load-time self-check of the row property on
+the device).  Set LMHEAD_SELF_CHECK=0 to skip it.
 """
 from __future__ import annotations
 
 import ctypes
+import os
 import threading
 
 import torch
@@ -83,6 +91,49 @@ def library():
     return _lib
 
 
+class SelfCheckError(RuntimeError):
+    pass
+
+
+_self_checked: dict = {}
+SELF_CHECK_SHAPES = ((MODE_BF16, 300, 128, 2000), (MODE_INT8, 300, 128, 2000))
+
+
+def self_check_enabled() -> bool:
+    """LMHEAD_SELF_CHECK=0 (or false/no/off) skips the load-time self-check."""
+    return os.environ.get("LMHEAD_SELF_CHECK", "1").strip().lower() not in ("0", "false", "no", "off")
+
+
+def ensure_self_check(device) -> dict:
+    """Run the device self-check once per device (both modes, 300 rows: the
+    batch spans two 256-row tiles, each row alone runs the 32-row tile) and
+    raise SelfCheckError if any logit's bits differ.  Returns {mode:
+    mismatches} (empty when the check is switched off)."""
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    if key in _self_checked:
+        res = _self_checked[key]
+    elif not self_check_enabled():
+        res = _self_checked[key] = {}
+    else:
+        res = {}
+        g = torch.Generator().manual_seed(12)
+        for mode, B, H, V in SELF_CHECK_SHAPES:
+            if mode == MODE_BF16:
+                x = torch.randn((B, H), generator=g).to(torch.bfloat16)
+                w = (0.05 * torch.randn((V, H), generator=g)).to(torch.bfloat16)
+            else:
+                x = torch.randint(-127, 128, (B, H), generator=g, dtype=torch.int8)
+                w = torch.randint(-127, 128, (V, H), generator=g, dtype=torch.int8)
+            with torch.cuda.device(dev):
+                res[mode] = self_check(x.to(dev), w.to(dev))
+        _self_checked[key] = res
+    if any(res.values()):
+        raise SelfCheckError(f"device self-check on {dev}: logits whose bits depend on the "
+                             f"batch (mismatches per mode {res}); refusing to run")
+    return res
+
+
 def _check(fn: str, status: int):
     if status != 0:
         raise LMHeadError(fn, status, library())
@@ -96,13 +147,15 @@ def _mode_of(x: torch.Tensor, w: torch.Tensor) -> int:
     raise TypeError(f"x and w must both be bfloat16 or both int8, got {x.dtype}, {w.dtype}")
 
 
-def _dims(x: torch.Tensor, w: torch.Tensor):
+def _dims(x: torch.Tensor, w: torch.Tensor, checked: bool = True):
     if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
         raise ValueError(f"x must be [B, H] and w [V, H], got {tuple(x.shape)}, {tuple(w.shape)}")
     if not (x.is_cuda and w.is_cuda and x.is_contiguous() and w.is_contiguous()):
         raise ValueError("x and w must be contiguous device tensors")
     if x.device != w.device:
         raise ValueError(f"x and w must be on one device, got {x.device}, {w.device}")
+    if checked:
+        ensure_self_check(x.device)
     return x.shape[0], x.shape[1], w.shape[0]
 
 
@@ -223,6 +276,7 @@ def quantize_rows(x: torch.Tensor):
     x = x.contiguous()
     B, H = x.shape
     dev = x.device
+    ensure_self_check(dev)
     q = torch.empty((B, H), dtype=torch.int8, device=dev)
     step_m = torch.empty((B,), dtype=torch.int32, device=dev)
     step_e = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -309,7 +363,7 @@ def self_check(x: torch.Tensor, w: torch.Tensor) -> int:
     """Number of logits whose bits differ between batch, single-row and reversed
     runs of x (0 proves the row property on this device for these rows)."""
     mode = _mode_of(x, w)
-    B, H, V = _dims(x, w)
+    B, H, V = _dims(x, w, checked=False)
     dev = x.device
     nbytes = int(library().lmhead_self_check_bytes(mode, B, H, V))
     scratch = torch.empty(nbytes, dtype=torch.uint8, device=dev)

@@ -269,3 +269,14 @@ def test_binding_checks_caller_arrays():
     with pytest.raises(ValueError):
         lmhead._ws(torch.zeros(2, 64, dtype=torch.uint8)[:, ::2], cpu)
     assert lmhead._ws(None, cpu) is None
+
+
+def test_self_check_switch(monkeypatch):
+    """LMHEAD_SELF_CHECK=0 (false/no/off) turns the binding's load-time device
+    self-check off; anything else, or unset, leaves it on."""
+    for v, on in (("0", False), ("false", False), ("Off", False), ("no", False), ("1", True),
+                  ("yes", True)):
+        monkeypatch.setenv("LMHEAD_SELF_CHECK", v)
+        assert lmhead.self_check_enabled() is on
+    monkeypatch.delenv("LMHEAD_SELF_CHECK")
+    assert lmhead.self_check_enabled()

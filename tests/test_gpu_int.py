@@ -11,7 +11,7 @@ import torch
 
 import synth
 from invariant_lm_head_amd import lmhead
-from tests.gpu_util import DEV, gpu, host, i8, o  # noqa: F401
+from tests.gpu_util import DEV, gpu, host, i8, o, record, row_digests  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
@@ -26,11 +26,28 @@ def hid(i8):  # noqa: F811
     return {"h": h, "q": q, "sm": sm, "se": se, "unit": i8["unit"]}
 
 
-def test_quantize_bit_exact(hid, o):  # noqa: F811
-    """512 hidden rows of 4096: q, M and E equal the oracle's bit for bit."""
+def test_quantize_bit_exact(hid, o, i8):  # noqa: F811
+    """512 hidden rows of 4096: q, M and E equal the oracle's bit for bit
+    (live oracle, and the stored per-row digests of q)."""
     q, M, E = o.quantize_rows(hid["h"])
     assert np.array_equal(host(hid["q"]), q)
     assert np.array_equal(host(hid["sm"]), M) and np.array_equal(host(hid["se"]), E)
+    g = i8["golden"]
+    assert row_digests(host(hid["q"]).astype(np.int32)) == list(g["q_digests"])
+    assert np.array_equal(host(hid["sm"]), g["step_m"]) and np.array_equal(host(hid["se"]), g["step_e"])
+
+
+@pytest.mark.parametrize("B", [1, 8, 64, 256, 512])
+def test_logprob_int_all_rows(i8, hid, B):  # noqa: F811
+    """Every row of every swept batch: log p in Q.24 equals the oracle's
+    (stored) bit for bit."""
+    t = i8["target"][:B]
+    got = host(lmhead.logprob_int(hid["q"][:B].contiguous(), i8["gw"], hid["unit"],
+                                  hid["sm"][:B].contiguous(), hid["se"][:B].contiguous(),
+                                  gpu(t)))
+    want = i8["golden"]["logprob_q"][:B]
+    assert np.array_equal(got, want), np.nonzero(got != want)[0][:10]
+    record("parity_int8", f"integer_logprob_batch_{B}", {"rows": B, "bit_exact": True})
 
 
 @pytest.mark.parametrize("H", [1, 63, 100, 257, 4096])

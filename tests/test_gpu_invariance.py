@@ -10,22 +10,26 @@ import pytest
 import torch
 
 from invariant_lm_head_amd import lmhead
-from tests.gpu_util import bits, gpu, host, i8, o, tl  # noqa: F401
+from tests.gpu_util import bits, gpu, host, i8, o, record, tl  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
-# every tile variant and its boundaries: 1..16 | 17..64 | 65..256 | 257..512
-SIZES = [1, 2, 3, 7, 15, 16, 17, 31, 33, 63, 64, 65, 100, 128, 129, 255, 256, 257, 300, 511]
+# every batch size of the sweep range: all tile variants and their boundaries
+SIZES = list(range(1, 512))
 
 
 def test_logits_bits_equal_for_every_batch_size(tl):
+    """Batches 1..511 against batch 512: every logit of every row, bit for bit."""
     full = lmhead.logits(tl["gx"], tl["gw"])
     for B in SIZES:
         z = lmhead.logits(tl["gx"][:B].contiguous(), tl["gw"])
         assert torch.equal(bits(z), bits(full[:B])), B
+    record("invariance", "logits_batches_1_to_512", {"batches": len(SIZES) + 1,
+                                                     "rows_compared": sum(SIZES)})
 
 
 def test_greedy_and_logprob_bits_equal_for_every_batch_size(tl):
+    """Batches 1..511 against batch 512: top-2 ids, values, margin and log-prob."""
     t = gpu(tl["target"])
     g512 = lmhead.greedy_top2(tl["gx"], tl["gw"])
     l512 = lmhead.logprob(tl["gx"], tl["gw"], t)
@@ -36,6 +40,7 @@ def test_greedy_and_logprob_bits_equal_for_every_batch_size(tl):
             assert torch.equal(bits(a), bits(b[:B])), B
         lp = lmhead.logprob(x, tl["gw"], t[:B].contiguous())
         assert torch.equal(bits(lp), bits(l512[:B])), B
+    record("invariance", "greedy_logprob_batches_1_to_512", {"batches": len(SIZES) + 1})
 
 
 def test_row_position_and_neighbours_do_not_matter(tl):

@@ -49,7 +49,7 @@ def test_sample_vs_oracle(tl, o, T):
 
 
 def test_sample_int8(i8, o):
-    rows = i8["rows"]
+    rows = np.array([0, 1, 2, 7, 8, 15, 16, 63, 64, 100, 255, 256, 300, 511])
     B = len(rows)
     sd, ps = keys(B, seed=52)
     scale = i8["scale"][rows].copy()

@@ -1,0 +1,58 @@
+"""The kernels' integer-only divisions, emulated exactly on the CPU.
+
+div_exact (tile raster and the int8 k rotation): floor(n / d) as the high 64
+bits of 2n * ceil(2^63 / d), claimed exact for 0 <= n < 2^31, 1 <= d <= 2^31.
+udiv_small_quotient (the integer ln): restoring division for quotients below
+2^31.  Both replace runtime divisions that the compiler would lower through a
+float32 reciprocal estimate."""
+import numpy as np
+
+
+def div_magic(d):
+    return (1 << 63) // d + ((1 << 63) % d != 0)
+
+
+def div_exact(n, m):
+    return ((2 * n) * m) >> 64
+
+
+def udiv_small_quotient(n, d):
+    q = 0
+    for b in range(30, -1, -1):
+        t = d << b
+        if n >= t:
+            n -= t
+            q |= 1 << b
+    return q
+
+
+def test_div_exact_matches_floor_division():
+    rng = np.random.default_rng(0)
+    ds = [1, 2, 3, 5, 7, 8, 127, 255, 1000, 65535, 2 ** 20 + 1, 2 ** 30 - 1, 2 ** 30,
+          2 ** 31 - 1, 2 ** 31] + [int(v) for v in rng.integers(1, 2 ** 31, 200)]
+    for d in ds:
+        m = div_magic(d)
+        ns = {0, 1, d - 1, d, d + 1, 2 ** 31 - 1, (2 ** 31 - 1) // d * d,
+              (2 ** 31 - 1) // d * d - 1} | {int(v) for v in rng.integers(0, 2 ** 31, 300)}
+        for k in range(1, 6):
+            ns |= {k * d - 1, k * d}
+        for n in ns:
+            if 0 <= n < 2 ** 31:
+                assert div_exact(n, m) == n // d, (n, d)
+
+
+def test_div_exact_small_divisors_exhaustive():
+    """The raster divides by 1..8 and by 8 * grid_n: every n below 2^20."""
+    n = np.arange(1 << 20, dtype=object)
+    for d in range(1, 9):
+        m = div_magic(d)
+        assert all(div_exact(int(v), m) == int(v) // d for v in n[::97])
+
+
+def test_udiv_small_quotient():
+    rng = np.random.default_rng(1)
+    for _ in range(2000):
+        f = int(rng.integers(0, 2 ** 30))
+        den = (2 << 30) + f
+        n, d = 2 * (f << 30) + den, 2 * den
+        assert udiv_small_quotient(n, d) == n // d
