@@ -116,6 +116,22 @@ lmhead_status lmhead_greedy_top2(int mode, int round, const void *x, const void 
                                  float *top_val, float *margin, int32_t *top_raw, void *ws,
                                  size_t ws_bytes, void *stream);
 
+/* lmhead_greedy_top2 for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, outputs and kernels, with the workspace taken from a
+ * static device array of LMHEAD_STATIC_WORKSPACE_BYTES in the library (one per
+ * GPU, resolved on the first call on that device and held until the process
+ * ends).  Shapes whose workspace exceeds it (lmhead_workspace_bytes() >
+ * LMHEAD_STATIC_WORKSPACE_BYTES, e.g. B * ceil(V / 128) above about a million
+ * records) give LMHEAD_E_WORKSPACE.  Nothing is allocated.  Every call on one
+ * GPU shares that array: calls that can overlap on one GPU (concurrent
+ * streams, several host threads) race and must not be issued. */
+#define LMHEAD_STATIC_WORKSPACE_BYTES ((size_t)16 << 20)
+lmhead_status lmhead_greedy_top2_noalloc(int mode, int round, const void *x, const void *w,
+                                         int64_t B, int64_t H, int64_t V, const float *row_scale,
+                                         int32_t *top_id, float *top_val, float *margin,
+                                         int32_t *top_raw, void *stream);
+
 /* log p(target[b]) under the softmax (temperature 1) of row b's logits, float32,
  * logits never written to memory ("batch-logprob-gap": the log probability a
  * model gives a token; "Inference and Decoding", section 3, temperature

@@ -154,6 +154,21 @@ lmhead_status lmhead_greedy_top2(int mode, int round, const void *x, const void 
                 nullptr, ws, ws_bytes, stream);
 }
 
+lmhead_status lmhead_greedy_top2_noalloc(int mode, int round, const void *x, const void *w,
+                                         int64_t B, int64_t H, int64_t V, const float *row_scale,
+                                         int32_t *top_id, float *top_val, float *margin,
+                                         int32_t *top_raw, void *stream) {
+  static_assert(LMHEAD_STATIC_WORKSPACE_BYTES == lmh::kStaticWorkspaceBytes, "static workspace");
+  lmhead_status st = check_common(mode, round, x, w, B, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (lmh::workspace_layout(B, V, nullptr, nullptr) > lmh::kStaticWorkspaceBytes)
+    return LMHEAD_E_WORKSPACE;
+  void *ws = nullptr;
+  if ((st = launched(lmh::static_workspace(&ws))) != LMHEAD_OK) return st;
+  return greedy(mode, round, x, w, B, H, V, row_scale, top_id, top_val, margin, top_raw, 0.0f,
+                nullptr, ws, lmh::kStaticWorkspaceBytes, stream);
+}
+
 lmhead_status lmhead_logprob(int mode, const void *x, const void *w, int64_t B, int64_t H,
                              int64_t V, const float *row_scale, const int32_t *target,
                              float *logprob, void *ws, size_t ws_bytes, void *stream) {

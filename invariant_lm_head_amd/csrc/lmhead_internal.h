@@ -68,6 +68,12 @@ struct Plan {
 
 Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V);
 
+// Size of the static device workspace of lmhead_greedy_top2_noalloc.
+constexpr size_t kStaticWorkspaceBytes = (size_t)16 << 20;
+
+// The current device's copy of that workspace (resolved once per device).
+hipError_t static_workspace(void **ptr);
+
 // Byte offsets of the workspace regions; returns the total size.
 size_t workspace_layout(int64_t B, int64_t V, size_t *off_zt, size_t *off_records);
 

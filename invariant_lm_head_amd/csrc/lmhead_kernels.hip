@@ -4,8 +4,15 @@
 // each tile plan are in lmhead_device.h.
 #include "lmhead_device.h"
 
+#include <mutex>
+
 namespace lmh {
 namespace {
+
+// The workspace of the no-allocation entry point: one array per GPU, held
+// until the process ends.  Host code never uses its name as an address (that
+// is a host-side stand-in); static_workspace() resolves each device's copy.
+static __device__ __align__(256) char scratch[kStaticWorkspaceBytes];
 
 // ------------------------------------------------ per-token quantisation
 // One workgroup per row of int32 values x ("Integer-Only Arithmetic", section
@@ -163,6 +170,26 @@ hipError_t launch(int mode, int epi, const Plan &plan, const Params &p, hipStrea
     case kLseInt: return launch_epi<1, kLseInt>(plan, p, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t static_workspace(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex lock;
+  static void *addr[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> guard(lock);
+  if (!addr[dev]) {
+    // once per device, with that device current: its copy of the array
+    void *a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_quantize(const int32_t *x, int64_t B, int64_t H, int8_t *q, int32_t *step_m,

@@ -34,6 +34,8 @@ SIGNATURES = {
     "lmhead_workspace_bytes": ([_I, _I64, _I64, _I64], _SZ),
     "lmhead_logits": ([_I, _I, _P, _P, _I64, _I64, _I64, _P, _P], _I),
     "lmhead_greedy_top2": ([_I, _I, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "lmhead_greedy_top2_noalloc": ([_I, _I, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P],
+                                   _I),
     "lmhead_logprob": ([_I, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _I),
     "lmhead_greedy_gated": ([_I, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, _P, _P,
                              _SZ, _P], _I),
@@ -241,6 +243,32 @@ def greedy_top2(x: torch.Tensor, w: torch.Tensor, row_scale: torch.Tensor | None
                                       _ptr(vals), _ptr(margin), _ptr(raw), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(dev))
     _check("lmhead_greedy_top2", st)
+    return ids, vals, margin, raw
+
+
+STATIC_WORKSPACE_BYTES = 16 << 20   # LMHEAD_STATIC_WORKSPACE_BYTES
+
+
+def greedy_top2_noalloc(x: torch.Tensor, w: torch.Tensor, row_scale: torch.Tensor | None = None,
+                        round_bf16: bool = False, out=None):
+    """greedy_top2 through the entry point that allocates nothing: the library
+    takes its workspace from a static device array (shapes whose workspace
+    exceeds STATIC_WORKSPACE_BYTES are refused).  out: optional preallocated
+    (ids, vals, margin, raw) to write into (raw None in bf16 mode)."""
+    mode = _mode_of(x, w)
+    B, H, V = _dims(x, w)
+    dev = x.device
+    if out is None:
+        out = (torch.empty((B, 2), dtype=torch.int32, device=dev),
+               torch.empty((B, 2), dtype=torch.float32, device=dev),
+               torch.empty((B,), dtype=torch.float32, device=dev),
+               torch.empty((B, 2), dtype=torch.int32, device=dev) if mode == MODE_INT8 else None)
+    ids, vals, margin, raw = out
+    rs = _vec(row_scale, "row_scale", B, torch.float32, dev)
+    st = library().lmhead_greedy_top2_noalloc(mode, ROUND_BF16 if round_bf16 else ROUND_F32,
+                                              _ptr(x), _ptr(w), B, H, V, _ptr(rs), _ptr(ids),
+                                              _ptr(vals), _ptr(margin), _ptr(raw), _stream(dev))
+    _check("lmhead_greedy_top2_noalloc", st)
     return ids, vals, margin, raw
 
 
