@@ -25,6 +25,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -183,28 +184,107 @@ def traffic_from_profile(kernel_tag: str):
     return val if src == source_digest() else None
 
 
+def host_facts() -> dict:
+    """The host the CPU leg runs on: online CPUs and the CPU model."""
+    model = None
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"online_cpus": os.cpu_count(), "cpu_model": model,
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
 def cpu_baseline():
-    """The float64 oracle's greedy top-2 on the host's cores: chunks of 256
-    rows of the tinyllama workload until about 8 s have passed (at most 2048
-    rows), then 64 rows on one thread."""
+    """The float64 / int64 oracle on the host's cores (threads: OMP_NUM_THREADS
+    if set, else the online CPUs, at most 16).  The metric's workload: greedy
+    top-2 of the H=2048, V=32000 head, chunks of 256 rows until about 8 s have
+    passed (at most 2048 rows), then 64 rows on one thread.  The other
+    workloads on bounded samples (a few seconds each): the tiny head in full,
+    64 near-tie rows, 8 rows of the 16384 x 151936 scoring batch, 16 rows of the
+    int8 head (greedy, and the integer log-softmax of 16 quantised rows)."""
     import oracle
     import synth
+    o = oracle.default()
     d = synth.make_inputs("tinyllama", rows=2048)
     n = oracle.default_threads()
     rows = 0
     t0 = time.perf_counter()
     while rows < 2048 and time.perf_counter() - t0 < 8.0:
-        oracle.greedy_bf16(d["x"][rows:rows + 256], d["w"], nthreads=n)
+        o.greedy_bf16(d["x"][rows:rows + 256], d["w"], nthreads=n)
         rows += 256
     dt = time.perf_counter() - t0
     t1 = time.perf_counter()
-    oracle.greedy_bf16(d["x"][:64], d["w"], nthreads=1)
+    o.greedy_bf16(d["x"][:64], d["w"], nthreads=1)
     dt1 = time.perf_counter() - t1
+    del d
+
+    def timed(f):
+        t = time.perf_counter()
+        f()
+        return time.perf_counter() - t
+
+    other = {}
+    dt_ = synth.make_inputs("tiny")
+    t = timed(lambda: o.greedy_bf16(dt_["x"], dt_["w"], nthreads=n))
+    other["tiny_greedy_4x64x1000"] = {"rows": 4, "s": t, "rows_per_s": 4 / t}
+    nt = synth.make_inputs("neartie", rows=64)
+    t = timed(lambda: o.greedy_bf16(nt["x"], nt["w"], nthreads=n))
+    other["neartie_greedy_2048x32000"] = {"rows": 64, "s": t, "rows_per_s": 64 / t}
+    del nt
+    lp = synth.make_inputs("logprob", rows=8)
+    t = timed(lambda: o.logprob_bf16(lp["x"], lp["w"], lp["target"], nthreads=n))
+    other["logprob_4096x151936"] = {"rows": 8, "s": t, "rows_per_s": 8 / t}
+    del lp
+    i8 = synth.make_inputs("int8", rows=16)
+    t = timed(lambda: o.greedy_i8(i8["x"], i8["w"], i8["scale"], nthreads=n))
+    other["int8_greedy_4096x128256"] = {"rows": 16, "s": t, "rows_per_s": 16 / t}
+    q, M, E = o.quantize_rows(i8["hidden"])
+    t = timed(lambda: o.logprob_int(q, i8["w"], *i8["unit"], M, E, i8["target"], nthreads=n))
+    other["int8_integer_logprob_4096x128256"] = {"rows": 16, "s": t, "rows_per_s": 16 / t}
+    del i8
     return {"value": rows / dt, "unit": "rows/s", "cores": n, "kind": "oracle",
             "sample": f"float64 greedy top-2 of rows 0..{rows - 1} of the H=2048, V=32000 head "
                       f"({dt:.1f} s wall on {n} threads)",
+            "threads": n, "host": host_facts(),
             "single_thread_rows_per_s": 64 / dt1,
-            "single_thread_sample": f"rows 0..63 on one thread ({dt1:.1f} s)"}
+            "single_thread_sample": f"rows 0..63 on one thread ({dt1:.1f} s)",
+            "other": other}
+
+
+def output_digests(torch, lmhead, synth, bf16, dev) -> dict:
+    """SHA-256 (16 hex digits) of the outputs of fixed scenarios, one per mode
+    and call: a result, so that two runs or two builds can be compared bit for
+    bit (the integer head's bits are also those of the stored oracle outputs
+    the tests compare with)."""
+    def h(*ts):
+        m = hashlib.sha256()
+        for t in ts:
+            m.update(t.detach().contiguous().cpu().numpy().tobytes())
+        return m.hexdigest()[:16]
+
+    d = synth.make_inputs("tinyllama")
+    x, w = bf16(d["x"]), bf16(d["w"])
+    t = torch.from_numpy(d["target"]).to(dev)
+    seed = torch.arange(512, dtype=torch.int64, device=dev) * 7919 + 1
+    pos = torch.arange(512, dtype=torch.int64, device=dev)
+    out = {"float_logits_512x2048x32000": h(lmhead.logits(x, w)),
+           "float_greedy_512": h(*lmhead.greedy_top2(x, w)[:3]),
+           "float_logprob_512": h(lmhead.logprob(x, w, t)),
+           "bf16_output_gated_tau1e-3_512": h(*lmhead.greedy_gated(x, w, 1e-3)),
+           "float_sample_T0.7_512": h(*lmhead.sample_gumbel(x, w, 0.7, seed, pos))}
+    del x, w
+    i8 = synth.make_inputs("int8")
+    xi, wi = torch.from_numpy(i8["x"]).to(dev), torch.from_numpy(i8["w"]).to(dev)
+    si, ti = torch.from_numpy(i8["scale"]).to(dev), torch.from_numpy(i8["target"]).to(dev)
+    out["int8_logits_8x4096x128256"] = h(lmhead.logits(xi[:8].contiguous(), wi))
+    out["int8_greedy_512"] = h(*lmhead.greedy_top2(xi, wi, row_scale=si))
+    q, sm, se = lmhead.quantize_rows(torch.from_numpy(i8["hidden"]).to(dev))
+    out["int8_integer_logprob_512"] = h(lmhead.logprob_int(q, wi, i8["unit"], sm, se, ti))
+    return out
 
 
 def main():
@@ -218,7 +298,18 @@ def main():
                     help="only launch what the counter runs read: a 512 MiB device copy "
                          "(calibration), greedy top-2 at batch 1, 256 and 512 and the int8 "
                          "head at batch 512")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DB",
+                    help="print the markdown summary of rocprofv3 --pmc databases of "
+                         "--counters runs (no GPU needed)")
+    ap.add_argument("--summarize-trace", metavar="DB",
+                    help="print the per-kernel durations of a rocprofv3 --kernel-trace database")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(rows shard across GPUs with no exchange).", file=sys.stderr)
@@ -312,11 +403,13 @@ def main():
     # ---- other workloads (reported, not in value)
     if not args.no_extras:
         out["other"] = extras(torch, lmhead, synth, bf16, x, ws_, d)
+        out["output_digests"] = output_digests(torch, lmhead, synth, bf16, dev)
     del callers
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
-        log(f"cpu oracle: {out['cpu_baseline']['value']:.1f} rows/s on "
-            f"{out['cpu_baseline']['cores']} threads")
+        cb = out["cpu_baseline"]
+        log(f"cpu oracle: {cb['value']:.1f} rows/s on {cb['cores']} threads "
+            f"({cb['host']['online_cpus']} online CPUs, {cb['host']['cpu_model']})")
     print(json.dumps(out), flush=True)
 
 
@@ -356,6 +449,154 @@ def counters_run(torch, lmhead, synth, dev):
         c()
     torch.cuda.synchronize()
     log("counter launches: int8 greedy 4096 x 128256 batch 512 done")
+
+
+# ------------------------------------------------------------ profile summaries
+# Kernels of the launch sequence of --counters, by (template arguments, mode,
+# epilogue, threads in the grid): the workload each one belongs to.
+COUNTER_CONFIGS = [
+    ("Tile<32, 128, 1, 4, 512, 2, 2, false, false>, 0, 1>", 64000, "tinyllama greedy, batch 1, tile kernel"),
+    ("lmhead_merge_top2_kernel<0, 1>", 256, "tinyllama greedy, batch 1, fold kernel"),
+    ("Tile<256, 128, 4, 2, 128, 2, 4, false, false>, 0, 1>", 128000, "tinyllama greedy, batch 256, tile kernel"),
+    ("lmhead_merge_top2_kernel<0, 1>", 16384, "tinyllama greedy, batch 256, fold kernel"),
+    ("Tile<256, 256, 4, 2, 128, 2, 3, false, true>, 0, 1>", 128000, "tinyllama greedy, batch 512, tile kernel"),
+    ("lmhead_merge_top2_kernel<0, 1>", 32768, "tinyllama greedy, batch 512, fold kernel"),
+    ("Tile<256, 256, 4, 2, 128, 2, 3, false, true>, 1, 1>", 513024, "int8 4096x128256 greedy, batch 512, tile kernel"),
+    ("lmhead_merge_top2_kernel<1, 1>", 32768, "int8 4096x128256 greedy, batch 512, fold kernel"),
+]
+COPY_KERNEL = ("__amd_rocclr_copyBuffer", 131072)   # the 512 MiB calibration copy
+
+
+def _rocpd(db):
+    """(per-dispatch rows {name, grid, dur_ns, counters}) of a rocprofv3 database."""
+    import sqlite3
+    con = sqlite3.connect(str(db))
+    cur = con.cursor()
+    out = {}
+    for d, name, dur, grid in cur.execute(
+            "select dispatch_id, name, duration, grid_x * grid_y * grid_z from kernels"):
+        out[d] = {"name": name, "grid": grid, "dur_ns": dur, "c": {}}
+    try:
+        for d, cn, v in cur.execute("select dispatch_id, counter_name, value from counters_collection"):
+            if d in out:
+                out[d]["c"][cn] = v
+    except sqlite3.OperationalError:
+        pass
+    return list(out.values())
+
+
+def _label(name, grid):
+    for key, g, label in COUNTER_CONFIGS:
+        if key in name and g == grid:
+            return label
+    return None
+
+
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+
+
+def _pmc_names(db):
+    import sqlite3
+    con = sqlite3.connect(str(db))
+    try:
+        return sorted({r[0] for r in con.execute("select distinct counter_name from counters_collection")})
+    except sqlite3.OperationalError:
+        return []
+
+
+def summarize_counters(dbs) -> str:
+    """Markdown summary of --counters runs: per workload kernel, the median of
+    each counter over its dispatches, and derived figures (HBM bytes from the
+    calibrated FETCH_SIZE / WRITE_SIZE, MFMA busy cycles against the time the
+    kernel took at the 2.4 GHz peak clock, LDS, TA and TD busy shares)."""
+    per = {}
+    calib = {}
+    for db in dbs:
+        for r in _rocpd(db):
+            if COPY_KERNEL[0] in r["name"] and r["grid"] == COPY_KERNEL[1]:
+                for cn, v in r["c"].items():
+                    calib.setdefault(cn, []).append(v)
+                continue
+            lab = _label(r["name"], r["grid"])
+            if lab is None:
+                continue
+            e = per.setdefault(lab, {"name": r["name"], "dur": [], "c": {}})
+            e["dur"].append(r["dur_ns"])
+            for cn, v in r["c"].items():
+                e["c"].setdefault(cn, []).append(v)
+    fetch_f = 524288.0 / _median(calib["FETCH_SIZE"]) if "FETCH_SIZE" in calib else None
+    write_f = 524288.0 / _median(calib["WRITE_SIZE"]) if "WRITE_SIZE" in calib else None
+    lines = ["| kernel | counter | median per dispatch |", "|---|---|---|"]
+    derived = ["| kernel | duration us (profiled) | MFMA busy at 2.4 GHz | MFMA busy / active cycles | "
+               "LDS active | TA busy | TD busy | read MB | written MB |",
+               "|---|---|---|---|---|---|---|---|---|"]
+    traffic = {}
+    for key, _g, lab in COUNTER_CONFIGS:
+        if lab not in per:
+            continue
+        e = per[lab]
+        c = {cn: _median(v) for cn, v in e["c"].items()}
+        for cn in sorted(c):
+            lines.append(f"| {lab} | {cn} | {c[cn]:.6g} |")
+        dur = _median(e["dur"]) / 1e3
+        # GRBM_GUI_ACTIVE: busy cycles summed over the 8 XCDs (its window is a
+        # few microseconds longer than the dispatch, so shares over it are
+        # lower bounds)
+        cyc = c["GRBM_GUI_ACTIVE"] / 8 if "GRBM_GUI_ACTIVE" in c else None
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        peak = busy / (1024 * dur * 1e3 * 2.4) if busy is not None else None
+        mfma = busy / (1024 * cyc) if cyc and busy is not None else None
+        lds = 4 * c["SQ_LDS_IDX_ACTIVE"] / (256 * cyc) if cyc and "SQ_LDS_IDX_ACTIVE" in c else None
+        ta = c["TA_TA_BUSY_sum"] / (256 * cyc) if cyc and "TA_TA_BUSY_sum" in c else None
+        td = c["TD_TD_BUSY_sum"] / (256 * cyc) if cyc and "TD_TD_BUSY_sum" in c else None
+        rd = c["FETCH_SIZE"] * 1024 * fetch_f / 1e6 if fetch_f and "FETCH_SIZE" in c else None
+        wr = c["WRITE_SIZE"] * 1024 * write_f / 1e6 if write_f and "WRITE_SIZE" in c else None
+        if rd is not None and wr is not None:
+            traffic[lab] = (rd + wr) * 1e6
+        f = lambda v, fmt: "" if v is None else format(v, fmt)  # noqa: E731
+        derived.append(f"| {lab} | {dur:.2f} | {f(peak, '.1%')} | {f(mfma, '.1%')} | {f(lds, '.1%')} | "
+                       f"{f(ta, '.1%')} | {f(td, '.1%')} | {f(rd, '.2f')} | {f(wr, '.2f')} |")
+    cal = []
+    if fetch_f:
+        cal.append(f"| FETCH_SIZE | {_median(calib['FETCH_SIZE']):.1f} KiB | {fetch_f:.3f} |")
+    if write_f:
+        cal.append(f"| WRITE_SIZE | {_median(calib['WRITE_SIZE']):.1f} KiB | {write_f:.3f} |")
+    call = [traffic.get("tinyllama greedy, batch 512, " + k) for k in ("tile kernel", "fold kernel")]
+    head = [f"source_digest: {source_digest()}"]
+    if None not in call:
+        head.append(f"hbm_bytes_per_launch: {sum(call):.0f}")
+    head += ["", "Commands (from the repository root on the GPU host, one rocprofv3 run per "
+             "counter set):", "", "    cd /tmp && export TMPDIR=/tmp"]
+    for db in dbs:
+        names = [n for n in _pmc_names(db)]
+        d = Path(db).parent
+        d = d if d.is_absolute() else Path("/root/repo") / d
+        head.append(f"    timeout -s KILL 120 rocprofv3 --pmc {' '.join(names)} -d {d} -o pmc -- "
+                    f"python3 /root/repo/bench.py --counters")
+    out = head + ["", "## Derived per kernel (medians over its dispatches)", ""] + derived + [""]
+    if cal:
+        out += ["## Calibration: a plain copy of 512 MiB (524288 KiB read, 524288 KiB written)", "",
+                "| counter | copy reads as | factor |", "|---|---|---|"] + cal + [""]
+    out += ["## Raw counters", ""] + lines + [""]
+    return "\n".join(out)
+
+
+def summarize_trace(db) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace database: calls and
+    average / min / max duration per kernel."""
+    per = {}
+    for r in _rocpd(db):
+        per.setdefault(r["name"], []).append(r["dur_ns"] / 1e3)
+    rows = ["| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        if "lmhead" not in name and "quantize" not in name:
+            continue
+        short = name.replace("lmh::(anonymous namespace)::", "").replace("void ", "")
+        short = short.replace("(lmh::Params)", "")
+        rows.append(f"| `{short}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    return "\n".join(rows) + "\n"
 
 
 def extras(torch, lmhead, synth, bf16, x, w_copies, d):
