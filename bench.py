@@ -303,7 +303,12 @@ def main():
                          "--counters runs (no GPU needed)")
     ap.add_argument("--summarize-trace", metavar="DB",
                     help="print the per-kernel durations of a rocprofv3 --kernel-trace database")
+    ap.add_argument("--write-tables", action="store_true",
+                    help="regenerate the tables of README.md and DESIGN.md from results/ (no GPU)")
     args = ap.parse_args()
+    if args.write_tables:
+        write_tables(ROOT / "results", [ROOT / "README.md", ROOT / "DESIGN.md"])
+        return
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters))
         return
@@ -597,6 +602,153 @@ def summarize_trace(db) -> str:
         short = short.replace("(lmh::Params)", "")
         rows.append(f"| `{short}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
     return "\n".join(rows) + "\n"
+
+
+# ------------------------------------------------------- generated tables
+def _fmt_roof(r):
+    return f"{100 * r['frac']:.1f}% of {'HBM' if r['bound'] == 'hbm' else 'MFMA'} peak"
+
+
+def render_tables(results: Path) -> dict:
+    """Markdown tables from the committed result files: the bench line
+    (results/bench_full.json) and the GPU tests' parity files."""
+    b = json.loads((results / "bench_full.json").read_text())
+    t = {}
+    rows = ["| batch | us / call (W from HBM) | rows/s | roofline | us / call (W in the Infinity Cache) |",
+            "|---|---|---|---|---|"]
+    for r in b["per_batch"]:
+        rows.append(f"| {r['batch']} | {r['us_per_call']:.2f} | {r['rows_per_s'] / 1e6:.3f} M | "
+                    f"{_fmt_roof(r['roofline'])} | {r['us_per_call_warm_mall']:.2f} |")
+    rows.append(f"| sweep step (841 rows) | {b['ms_per_step'] * 1e3:.1f} | "
+                f"{b['value'] / 1e6:.3f} M | dominant call: {_fmt_roof(b['roofline'])} | |")
+    t["per_batch"] = "\n".join(rows)
+    o = b.get("other", {})
+    names = {
+        "tinyllama_logprob_b512": "log-prob, 2048 x 32000, batch 512",
+        "tinyllama_logits_b512": "float32 logits stored, 2048 x 32000, batch 512",
+        "neartie_4096": "near-tie set, 2048 x 32000, 4096 rows",
+        "logprob_16384x151936x4096": "log-prob scoring, 4096 x 151936, 16384 rows",
+        "greedy_4096x151936_b1": "greedy, 4096 x 151936 (1.24 GB of W), batch 1",
+        "greedy_4096x151936_b64": "greedy, 4096 x 151936, batch 64",
+        "int8_b1": "int8 greedy, 4096 x 128256, batch 1",
+        "int8_b8": "int8 greedy, batch 8",
+        "int8_b64": "int8 greedy, batch 64",
+        "int8_b256": "int8 greedy, batch 256",
+        "int8_b512": "int8 greedy, batch 512",
+        "int_logprob_b1": "integer log-prob (Q.24), 4096 x 128256, batch 1",
+        "int_logprob_b512": "integer log-prob (Q.24), batch 512",
+    }
+    rows = ["| workload | time / call | rows/s | roofline |", "|---|---|---|---|"]
+    for k, label in names.items():
+        if k not in o:
+            continue
+        r = o[k]
+        tt = f"{r['ms_per_call']:.2f} ms" if "ms_per_call" in r else f"{r['us_per_call']:.1f} us"
+        rows.append(f"| {label} | {tt} | {r['rows_per_s'] / 1e6:.3f} M | {_fmt_roof(r['roofline'])} |")
+    for B in (1, 512):
+        g, sm = o.get(f"gated_tau1e-3_b{B}"), o.get(f"sample_gumbel_b{B}")
+        if g:
+            rows.append(f"| margin-gated head (tau 1e-3), batch {B} | {g['us_per_call']:.1f} us | | "
+                        f"{100 * g['overhead']:+.1f}% against the bf16-output head, "
+                        f"{100 * g['gate_rate']:.2f}% of rows recomputed |")
+        if sm:
+            rows.append(f"| seeded Gumbel-max sampling, batch {B} | {sm['us_per_call']:.1f} us | "
+                        f"{sm['rows_per_s'] / 1e6:.3f} M | {100 * sm['overhead']:+.1f}% against greedy |")
+    if "tiny_b4" in o:
+        tb = o["tiny_b4"]
+        rows.append(f"| tiny 4 x 64 x 1000: greedy / log-prob / logits | {tb['greedy_us_per_call']:.1f} / "
+                    f"{tb['logprob_us_per_call']:.1f} / {tb['logits_us_per_call']:.1f} us | | latency |")
+    t["other"] = "\n".join(rows)
+    c = b.get("cpu_baseline")
+    if c:
+        h = c.get("host", {})
+        rows = [f"Host: {h.get('cpu_model')}, {h.get('online_cpus')} online CPUs; the oracle ran on "
+                f"{c['threads']} threads.", "",
+                "| oracle workload | rows | rows/s |", "|---|---|---|",
+                f"| float64 greedy, 2048 x 32000 (the metric's) | {c['sample'].split('rows ')[1].split(' ')[0]} | "
+                f"{c['value']:.1f} ({c['single_thread_rows_per_s']:.1f} on one thread) |"]
+        for k, r in c.get("other", {}).items():
+            rows.append(f"| {k} | {r['rows']} | {r['rows_per_s']:.1f} |")
+        t["cpu"] = "\n".join(rows)
+    par = {}
+    for f in (sorted(results.glob("parity_*.json")) + sorted(results.glob("invariance.json"))
+              + sorted(results.glob("batch_variance.json"))):
+        par[f.stem] = json.loads(f.read_text())
+    rows = ["| check | rows | result |", "|---|---|---|"]
+    g = par.get("parity_tinyllama_greedy", {})
+    for B in (1, 8, 64, 256, 512):
+        e = g.get(f"batch_{B}")
+        if e:
+            rows.append(f"| float32 greedy, 2048 x 32000, batch {B}, against the oracle | {e['rows']} | "
+                        f"{e['exempt_rows']} exempt rows (oracle gap < 1e-4); max error of values "
+                        f"{e['max_abs_err_values']:.1e} |")
+    e = par.get("parity_tinyllama_logprob", {}).get("batch_512")
+    if e:
+        rows.append(f"| float32 log-prob, 2048 x 32000 | {e['rows']} | max error {e['max_abs_err']:.1e} |")
+    e = par.get("parity_logprob_scoring", {}).get("rows_0_255_and_every_64th")
+    if e:
+        rows.append(f"| float32 log-prob, 4096 x 151936 (16384-row batch) | {e['rows']} | "
+                    f"max error {e['max_abs_err']:.1e} |")
+    nt = par.get("parity_neartie", {})
+    e = nt.get("float32_head_vs_oracle")
+    if e:
+        gaps = e["exempt_gap_bf16_ulps"]
+        rows.append(f"| float32 greedy, near-tie set | {e['rows']} | {e['exempt_rows']} exempt rows "
+                    f"(gaps {min(gaps, default=0):.2f}-{max(gaps, default=0):.2f} bf16 ulps), "
+                    f"{e['exempt_rows_top1_differs']} of them with the other top-1 |")
+    e = nt.get("bf16_head_vs_oracle_bf16_rounding")
+    if e:
+        rows.append(f"| bf16-output head against the oracle's bf16-rounded logits | {e['rows']} | "
+                    f"{e['top1_differs']} top-1 differ, {e['values_differ_by_one_bf16_ulp']} values one bf16 ulp apart |")
+    i8 = par.get("parity_int8", {})
+    n = sum(v["rows"] for k, v in i8.items() if k.startswith("greedy_batch") and v.get("bit_exact"))
+    if n:
+        rows.append(f"| int8 greedy (ids, raw, values, margin), batches 1/8/64/256/512 | {n} | bit-exact |")
+    n = sum(v["rows"] for k, v in i8.items() if k.startswith("integer_logprob") and v.get("bit_exact"))
+    if n:
+        rows.append(f"| integer log-prob (Q.24), batches 1/8/64/256/512 | {n} | bit-exact |")
+    if "logits_rows_compared" in i8:
+        rows.append(f"| int8 logits of a 512-row call | {i8['logits_rows_compared']} | bit-exact |")
+    e = i8.get("float_logprob_batch_512")
+    if e:
+        rows.append(f"| float log-prob of the int8 head | {e['rows']} | max error {e['max_abs_err']:.1e} |")
+    inv = par.get("invariance", {})
+    if "logits_batches_1_to_512" in inv:
+        rows.append(f"| bitwise invariance: logits, top-2, log-prob at every batch 1..512 | "
+                    f"{inv['logits_batches_1_to_512']['rows_compared']} rows x 32000 logits | identical |")
+    t["parity"] = "\n".join(rows)
+    bv = par.get("batch_variance")
+    if bv:
+        rows = ["| head | compared | log-prob bits differ | max abs dlog p | ratio outside [0.9, 1.1] |",
+                "|---|---|---|---|---|"]
+        for key, r in bv.items():
+            head, cmp_ = key.split(" | ")
+            rows.append(f"| {head} | {cmp_.replace('_', ' ')} | {100 * r['bits_differ']:.2f}% | "
+                        f"{r['max_abs_dlogp']:.1e} | {100 * r['ratio_out_of_band']:.2f}% |")
+        t["batch_variance"] = "\n".join(rows)
+    nt_tab = nt.get("agreement_with_planted_winner")
+    if nt_tab:
+        rows = ["| planted gap (bf16 ulps) | rows | float32 head picks the planted winner | bf16-output head |",
+                "|---|---|---|---|"]
+        for r in nt_tab:
+            lo, hi = r["gap_bf16_ulps"]
+            rows.append(f"| {'0 (exact tie)' if hi == 0 else f'({lo}, {hi}]'} | {r['rows']} | "
+                        f"{100 * r['float32_head_agrees']:.2f}% | {100 * r['bf16_head_agrees']:.2f}% |")
+        t["neartie"] = "\n".join(rows)
+    return t
+
+
+def write_tables(results: Path, docs) -> None:
+    """Replace every <!-- generated:NAME --> ... <!-- /generated:NAME --> block
+    of the docs with the table NAME."""
+    import re
+    tabs = render_tables(results)
+    for doc in docs:
+        text = doc.read_text()
+        for name, md in tabs.items():
+            text = re.sub(rf"(<!-- generated:{name} -->).*?(<!-- /generated:{name} -->)",
+                          lambda m: m.group(1) + "\n" + md + "\n" + m.group(2), text, flags=re.S)
+        doc.write_text(text)
 
 
 def extras(torch, lmhead, synth, bf16, x, w_copies, d):

@@ -24,10 +24,10 @@
  * integer sum), never by the number of rows or a row's position in the batch;
  * the softmax partial sums are fixed by V alone.  A row's outputs are
  * therefore bitwise identical at every batch size.  ("12 Exactness", section
- * 12.2: every matrix-product kernel fixes its reduction order by the weight's
- * shape and never by the row count;
- * "Integer-Only Arithmetic", section "Why kernels don't always add in the same
- * order": split reductions chosen by batch size break batch invariance.)
+ * 12.2: the summation order of a product is a function of the weight's
+ * dimensions alone, so the batch's row count cannot change it; "Integer-Only
+ * Arithmetic", section "Why kernels don't always add in the same order":
+ * split reductions chosen by batch size break batch invariance.)
  *
  * Layout.  x is [B, H] row-major, w is [V, H] row-major (each vocabulary row
  * contiguous in k).  bf16 tensors are raw 16-bit patterns.  x, w and the
@@ -162,9 +162,10 @@ lmhead_status lmhead_greedy_gated(int mode, const void *x, const void *w, int64_
                                   float *margin, int32_t *gated, void *ws, size_t ws_bytes,
                                   void *stream);
 
-/* Seeded Gumbel-max sampling ("12 Exactness", section 12.5: the token at index
- * t is the argmax of log p_t + G_t, with Gumbel noise G_t from a generator
- * seeded by (seed, t); an exact draw from p_t).  Since log p_t differs from
+/* Seeded Gumbel-max sampling ("12 Exactness", section 12.5: adding Gumbel
+ * noise, drawn from a generator keyed by the seed and the position, to every
+ * token's log-probability and taking the largest sum is an exact draw from
+ * the distribution).  Since log p_t differs from
  * z / T by a constant per row:
  *   token[b] = argmax_v ( z[b, v] / temperature + G(seed[b], position[b], v) ),
  *              the lowest id on a tie;

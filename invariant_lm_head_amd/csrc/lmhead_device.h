@@ -29,9 +29,10 @@
 //     blocks in 16 slots (block b into slot b mod 16, ascending), then a fixed
 //     pairing tree over the slots.  All of it depends on V only.  Top-2 with
 //     lowest-id ties is exact in any order.
-// ("12 Exactness", section 12.2: the reduction order is fixed by the weight's
-// shape and never by the row count; "Integer-Only Arithmetic", section "Why
-// kernels don't always add in the same order": split-K chosen by batch size.)
+// ("12 Exactness", section 12.2: a product's summation order follows from the
+// weight's dimensions alone, not from the batch's row count; "Integer-Only
+// Arithmetic", section "Why kernels don't always add in the same order":
+// split-K chosen by batch size.)
 //
 // Data movement: operand tiles are staged HBM -> LDS with global_load_lds_dwordx4
 // (no register round trip), in rings of stages whose W loads are spread over

@@ -273,8 +273,9 @@ void oracle_philox4x64(const uint64_t ctr[4], const uint64_t key[2], uint64_t ou
 }
 
 /* Gumbel noise of token v for the draw keyed by (seed, position) ("12
- * Exactness", section 12.5: the token at index t is the argmax of
- * log p_t + G_t, G_t Gumbel noise from a generator seeded by (seed, t)).
+ * Exactness", section 12.5: each token's log-probability plus Gumbel noise
+ * from a generator keyed by the seed and the position; the largest sum is the
+ * draw).
  * Word (v >> 5) & 3 of Philox4x64-10 at counter (32 (v >> 7) + (v & 31), 0, 0, 0)
  * under key (seed, position); its top 23 bits u give U = (2u + 1) 2^-24 in
  * (0, 1); G = -ln(-ln U). */

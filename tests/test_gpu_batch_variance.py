@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from invariant_lm_head_amd import lmhead
-from tests.gpu_util import DEV, gpu, host, o, tl  # noqa: F401
+from tests.gpu_util import DEV, gpu, host, o, record, tl  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
@@ -83,6 +83,8 @@ def test_batch_variance_demonstrator(tl):
     for name, r in res.items():
         for k, (ch, mx, out) in r.items():
             print(f"{name:24s} {k:11s} {100 * ch:10.2f}% {mx:11.2e} {100 * out:22.2f}%", flush=True)
+            record("batch_variance", f"{name} | {k}", {"bits_differ": ch, "max_abs_dlogp": mx,
+                                                        "ratio_out_of_band": out})
     for k in ("b8_vs_b1", "b512_vs_b1", "rerun"):
         assert res["this head"][k] == (0.0, 0.0, 0.0), k
     for name in res:
