@@ -170,8 +170,9 @@ lmhead_status lmhead_greedy_gated(int mode, const void *x, const void *w, int64_
  *   token[b] = argmax_v ( z[b, v] / temperature + G(seed[b], position[b], v) ),
  *              the lowest id on a tie;
  *   G(s, t, v) = -ln(-ln U), U = (2u + 1) 2^-24, u the top 23 bits of word
- *              (v >> 5) & 3 of Philox4x64-10 (Salmon et al., SC 2011) at counter
- *              (32 (v >> 7) + (v & 31), 0, 0, 0) under key (s, t).
+ *              (v >> 5) & 3 of Philox4x32-10 (Salmon et al., SC 2011) at counter
+ *              (32 (v >> 7) + (v & 31), 0, t mod 2^32, t div 2^32) under key
+ *              (s mod 2^32, s div 2^32), t taken as an unsigned 64-bit value.
  * A row's draw depends on its own (seed, position) and logits only, never on
  * the batch.  value[b] (optional) = the winning score, gap[b] (optional) = its
  * lead over the runner-up (small gaps are where float32 rounding could pick

@@ -304,53 +304,59 @@ template <int NR, int NM> __device__ __forceinline__ void interleave_reads() {
 }
 
 // ----------------------------------------------------- Gumbel-max noise
-// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, SC 2011): ten rounds of two
-// 64 x 64 -> 128-bit products of counter words with fixed multipliers, the high
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011): ten rounds of two
+// 32 x 32 -> 64-bit products of counter words with fixed multipliers, the high
 // halves mixed with the other counter words and the key, the key bumped by
-// fixed Weyl constants between rounds.  Here the counter is (c, 0, 0, 0).
-__device__ __forceinline__ void philox4x64(uint64_t c, uint64_t k0, uint64_t k1,
-                                           uint64_t (&out)[4]) {
-  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
-  uint64_t x0 = c, x1 = 0, x2 = 0, x3 = 0;
+// fixed Weyl constants between rounds.  Each product is one v_mad_u64_u32.
+__device__ __forceinline__ void philox4x32(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                           uint32_t k0, uint32_t k1, uint32_t (&out)[4]) {
+  constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+  constexpr unsigned kXor3 = 0x96;  // truth table of x ^ y ^ z
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) { k0 += W0; k1 += W1; }
-    const uint64_t h0 = __umul64hi(M0, x0), l0 = M0 * x0;
-    const uint64_t h1 = __umul64hi(M1, x2), l1 = M1 * x2;
-    const uint64_t y0 = h1 ^ x1 ^ k0, y2 = h0 ^ x3 ^ k1;
-    x0 = y0; x1 = l1; x2 = y2; x3 = l0;
+    const uint64_t p0 = (uint64_t)M0 * c0, p1 = (uint64_t)M1 * c2;
+    const uint32_t y0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, kXor3);
+    const uint32_t y2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, kXor3);
+    c0 = y0; c1 = (uint32_t)p1; c2 = y2; c3 = (uint32_t)p0;
   }
-  out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
 }
 
-// G = -ln(-ln U), U = (2u + 1) 2^-24 from the top 23 bits u of a Philox word.
-// -ln U: for U < 1/2 from the hardware log2 (no cancellation there); for
-// U >= 1/2 from d = 1 - U (exact) as 2 atanh(d / (2 - d)), whose series in
-// s = d / (2 - d) <= 1/3 is summed to s^17 (terms shrink at least 9-fold).
-__device__ __forceinline__ float gumbel_of(uint64_t word) {
-  const unsigned u = (unsigned)(word >> 41);
-  const float U = (float)(2u * u + 1u) * 0x1p-24f;
-  const float d = (float)((1u << 24) - 2u * u - 1u) * 0x1p-24f;  // 1 - U, exact
-  const float s = d / (2.0f - d);
+// G = -ln(-ln U), U = (2u + 1) 2^-24 from the top 23 bits u of a Philox word,
+// evaluated as G = -ln 2 log2(L) - ln(ln 2) with L = -log2 U = (-ln U) / ln 2.
+// For U < 3/4, L comes from the hardware log2 (|log2 U| > 0.41 there, so its
+// absolute error stays small relative to L).  For U >= 3/4 it comes from
+// d = 1 - U (exact) as (2 / ln 2) atanh(s), s = d / (2 - d) <= 1/7, whose odd
+// series is summed to s^9: the first term left out is below 4e-10 of the sum.
+// Every multiply-add is an explicit fma (one rounding each).
+// x < t ? a : b as one compare and one v_cndmask: both operands are computed
+// anyway by a 64-lane wave, and a select written in C++ is turned into a
+// branch around the costlier operand
+__device__ __forceinline__ float select_lt(float x, float t, float a, float b) {
+  float r;
+  asm("v_cmp_lt_f32_e32 vcc, %1, %2\n\tv_cndmask_b32_e32 %0, %4, %3, vcc"
+      : "=v"(r) : "v"(x), "v"(t), "v"(a), "v"(b) : "vcc");
+  return r;
+}
+constexpr float kLnLn2 = -0.366512920581664327f;  // ln(ln 2)
+__device__ __forceinline__ float gumbel_of(uint32_t word) {
+  constexpr float c1 = 2.88539008177792681f;  // 2 / ln 2, then c1 / k for s^k
+  const float U = (float)((word >> 8) | 1u) * 0x1p-24f;  // (2u + 1) 2^-24, exact
+  const float d = 1.0f - U;                               // exact
+  const float s = d * __builtin_amdgcn_rcpf(2.0f - d);
   const float s2 = s * s;
-  float a = 1.0f / 17.0f;
-  a = a * s2 + 1.0f / 15.0f;
-  a = a * s2 + 1.0f / 13.0f;
-  a = a * s2 + 1.0f / 11.0f;
-  a = a * s2 + 1.0f / 9.0f;
-  a = a * s2 + 1.0f / 7.0f;
-  a = a * s2 + 1.0f / 5.0f;
-  a = a * s2 + 1.0f / 3.0f;
-  a = a * s2 + 1.0f;
-  const float L_series = 2.0f * (s * a);
-  const float L_log = -kLn2 * log2_hw(U);
-  const float L = U < 0.5f ? L_log : L_series;
-  return -kLn2 * log2_hw(L);
+  float a = __builtin_fmaf(s2, c1 / 9.0f, c1 / 7.0f);
+  a = __builtin_fmaf(a, s2, c1 / 5.0f);
+  a = __builtin_fmaf(a, s2, c1 / 3.0f);
+  a = __builtin_fmaf(a, s2, c1);
+  const float L = select_lt(U, 0.75f, -log2_hw(U), s * a);
+  return __builtin_fmaf(-kLn2, log2_hw(L), -kLnLn2);
 }
 
-__device__ __forceinline__ uint64_t word_of(const uint64_t (&w)[4], int q) {
-  const uint64_t a = (q & 1) ? w[1] : w[0], b = (q & 1) ? w[3] : w[2];
+__device__ __forceinline__ uint32_t word_of(const uint32_t (&w)[4], int q) {
+  const uint32_t a = (q & 1) ? w[1] : w[0], b = (q & 1) ? w[3] : w[2];
   return (q & 2) ? b : a;
 }
 
@@ -1202,36 +1208,62 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
         // seeded Gumbel-max: every logit becomes y = z / T + G(seed, position,
         // column) in place (float32 bits), then the y are ranked like logits.
         // One Philox block per (row, 128-column block, column lane) serves the
-        // lane's column tiles of that block.
-#pragma unroll
-        for (int mt = 0; mt < T::WM; ++mt) {
-#pragma unroll
-          for (int b = 0; b < T::BPW; ++b) {
+        // lane's column tiles of that block, word q to the block's tile q.  The
+        // loops are unrolled at compile time: a rolled row loop would index the
+        // accumulators at run time.
+        // The tile's per-row keys and logit factors (1 / T, times the row
+        // scale in the int8 head) are staged in LDS first, after the exchange
+        // area: one global load per row for the workgroup instead of one
+        // dependent load per row value in every lane.
+        constexpr int TAB = T::BM * T::WAVES_N * 16;
+        static_assert(TAB + T::BM * 20 <= T::LDS, "draw table");
+        uint64_t *tseed = (uint64_t *)(smem + TAB);
+        uint64_t *tpos = tseed + T::BM;
+        float *tcr = (float *)(tpos + T::BM);
+        for (int r = tid; r < T::BM; r += T::NT) {
+          const int row = m0 + r;
+          if (row < p.B) {
+            float cr = p.inv_t;
+            if constexpr (MODE == 1) cr = (p.scale ? p.scale[row] : 1.0f) * p.inv_t;
+            tseed[r] = p.seed[row];
+            tpos[r] = (uint64_t)p.position[row];
+            tcr[r] = cr;
+          }
+        }
+        __syncthreads();
+        static_for<0, T::WM>([&](auto mt_) __attribute__((always_inline)) {
+          constexpr int mt = decltype(mt_)::value;
+          static_for<0, T::BPW>([&](auto b_) __attribute__((always_inline)) {
+            constexpr int b = decltype(b_)::value;
             const int col0 = wcol0 + b * T::NTB * 32 + j;
-            const uint64_t ctr = 32u * (uint64_t)(col0 >> 7) + (uint64_t)j;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int row = m0 + wm * T::WM * 32 + mt * 32 + acc_row(v, h);
+            const uint32_t ctr = 32u * (uint32_t)(col0 >> 7) + (uint32_t)j;
+            // tile of the block this lane's first column falls in (0 unless the
+            // block is split over waves)
+            const int q0 = (col0 >> 5) & 3;
+            static_for<0, 16>([&](auto v_) __attribute__((always_inline)) {
+              constexpr int v = decltype(v_)::value;
+              const int lr = wm * T::WM * 32 + mt * 32 + acc_row(v, h);
               // rows past B (tile padding) are never ranked: skip their noise
-              if (row < p.B) {
-                float cr = p.inv_t;
-                if constexpr (MODE == 1) cr = (p.scale ? p.scale[row] : 1.0f) * p.inv_t;
-                uint64_t words[4];
-                philox4x64(ctr, p.seed[row], (uint64_t)p.position[row], words);
+              if (m0 + lr < p.B) {
+                const float cr = tcr[lr];
+                const uint64_t seed = tseed[lr], pos = tpos[lr];
+                uint32_t words[4];
+                philox4x32(ctr, 0u, (uint32_t)pos, (uint32_t)(pos >> 32), (uint32_t)seed,
+                           (uint32_t)(seed >> 32), words);
 #pragma unroll
                 for (int k = 0; k < T::NTB; ++k) {
                   const int nt = b * T::NTB + k;
-                  const float y = (float)acc[mt][nt][v] * cr +
-                                  gumbel_of(word_of(words, ((col0 >> 5) + k) & 3));
+                  const uint32_t wq = T::PARTS == 1 ? words[k] : word_of(words, (q0 + k) & 3);
+                  const float y = (float)acc[mt][nt][v] * cr + gumbel_of(wq);
                   acc[mt][nt][v] = vfrom<val_t>(__float_as_int(y));
                 }
               }
               // one row value at a time: interleaving the 16 Philox chains would
               // buy nothing here and run out of registers
               __builtin_amdgcn_sched_barrier(0);
-            }
-          }
-        }
+            });
+          });
+        });
 #pragma unroll
         for (int mt = 0; mt < T::WM; ++mt) {
           const int lrow = wm * T::WM * 32 + mt * 32 + acc_row(u, h);  // row this lane ends with

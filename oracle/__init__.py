@@ -92,7 +92,7 @@ class Oracle:
             "oracle_logsoftmax_f64": ([P, i64, P], None),
             "oracle_logprob_i64_row": ([P, i64, D, i64], D),
             "oracle_round_bf16": ([D], D),
-            "oracle_philox4x64": ([P, P, P], None),
+            "oracle_philox4x32": ([P, P, P], None),
             "oracle_gumbel": ([ctypes.c_uint64, i64, i64], D),
             "oracle_sample_bf16": ([P, P, i64, i64, i64, D, P, P, P, P, P, i32], ctypes.c_int),
             "oracle_sample_i8": ([P, P, i64, i64, i64, P, D, P, P, P, P, P, i32], ctypes.c_int),
@@ -194,12 +194,12 @@ class Oracle:
         return ids, vals, margin, gated
 
     # ------------------------------------------------------- sampling
-    def philox4x64(self, ctr, key):
-        """Philox4x64-10 of a 4-word counter under a 2-word key (4 uint64 words)."""
-        c = np.ascontiguousarray(ctr, dtype=np.uint64)
-        k = np.ascontiguousarray(key, dtype=np.uint64)
-        out = np.empty(4, np.uint64)
-        self.lib.oracle_philox4x64(_ptr(c), _ptr(k), _ptr(out))
+    def philox4x32(self, ctr, key):
+        """Philox4x32-10 of a 4-word counter under a 2-word key (4 uint32 words)."""
+        c = np.ascontiguousarray(ctr, dtype=np.uint32)
+        k = np.ascontiguousarray(key, dtype=np.uint32)
+        out = np.empty(4, np.uint32)
+        self.lib.oracle_philox4x32(_ptr(c), _ptr(k), _ptr(out))
         return out
 
     def gumbel(self, seed: int, position: int, v: int) -> float:

@@ -35,7 +35,7 @@
  *             log p(t) = s_r (z_t - zmax) - ln S.
  *
  *  sampling   seeded Gumbel-max: token = argmax_v z_v / T + G(seed, t, v), the
- *             noise from Philox4x64-10 keyed by (seed, t) (see oracle_gumbel);
+ *             noise from Philox4x32-10 keyed by (seed, t) (see oracle_gumbel);
  *             int8 rows use the scaled logits raw_v * s_r.
  *
  *  integer    the all-integer front and back of the int8 head, an algorithm
@@ -251,22 +251,24 @@ double oracle_logprob_i64_row(const int64_t *z, int64_t V, double scale, int64_t
 }
 
 /* ------------------------------------------- seeded Gumbel-max sampling */
-/* Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
- * easy as 1, 2, 3", SC 2011): ten rounds of two 64 x 64 -> 128-bit products
- * of counter words with fixed multipliers, the high halves mixed with the other
- * counter words and the key, the key bumped by fixed Weyl constants between
- * rounds.  Counter and key are the whole state: output = f(counter, key). */
-void oracle_philox4x64(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]) {
-  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
-  uint64_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
-  uint64_t k0 = key[0], k1 = key[1];
+/* Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+ * easy as 1, 2, 3", SC 2011): ten rounds of two 32 x 32 -> 64-bit products
+ * of counter words 0 and 2 with fixed multipliers; the new counter is (high
+ * half of the second product ^ word 1 ^ key 0, its low half, high half of the
+ * first product ^ word 3 ^ key 1, its low half); the key is bumped by fixed
+ * Weyl constants between rounds.  Counter and key are the whole state:
+ * output = f(counter, key). */
+void oracle_philox4x32(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+  uint32_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
   for (int r = 0; r < 10; ++r) {
     if (r) { k0 += W0; k1 += W1; }
-    unsigned __int128 p0 = (unsigned __int128)M0 * x0;
-    unsigned __int128 p1 = (unsigned __int128)M1 * x2;
-    uint64_t y0 = (uint64_t)(p1 >> 64) ^ x1 ^ k0, y1 = (uint64_t)p1;
-    uint64_t y2 = (uint64_t)(p0 >> 64) ^ x3 ^ k1, y3 = (uint64_t)p0;
+    uint64_t p0 = (uint64_t)M0 * x0;
+    uint64_t p1 = (uint64_t)M1 * x2;
+    uint32_t y0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0, y1 = (uint32_t)p1;
+    uint32_t y2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1, y3 = (uint32_t)p0;
     x0 = y0; x1 = y1; x2 = y2; x3 = y3;
   }
   out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
@@ -276,16 +278,18 @@ void oracle_philox4x64(const uint64_t ctr[4], const uint64_t key[2], uint64_t ou
  * Exactness", section 12.5: each token's log-probability plus Gumbel noise
  * from a generator keyed by the seed and the position; the largest sum is the
  * draw).
- * Word (v >> 5) & 3 of Philox4x64-10 at counter (32 (v >> 7) + (v & 31), 0, 0, 0)
- * under key (seed, position); its top 23 bits u give U = (2u + 1) 2^-24 in
- * (0, 1); G = -ln(-ln U). */
+ * Word (v >> 5) & 3 of Philox4x32-10 at counter (32 (v >> 7) + (v & 31), 0,
+ * position mod 2^32, position div 2^32) under key (seed mod 2^32, seed div
+ * 2^32); its top 23 bits u give U = (2u + 1) 2^-24 in (0, 1); G = -ln(-ln U). */
 double oracle_gumbel(uint64_t seed, int64_t position, int64_t v) {
-  const uint64_t ctr[4] = {32 * (uint64_t)(v >> 7) + (uint64_t)(v & 31), 0, 0, 0};
-  const uint64_t key[2] = {seed, (uint64_t)position};
-  uint64_t out[4];
-  oracle_philox4x64(ctr, key, out);
-  const uint64_t u = out[(v >> 5) & 3] >> 41;
-  const double U = (double)(2 * u + 1) * 0x1p-24;
+  const uint64_t pos = (uint64_t)position;
+  const uint32_t ctr[4] = {(uint32_t)(32 * (v >> 7) + (v & 31)), 0, (uint32_t)pos,
+                           (uint32_t)(pos >> 32)};
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  oracle_philox4x32(ctr, key, out);
+  const uint32_t u = out[(v >> 5) & 3] >> 9;
+  const double U = (double)(2 * (uint64_t)u + 1) * 0x1p-24;
   return -log(-log(U));
 }
 

@@ -317,42 +317,57 @@ def _chi2_sf(stat, dof):
     return float(chi2.sf(stat, dof))
 
 
-def pin_philox_vs_numpy(o):
-    """Philox4x64-10 against numpy.random.Philox (an independent library
-    implementation of the same published generator; numpy advances the counter
-    before each block, so its counter c - 1 yields block c), including a carry
-    out of the low counter word."""
+_ROCRAND_TOOL: list = []
+
+
+def rocrand_philox_blocks(triples):
+    """Philox4x32-10 blocks from rocRAND's engine header (an independent
+    implementation of the published generator), built host-only once per
+    process: block of (seed, subsequence, n) = counter (n lo, n hi,
+    subsequence lo, subsequence hi) under key (seed lo, seed hi)."""
+    import subprocess
+    import tempfile
+    if not _ROCRAND_TOOL:
+        src = Path(__file__).resolve().parent / "philox_rocrand.cpp"
+        exe = Path(tempfile.mkdtemp(prefix="philox_rocrand_")) / "philox_rocrand"
+        subprocess.run(["/opt/rocm/llvm/bin/clang++", "-x", "hip", "--offload-host-only", "-O1",
+                        "-I/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+        _ROCRAND_TOOL.append(exe)
+    inp = "".join(f"{s} {q} {n}\n" for s, q, n in triples)
+    out = subprocess.run([str(_ROCRAND_TOOL[0])], input=inp, capture_output=True, text=True,
+                         check=True).stdout.split()
+    return np.array(out, dtype=np.uint64).astype(np.uint32).reshape(-1, 4)
+
+
+def pin_philox_vs_rocrand(o):
+    """Philox4x32-10 against rocRAND's engine on 64 random (counter, key) pairs
+    covering all four counter words (the second below 2^30) and both key words,
+    plus the zero block and single set bits."""
     rng = np.random.default_rng(41)
-    cases = [([1, 0, 0, 0], [0, 0]), ([0, 9, 3, 1], [5, 6])]
-    for _ in range(64):
-        c = rng.integers(0, 2 ** 63, 4, dtype=np.uint64) * np.uint64(2) + np.uint64(1)
-        cases.append((list(c), list(rng.integers(0, 2 ** 63, 2, dtype=np.uint64) * np.uint64(2))))
-    for ctr, key in cases:
-        prev = np.array(ctr, dtype=np.uint64)
-        if prev[0] == 0:                         # borrow from word 1
-            prev[0] = np.uint64(2 ** 64 - 1)
-            prev[1] -= np.uint64(1)
-        else:
-            prev[0] -= np.uint64(1)
-        ref = np.random.Philox(counter=prev, key=np.array(key, dtype=np.uint64)).random_raw(4)
-        assert np.array_equal(o.philox4x64(ctr, key), ref), (ctr, key)
+    triples = [(0, 0, 0), (1, 0, 0), (0, 1, 0), (0, 0, 1)]
+    for _ in range(64):   # n < 2^62: the engine takes the offset 4 n in 64 bits
+        seed, sub = (int(v) for v in rng.integers(0, 2 ** 63, 2, dtype=np.uint64) * 2 + 1)
+        triples.append((seed, sub, int(rng.integers(0, 2 ** 62))))
+    ref = rocrand_philox_blocks(triples)
+    m = (1 << 32) - 1
+    for (seed, sub, n), want in zip(triples, ref):
+        ctr = [n & m, n >> 32, sub & m, sub >> 32]
+        got = o.philox4x32(ctr, [seed & m, seed >> 32])
+        assert np.array_equal(got, want), (seed, sub, n)
 
 
 def pin_gumbel_decimal(o):
     """G = -ln(-ln U) to 50 digits, with U = (2u + 1) 2^-24 from the top 23
-    bits u of numpy's Philox block: word (v >> 5) & 3 of counter
-    32 (v >> 7) + (v & 31) under key (seed, position)."""
+    bits u of rocRAND's Philox4x32-10 block: word (v >> 5) & 3 of counter
+    (32 (v >> 7) + (v & 31), 0, position lo, position hi) under key (seed lo,
+    seed hi)."""
     getcontext().prec = 50
     rng = np.random.default_rng(42)
-    for _ in range(40):
-        seed, pos, v = int(rng.integers(0, 2 ** 63)), int(rng.integers(0, 2 ** 40)), \
-            int(rng.integers(0, 200000))
-        c = 32 * (v >> 7) + (v & 31)
-        blk = np.random.Philox(counter=np.array([c - 1 if c else 2 ** 64 - 1, 0 if c else 2 ** 64 - 1,
-                                                 0 if c else 2 ** 64 - 1, 0 if c else 2 ** 64 - 1],
-                                                dtype=np.uint64),
-                               key=np.array([seed, pos], dtype=np.uint64)).random_raw(4)
-        u = int(blk[(v >> 5) & 3]) >> 41
+    cases = [(int(rng.integers(0, 2 ** 63)) * 2 + 1, int(rng.integers(0, 2 ** 40)),
+              int(rng.integers(0, 200000))) for _ in range(40)]
+    blocks = rocrand_philox_blocks([(seed, pos, 32 * (v >> 7) + (v & 31)) for seed, pos, v in cases])
+    for (seed, pos, v), blk in zip(cases, blocks):
+        u = int(blk[(v >> 5) & 3]) >> 9
         U = Decimal(2 * u + 1) / Decimal(2 ** 24)
         g = -(-(U.ln())).ln()
         assert abs(Decimal(o.gumbel(seed, pos, v)) - g) < Decimal("1e-12"), (seed, pos, v)
@@ -835,7 +850,7 @@ FAST = [
     pin_int_logits_bruteforce, pin_int_overflow_bound, pin_top2_bruteforce,
     pin_top2_hand_ties, pin_greedy_identical_rows, pin_greedy_permutation,
     pin_greedy_near_ties, pin_gated_hand_cases, pin_gated_rerank_bruteforce,
-    pin_philox_vs_numpy, pin_gumbel_decimal, pin_sample_distribution, pin_sample_limits_and_keys,
+    pin_philox_vs_rocrand, pin_gumbel_decimal, pin_sample_distribution, pin_sample_limits_and_keys,
     pin_int_scaled_values, pin_logsoftmax_sums_to_one,
     pin_logprob_closed_forms, pin_logprob_shift_invariance, pin_logprob_decimal,
     pin_logprob_out_of_range, pin_round_bf16, pin_pages_float_examples,

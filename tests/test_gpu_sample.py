@@ -7,7 +7,7 @@ import torch
 
 import synth
 from invariant_lm_head_amd import lmhead
-from tests.gpu_util import DEV, TOL, gpu, gpu_bf16, host, i8, o, tl  # noqa: F401
+from tests.gpu_util import DEV, TOL, gpu, gpu_bf16, host, i8, o, record, tl  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,10 @@ def test_sample_vs_oracle(tl, o, T):
     tok, val, gap = lmhead.sample_gumbel(tl["gx"][:B].contiguous(), tl["gw"], T, *dkeys(sd, ps))
     o_tok, o_val, o_gap = o.sample_bf16(tl["x"][:B], tl["w"], T, sd, ps)
     ex = check_draws(tok, val, gap, o_tok, o_val, o_gap, TOL / T + G_TOL)
-    print(f"T={T}: {ex} of {B} rows with a lead below the tolerance", flush=True)
+    err = float(np.max(np.abs(host(val).astype(np.float64) - o_val)))
+    record("sampling", f"tinyllama_128_rows_T{T}", {
+        "rows": B, "tokens_equal": int((host(tok) == o_tok).sum()), "exempt_rows": ex,
+        "max_value_error": err, "tolerance": TOL / T + G_TOL})
 
 
 def test_sample_int8(i8, o):
@@ -106,7 +109,8 @@ def test_sample_distribution():
         p /= p.sum()
         cnt = np.bincount(host(tok), minlength=len(z))
         stat = float(np.sum((cnt - n * p) ** 2 / (n * p)))
-        print(f"T={T}: chi2 {stat:.1f} on {len(z) - 1} dof", flush=True)
+        record("sampling", f"distribution_T{T}", {"draws": n, "chi2": stat, "dof": len(z) - 1,
+                                                   "p_value": float(chi2.sf(stat, len(z) - 1))})
         assert chi2.sf(stat, len(z) - 1) > 1e-6, (cnt, n * p)
 
 
@@ -124,8 +128,9 @@ def test_gumbel_noise_accuracy(o):
     g_hi, g_lo = val.astype(np.float64), (val - gap).astype(np.float64)
     o_hi, o_lo = o_val, o_val - o_gap
     err = max(np.max(np.abs(g_hi - o_hi)), np.max(np.abs(g_lo - o_lo)))
-    print(f"max |G_gpu - G_f64| = {err:.2e} over {2 * n} values "
-          f"(range {o_lo.min():.2f} .. {o_hi.max():.2f})", flush=True)
+    record("sampling", "gumbel_noise_accuracy", {
+        "values": 2 * n, "max_abs_error": float(err), "tolerance": G_TOL,
+        "noise_min": float(o_lo.min()), "noise_max": float(o_hi.max())})
     assert err <= G_TOL
     close = o_gap < 2 * G_TOL
     assert np.array_equal(tok[~close], o_tok[~close])

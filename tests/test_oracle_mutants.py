@@ -71,6 +71,21 @@ MUTANTS = [
     ("quantise: step rounded down",
      "mm = ((a << (-ee)) + 126) / 127;",
      "mm = (a << (-ee)) / 127;"),
+    ("Philox: key not bumped between rounds",
+     "if (r) { k0 += W0; k1 += W1; }",
+     "if (r) { k0 += 0 * W0; k1 += W1; }"),
+    ("Philox: counter words 1 and 3 swapped in the mix",
+     "uint32_t y0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0, y1 = (uint32_t)p1;",
+     "uint32_t y0 = (uint32_t)(p1 >> 32) ^ x3 ^ k0, y1 = (uint32_t)p1;"),
+    ("Gumbel: low bits of the word",
+     "const uint32_t u = out[(v >> 5) & 3] >> 9;",
+     "const uint32_t u = out[(v >> 5) & 3] & 0x7fffffu;"),
+    ("Gumbel: word of the wrong column tile",
+     "const uint32_t u = out[(v >> 5) & 3] >> 9;",
+     "const uint32_t u = out[(v >> 6) & 3] >> 9;"),
+    ("Gumbel: position in the key instead of the counter",
+     "const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};",
+     "const uint32_t key[2] = {(uint32_t)seed, (uint32_t)pos};"),
     ("row scale: exponent sign",
      "const int64_t kk = -((int64_t)sh + ue + E);",
      "const int64_t kk = -((int64_t)sh + ue - E);"),
