@@ -501,11 +501,17 @@ __device__ __forceinline__ uint32_t iexp_q30(uint64_t T) {
   const bool zero = T >= 32ull * kLn2Q24;
   const uint32_t t = zero ? 0u : (uint32_t)T;
   const uint32_t q = t / kLn2Q24, r = t - q * kLn2Q24;
+  static_assert(kNatsFrac == 24 && kLn2Q24 < (1u << 24), "r 2^8 fits 32 bits");
+  // rnd(y r, 24) = floor((y r 2^8 + 2^31) / 2^32): the high word of one
+  // 32 x 32 + 64-bit multiply-add (the same value as the 24-bit shift)
+  const uint32_t r8 = r << 8;
   uint32_t y = kTaylor.c[kExpDegree];
 #pragma unroll
   for (int n = kExpDegree - 1; n >= 0; --n)
-    y = kTaylor.c[n] - (uint32_t)(((uint64_t)y * r + (1u << (kNatsFrac - 1))) >> kNatsFrac);
-  const uint32_t e = (uint32_t)(((uint64_t)y + ((1ull << q) >> 1)) >> q);
+    y = kTaylor.c[n] - (uint32_t)(((uint64_t)y * r8 + (1ull << 31)) >> 32);
+  // y <= 2^30 (the partial sums of the alternating series stay in (0, 1]),
+  // so the rounding shift by q <= 31 stays within 32 bits
+  const uint32_t e = (y + ((1u << q) >> 1)) >> q;
   return zero ? 0u : e;
 }
 
@@ -550,9 +556,10 @@ __device__ int64_t iln_q30(uint64_t S) {
 struct IntScale {
   uint32_t m;
   int sh;
+  uint64_t half;  // 2^(sh - 1), 0 when sh = 0: the rounding term of int_nats
 };
 __device__ __forceinline__ IntScale int_row_scale(int um, int ue, int M, int E) {
-  if (um <= 0 || M <= 0) return IntScale{0u, 0};
+  if (um <= 0 || M <= 0) return IntScale{0u, 0, 0};
   const uint64_t P = (uint64_t)um * (uint64_t)M;  // < 2^62
   int sh = (64 - __clzll((long long)P)) - 31;     // bits beyond 31
   uint64_t mm;
@@ -566,13 +573,15 @@ __device__ __forceinline__ IntScale int_row_scale(int um, int ue, int M, int E) 
     mm = P << (-sh);
   }
   const int64_t k = -((int64_t)sh + ue + E);  // real = mm 2^-k
-  if (k < kNatsFrac || k > kNatsFrac + 62) return IntScale{0u, 0};
-  return IntScale{(uint32_t)mm, (int)(k - kNatsFrac)};
+  if (k < kNatsFrac || k > kNatsFrac + 62) return IntScale{0u, 0, 0};
+  const int sh2 = (int)(k - kNatsFrac);
+  return IntScale{(uint32_t)mm, sh2, sh2 > 0 ? 1ull << (sh2 - 1) : 0ull};
 }
 
 // T(d) = rnd(d m, sh): a logit difference d >= 0 in Q.24 nats
 __device__ __forceinline__ uint64_t int_nats(uint32_t d, const IntScale &s) {
-  return rnd64((uint64_t)d * s.m, s.sh);
+  // d m + 2^(sh - 1) < 2^63 + 2^61: one multiply-add, then the shift
+  return ((uint64_t)d * s.m + s.half) >> s.sh;
 }
 
 // integer softmax partial carried through the lane tree: the block max and
@@ -1348,6 +1357,24 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
       int *xmax = (int *)smem;
       uint64_t *xsum = (uint64_t *)(smem + T::WAVES_M * 32 * T::WAVES_N * 4);
       const int xbase = wm * 32;
+      // the tile's row targets and logit scales, computed once per row and
+      // staged in LDS after the exchange areas (rows past B: target -1, scale 0)
+      constexpr int TAB = (T::WAVES_M * 32 * T::WAVES_N * 12 + 15) / 16 * 16;
+      static_assert(TAB + T::BM * (int)(sizeof(IntScale) + 4) <= T::LDS, "row table");
+      IntScale *tsc = (IntScale *)(smem + TAB);
+      int *ttg = (int *)(tsc + T::BM);
+      for (int r = tid; r < T::BM; r += T::NT) {
+        const int row = m0 + r;
+        IntScale sr{0u, 0, 0};
+        int tr = -1;
+        if (row < p.B) {
+          sr = int_row_scale(p.unit_m, p.unit_e, p.step_m[row], p.step_e[row]);
+          tr = p.target[row];
+        }
+        tsc[r] = sr;
+        ttg[r] = tr;
+      }
+      __syncthreads();
       static_for<0, T::WM>([&](auto mt_) __attribute__((always_inline)) {
         constexpr int mt = decltype(mt_)::value;
         const int lbase = wm * T::WM * 32 + mt * 32;  // first local row of this m-tile
@@ -1356,9 +1383,8 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
         IntScale sc[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int row = min(m0 + lbase + acc_row(v, h), p.B - 1);  // rows past B: any scale
-          tgt[v] = m0 + lbase + acc_row(v, h) < p.B ? p.target[row] : -1;
-          sc[v] = int_row_scale(p.unit_m, p.unit_e, p.step_m[row], p.step_e[row]);
+          tgt[v] = ttg[lbase + acc_row(v, h)];
+          sc[v] = tsc[lbase + acc_row(v, h)];
         }
 #pragma unroll
         for (int nt = 0; nt < T::WN; ++nt) {
@@ -1451,6 +1477,20 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
       int *xmax = (int *)smem;
       float *xsum = (float *)(smem + T::WAVES_M * 32 * T::WAVES_N * 4);
       const int xbase = wm * 32;  // this wave row's slice of the exchange areas
+      // the tile's row targets and exp2 factors (log2(e) for bf16, s_r log2(e)
+      // for int8), staged in LDS once after the exchange areas
+      constexpr int TAB = T::WAVES_M * 32 * T::WAVES_N * (4 + 32 * 4);
+      static_assert(TAB + T::BM * 8 <= T::LDS, "row table");
+      int *ttg = (int *)(smem + TAB);
+      float *tcr = (float *)(ttg + T::BM);
+      for (int r = tid; r < T::BM; r += T::NT) {
+        const int row = m0 + r;
+        float c = kLog2e;
+        if constexpr (MODE == 1) c = ((p.scale && row < p.B) ? p.scale[row] : 1.0f) * kLog2e;
+        ttg[r] = row < p.B ? p.target[row] : -1;
+        tcr[r] = c;
+      }
+      __syncthreads();
 #pragma unroll
       for (int mt = 0; mt < T::WM; ++mt) {
         const int lbase = wm * T::WM * 32 + mt * 32;  // first local row of this m-tile
@@ -1459,10 +1499,8 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
         float cr[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int row = m0 + lbase + acc_row(v, h);
-          tgt[v] = row < p.B ? p.target[row] : -1;
-          cr[v] = kLog2e;  // log2(e) (bf16) or s_r log2(e) (int8)
-          if constexpr (MODE == 1) cr[v] = ((p.scale && row < p.B) ? p.scale[row] : 1.0f) * kLog2e;
+          tgt[v] = ttg[lbase + acc_row(v, h)];
+          cr[v] = tcr[lbase + acc_row(v, h)];
         }
         // target logit capture
 #pragma unroll
