@@ -719,12 +719,16 @@ def render_tables(results: Path) -> dict:
     t["parity"] = "\n".join(rows)
     bv = par.get("batch_variance")
     if bv:
-        rows = ["| head | compared | log-prob bits differ | max abs dlog p | ratio outside [0.9, 1.1] |",
-                "|---|---|---|---|---|"]
+        rows = ["| rows | head | compared | log-prob bits differ | max abs dlog p | "
+                "ratio outside [0.9, 1.1] |", "|---|---|---|---|---|---|"]
         for key, r in bv.items():
-            head, cmp_ = key.split(" | ")
-            rows.append(f"| {head} | {cmp_.replace('_', ' ')} | {100 * r['bits_differ']:.2f}% | "
-                        f"{r['max_abs_dlogp']:.1e} | {100 * r['ratio_out_of_band']:.2f}% |")
+            parts = key.split(" | ")
+            if len(parts) != 3:
+                continue
+            rset, head, cmp_ = parts
+            rows.append(f"| {rset} | {head} | {cmp_.replace('_', ' ')} | "
+                        f"{100 * r['bits_differ']:.2f}% | {r['max_abs_dlogp']:.1e} | "
+                        f"{100 * r['ratio_out_of_band']:.2f}% |")
         t["batch_variance"] = "\n".join(rows)
     nt_tab = nt.get("agreement_with_planted_winner")
     if nt_tab:

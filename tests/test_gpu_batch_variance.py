@@ -3,8 +3,15 @@ exp(logp_new - logp_old) of an unchanged policy leaves [0.9, 1.1] when only the
 batch shape changes; repeating the same batch is bit-exact).  Without a model:
 log p(target) of the same 512 rows scored as one batch of 512, as 64 batches of
 8 and one row at a time, by this head and by batch-variant comparators built
-from library GEMMs, and the ratio between them.  This head must give the same
-bits at every batch size; the comparators are measured and printed."""
+from library GEMMs, and the ratio between them.
+
+Two row sets: the TinyLlama-shaped head (logit std 0.9), and the same rows with
+W scaled by 3.5 (logit std 3.2, the spread of a trained model's logits).  The
+comparators with bf16 engine numerics (bf16 logits and a bf16 log-softmax, as
+an inference engine keeps them) quantise log p to 2^-3 nats at |log p| >= 16,
+so a batch-dependent rounding flip moves the ratio by 13%: at the wider spread
+they leave the band on a few percent of rows, the shape of the pages' table,
+while this head gives the same bits at every batch size."""
 import numpy as np
 import pytest
 import torch
@@ -51,14 +58,33 @@ def comparators(x, w, t):
                 for k in range(0, H, H // s))
         return torch.log_softmax(z, dim=-1).gather(1, t[r0:r1, None].long())[:, 0]
 
+    def engine_bf16(r0, r1):                   # library bf16 GEMM, bf16 log-softmax
+        z = torch.matmul(x[r0:r1], wt_bf)
+        return torch.log_softmax(z, dim=-1).gather(1, t[r0:r1, None].long())[:, 0].float()
+
+    H = x.shape[1]
+    # k slices of W, transposed and contiguous, for one and four splits
+    w_k = {s: [w[:, k:k + H // s].t().contiguous() for k in range(0, H, H // s)] for s in (1, 4)}
+
+    def split_k_bf16(r0, r1):                  # bf16 partials, split count by batch, bf16 log-softmax
+        s = 1 if r1 - r0 <= 8 else 4
+        z = None
+        for i, wk in enumerate(w_k[s]):
+            part = torch.matmul(x[r0:r1, i * (H // s):(i + 1) * (H // s)].contiguous(), wk)
+            z = part if z is None else z + part
+        return torch.log_softmax(z, dim=-1).gather(1, t[r0:r1, None].long())[:, 0].float()
+
     return {"library bf16 GEMM": lib_bf16, "library fp32 GEMM": lib_fp32,
-            "fp32 split-K by batch": split_k}
+            "fp32 split-K by batch": split_k, "bf16 engine (bf16 log-softmax)": engine_bf16,
+            "bf16 split-K by batch (bf16 log-softmax)": split_k_bf16}
 
 
-def measure(tl, n=512):
+def measure(tl, n=512, w_scale=1.0):
     """{name: {(B, 1): (changed, max|dlogp|, out-of-band)}} for this head and the
     comparators, plus the rerun control (the same batch twice)."""
     x, w = tl["gx"][:n].contiguous(), tl["gw"]
+    if w_scale != 1.0:
+        w = (w.float() * w_scale).to(torch.bfloat16).contiguous()
     t = gpu(tl["target"][:n])
 
     def ours(r0, r1):
@@ -76,16 +102,21 @@ def measure(tl, n=512):
     return res
 
 
-def test_batch_variance_demonstrator(tl):
-    res = measure(tl)
-    print(f"{'head':24s} {'compare':11s} {'bits differ':>11s} {'max|dlogp|':>11s} "
-          f"{'ratio out of [0.9,1.1]':>23s}", flush=True)
+ROW_SETS = {"tinyllama": 1.0, "tinyllama, W x 3.5": 3.5}
+
+
+@pytest.mark.parametrize("rows", list(ROW_SETS))
+def test_batch_variance_demonstrator(tl, rows):
+    res = measure(tl, w_scale=ROW_SETS[rows])
     for name, r in res.items():
         for k, (ch, mx, out) in r.items():
-            print(f"{name:24s} {k:11s} {100 * ch:10.2f}% {mx:11.2e} {100 * out:22.2f}%", flush=True)
-            record("batch_variance", f"{name} | {k}", {"bits_differ": ch, "max_abs_dlogp": mx,
-                                                        "ratio_out_of_band": out})
+            record("batch_variance", f"{rows} | {name} | {k}",
+                   {"bits_differ": ch, "max_abs_dlogp": mx, "ratio_out_of_band": out})
     for k in ("b8_vs_b1", "b512_vs_b1", "rerun"):
         assert res["this head"][k] == (0.0, 0.0, 0.0), k
     for name in res:
         assert res[name]["rerun"][0] == 0.0, name       # every head is bit-exact on a rerun
+    if ROW_SETS[rows] > 1.0:
+        # the demonstrator shows the effect: a batch-dependent split with bf16
+        # numerics leaves the band on some rows at a trained model's spread
+        assert res["bf16 split-K by batch (bf16 log-softmax)"]["b512_vs_b1"][2] > 0.0
