@@ -644,7 +644,11 @@ def render_tables(results: Path) -> dict:
             continue
         r = o[k]
         tt = f"{r['ms_per_call']:.2f} ms" if "ms_per_call" in r else f"{r['us_per_call']:.1f} us"
-        rows.append(f"| {label} | {tt} | {r['rows_per_s'] / 1e6:.3f} M | {_fmt_roof(r['roofline'])} |")
+        roof = _fmt_roof(r["roofline"])
+        if "float_logprob_us" in r:
+            roof += (f"; {100 * (r['us_per_call'] / r['float_logprob_us'] - 1):+.1f}% against the "
+                     f"float log-prob of the int8 head ({r['float_logprob_us']:.1f} us)")
+        rows.append(f"| {label} | {tt} | {r['rows_per_s'] / 1e6:.3f} M | {roof} |")
     for B in (1, 512):
         g, sm = o.get(f"gated_tau1e-3_b{B}"), o.get(f"sample_gumbel_b{B}")
         if g:
@@ -742,11 +746,30 @@ def render_tables(results: Path) -> dict:
     return t
 
 
+def render_counter_table(profile: Path) -> dict:
+    """The tile kernels' rows of the committed counter summary's derived table."""
+    if not profile.exists():
+        return {}
+    label = {"tinyllama greedy, batch 1, tile kernel": "batch 1 (32 × 128 tile)",
+             "tinyllama greedy, batch 256, tile kernel": "batch 256 (256 × 128)",
+             "tinyllama greedy, batch 512, tile kernel": "batch 512 (256 × 256)",
+             "int8 4096x128256 greedy, batch 512, tile kernel":
+                 "int8 4096 × 128256, batch 512 (256 × 256)"}
+    rows = ["| kernel | MFMA busy at 2.4 GHz | MFMA busy / active cycles | LDS active | TA busy | "
+            "TD busy |", "|---|---|---|---|---|---|"]
+    for line in profile.read_text().splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 9 and cells[0] in label:
+            rows.append(f"| {label[cells[0]]} | " + " | ".join(cells[2:7]) + " |")
+    return {"counters": "\n".join(rows)} if len(rows) > 2 else {}
+
+
 def write_tables(results: Path, docs) -> None:
     """Replace every <!-- generated:NAME --> ... <!-- /generated:NAME --> block
     of the docs with the table NAME."""
     import re
     tabs = render_tables(results)
+    tabs.update(render_counter_table(ROOT / "profiles" / "counters_greedy_tinyllama_b512.md"))
     for doc in docs:
         text = doc.read_text()
         for name, md in tabs.items():
