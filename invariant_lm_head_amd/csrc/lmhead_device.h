@@ -64,7 +64,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.693147180559945309417f;
-constexpr int kSlots = 16;  // slots of the final per-row fold
+constexpr int kSlots = 64;  // slots (lanes) of the log-prob fold per row: one wave
 constexpr int kChunk = 16;  // records per slot loaded per round of the fold
 
 template <class V> __device__ __forceinline__ V lowest_of();
@@ -495,24 +495,41 @@ __device__ __forceinline__ uint64_t rnd64(uint64_t p, int s) {  // p < 2^63, 0 <
   return s == 0 ? p : (p + ((uint64_t)1 << (s - 1))) >> s;
 }
 
-// e^(-T / 2^24) in Q.30 (T in Q.24 nats)
-__device__ __forceinline__ uint32_t iexp_q30(uint64_t T) {
-  // 2^-q with q >= 32 rounds a Q.30 value to 0 (branch-free: select at the end)
-  const bool zero = T >= 32ull * kLn2Q24;
-  const uint32_t t = zero ? 0u : (uint32_t)T;
-  const uint32_t q = t / kLn2Q24, r = t - q * kLn2Q24;
+// e^(-T[i] / 2^24) in Q.30 for N independent T (Q.24 nats), evaluated in
+// lockstep so the N Horner chains of dependent multiply-adds interleave (one
+// chain alone waits on each multiply-add's latency); each result is the same
+// as evaluated alone
+template <int N>
+__device__ __forceinline__ void iexp_q30_n(const uint64_t (&T)[N], uint32_t (&e)[N]) {
   static_assert(kNatsFrac == 24 && kLn2Q24 < (1u << 24), "r 2^8 fits 32 bits");
-  // rnd(y r, 24) = floor((y r 2^8 + 2^31) / 2^32): the high word of one
-  // 32 x 32 + 64-bit multiply-add (the same value as the 24-bit shift)
-  const uint32_t r8 = r << 8;
-  uint32_t y = kTaylor.c[kExpDegree];
+  bool zero[N];
+  uint32_t q[N], r8[N], y[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    // 2^-q with q >= 32 rounds a Q.30 value to 0 (branch-free: select at the end)
+    zero[i] = T[i] >= 32ull * kLn2Q24;
+    const uint32_t t = zero[i] ? 0u : (uint32_t)T[i];
+    q[i] = t / kLn2Q24;
+    // rnd(y r, 24) = floor((y r 2^8 + 2^31) / 2^32): the high word of one
+    // 32 x 32 + 64-bit multiply-add (the same value as the 24-bit shift)
+    r8[i] = (t - q[i] * kLn2Q24) << 8;
+    y[i] = kTaylor.c[kExpDegree];
+  }
 #pragma unroll
   for (int n = kExpDegree - 1; n >= 0; --n)
-    y = kTaylor.c[n] - (uint32_t)(((uint64_t)y * r8 + (1ull << 31)) >> 32);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      y[i] = kTaylor.c[n] - (uint32_t)(((uint64_t)y[i] * r8[i] + (1ull << 31)) >> 32);
   // y <= 2^30 (the partial sums of the alternating series stay in (0, 1]),
   // so the rounding shift by q <= 31 stays within 32 bits
-  const uint32_t e = (y + ((1u << q) >> 1)) >> q;
-  return zero ? 0u : e;
+#pragma unroll
+  for (int i = 0; i < N; ++i) e[i] = zero[i] ? 0u : (y[i] + ((1u << q[i]) >> 1)) >> q[i];
+}
+__device__ __forceinline__ uint32_t iexp_q30(uint64_t T) {
+  const uint64_t t[1] = {T};
+  uint32_t e[1];
+  iexp_q30_n<1>(t, e);
+  return e[0];
 }
 
 // floor(n / d) by restoring binary division, for a quotient below 2^31 (n <
@@ -819,7 +836,9 @@ __device__ __forceinline__ void put_top2(const Params &p, int row, const Top2 &t
   }
 }
 
-// The log-prob fold of rows row0 .. row0 + nrows - 1: kSlots threads per row.
+// The log-prob fold of rows row0 .. row0 + nrows - 1: one wave (kSlots lanes)
+// per row, so a row's records are loaded in one round up to 1024 blocks and
+// its latency is paid once, not once per 256 blocks.
 template <int MODE, int EPI>
 __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nthreads) {
   static_assert(EPI == kLse || EPI == kLseInt, "top-2 folds use lmhead_merge_top2_kernel");
@@ -830,11 +849,11 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
     const int row = row0 + g;
     const uint4 *rec = p.records + (int64_t)row * nb;
     // The row max (exact), then the sum of the rescaled block sums in slot
-    // order.  16 records per slot are in flight per round of loads (one
-    // memory latency per round).  When one round covers the row (nb <= 256),
-    // its records stay in registers for the sum; otherwise they are read
-    // again.  The row's own inputs are loaded first, so their latency
-    // overlaps the records'.
+    // order, then an xor butterfly over the slots.  kChunk records per slot
+    // are in flight per round of loads (one memory latency per round).  When
+    // one round covers the row (nb <= kChunk * kSlots), its records stay in
+    // registers for the sum; otherwise they are read again.  The row's own
+    // inputs are loaded first, so their latency overlaps the records'.
     const int tgt = p.target[row];
     const int zt = p.zt[row];  // meaningful only for a target in range
     const bool one_round = nb <= kChunk * kSlots;
@@ -848,11 +867,11 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
 #pragma unroll
         for (int q = 0; q < kChunk; ++q) mx = (int)r[q].x > mx ? (int)r[q].x : mx;
       }
-      int o;
-      o = perm<kQuadX1>(mx); mx = o > mx ? o : mx;
-      o = perm<kQuadX2>(mx); mx = o > mx ? o : mx;
-      o = perm<kHalfMirror>(mx); mx = o > mx ? o : mx;
-      o = perm<kMirror>(mx); mx = o > mx ? o : mx;
+#pragma unroll
+      for (int m = 1; m < kSlots; m <<= 1) {
+        const int o = __shfl_xor(mx, m);
+        mx = o > mx ? o : mx;
+      }
       // integer terms: the order does not matter
       uint64_t S = 0;
       for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
@@ -860,19 +879,23 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
 #pragma unroll
           for (int q = 0; q < kChunk; ++q) r[q] = rec[min(b0 + q * kSlots, nb - 1)];
         }
+        // the chunk's rescale factors in lockstep (records past nb repeat the
+        // last one and are left out of the exact sum)
+        uint64_t tq[kChunk];
+        uint32_t Rq[kChunk];
+#pragma unroll
+        for (int q = 0; q < kChunk; ++q) tq[q] = int_nats((uint32_t)mx - r[q].x, sc);
+        iexp_q30_n<kChunk>(tq, Rq);
 #pragma unroll
         for (int q = 0; q < kChunk; ++q) {
-          if (b0 + q * kSlots < nb) {
-            const uint64_t R = iexp_q30(int_nats((uint32_t)mx - r[q].x, sc));
-            // rnd(S_b R, 30) with S_b < 2^38 split at bit 32: both products fit
-            S += ((uint64_t)r[q].z * R << 2) + rnd64((uint64_t)r[q].y * R, kExpFrac);
-          }
+          const uint64_t R = Rq[q];
+          // rnd(S_b R, 30) with S_b < 2^38 split at bit 32: both products fit
+          const uint64_t term = ((uint64_t)r[q].z * R << 2) + rnd64((uint64_t)r[q].y * R, kExpFrac);
+          S += b0 + q * kSlots < nb ? term : 0ull;
         }
       }
-      S += perm64<kQuadX1>(S);
-      S += perm64<kQuadX2>(S);
-      S += perm64<kHalfMirror>(S);
-      S += perm64<kMirror>(S);
+#pragma unroll
+      for (int m = 1; m < kSlots; m <<= 1) S += __shfl_xor(S, m);
       if (slot == 0) {
         int64_t lp = INT64_MIN;
         if (tgt >= 0 && tgt < p.V && sc.m != 0u) {
@@ -900,11 +923,11 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
           mx = o > mx ? o : mx;
         }
       }
-      val_t o;
-      o = perm<kQuadX1>(mx); mx = o > mx ? o : mx;
-      o = perm<kQuadX2>(mx); mx = o > mx ? o : mx;
-      o = perm<kHalfMirror>(mx); mx = o > mx ? o : mx;
-      o = perm<kMirror>(mx); mx = o > mx ? o : mx;
+#pragma unroll
+      for (int m = 1; m < kSlots; m <<= 1) {
+        const val_t o = __shfl_xor(mx, m);
+        mx = o > mx ? o : mx;
+      }
       float s = 0.0f;
       for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
         if (!one_round) {
@@ -921,10 +944,10 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
           }
         }
       }
-      s = s + perm<kQuadX1>(s);
-      s = s + perm<kQuadX2>(s);
-      s = s + perm<kHalfMirror>(s);
-      s = s + perm<kMirror>(s);
+      // xor butterfly: s + partner is the same sum on both partners, so every
+      // lane ends with the same bits
+#pragma unroll
+      for (int m = 1; m < kSlots; m <<= 1) s = s + __shfl_xor(s, m);
       if (slot == 0) {
         float lp = __builtin_nanf("");
         if (tgt >= 0 && tgt < p.V) {
@@ -1393,8 +1416,8 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
           for (int v = 0; v < 16; ++v)
             if (col == tgt[v]) p.zt[m0 + lbase + acc_row(v, h)] = (int)acc[mt][nt][v];
         }
-#pragma unroll
-        for (int b = 0; b < T::BPW; ++b) {
+        static_for<0, T::BPW>([&](auto b_) __attribute__((always_inline)) {
+          constexpr int b = decltype(b_)::value;
           // block max (exact), in every lane
           int mx[16];
 #pragma unroll
@@ -1436,12 +1459,16 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
           for (int v = 0; v < 16; ++v) {
             uint64_t e = 0;
             if (m0 + lbase + acc_row(v, h) < p.B) {
+              uint64_t tk[T::NTB];
+              uint32_t ek[T::NTB];
+#pragma unroll
+              for (int k = 0; k < T::NTB; ++k)
+                tk[k] = int_nats((uint32_t)mx[v] - (uint32_t)acc[mt][b * T::NTB + k][v], sc[v]);
+              iexp_q30_n<T::NTB>(tk, ek);  // the lane's logits of this row value in lockstep
 #pragma unroll
               for (int k = 0; k < T::NTB; ++k) {
                 const int col = wcol0 + (b * T::NTB + k) * 32 + j;
-                const int z = acc[mt][b * T::NTB + k][v];
-                const uint32_t ek = iexp_q30(int_nats((uint32_t)mx[v] - (uint32_t)z, sc[v]));
-                e += col < p.V ? ek : 0u;
+                e += col < p.V ? ek[k] : 0u;
               }
             }
             part[v] = lse_i(mx[v], e);
@@ -1469,7 +1496,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
               put_record(&p.records[(int64_t)row * p.nblocks + blk],
                          make_uint4((unsigned)r.m, r.lo, r.hi, 0u));
           }
-        }
+        });
       });
     } else {  // kLse
       // exchange areas for one 32-row tile per wave row: block-part maxima

@@ -25,7 +25,7 @@ hipError_t launch_tile(const Params &p, hipStream_t s) {
     hipLaunchKernelGGL((lmhead_merge_top2_kernel<MODE, EPI>), dim3((p.B + 3) / 4), dim3(256), 0,
                        s, p);
   } else {
-    // 256 / kSlots rows per workgroup
+    // 256 / kSlots rows per workgroup (one wave per row)
     hipLaunchKernelGGL((lmhead_merge_kernel<MODE, EPI>),
                        dim3((p.B + 256 / kSlots - 1) / (256 / kSlots)), dim3(256), 0, s, p);
   }
