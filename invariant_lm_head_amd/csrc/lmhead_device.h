@@ -1636,7 +1636,7 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(Params p) {
 // bit (the log-prob folds keep their fixed slot order in merge_rows).
 template <int MODE, int EPI>
 __global__ __launch_bounds__(256) void lmhead_merge_top2_kernel(Params p) {
-  constexpr int kRowsPerWg = 4, kPerLane = 4;  // records per lane in flight per round
+  constexpr int kRowsPerWg = 4;
   const int row0 = blockIdx.x * kRowsPerWg;
   const int row = row0 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -1644,14 +1644,22 @@ __global__ __launch_bounds__(256) void lmhead_merge_top2_kernel(Params p) {
   if (row < p.B) {
     const uint4 *rec = p.records + (int64_t)row * nb;
     Top2 t{0, 0};
-    for (int b0 = lane; b0 < nb; b0 += 64 * kPerLane) {
-      uint4 r[kPerLane];  // all issued (a clamped index stays in bounds), then merged
+    // PER records per lane in flight per round: 4 cover rows up to 256
+    // blocks in one round, 16 rows up to 1024 blocks (fewer clamped repeats
+    // of the last record on short rows)
+    auto fold = [&](auto per_) {
+      constexpr int PER = decltype(per_)::value;
+      for (int b0 = lane; b0 < nb; b0 += 64 * PER) {
+        uint4 r[PER];  // all issued (a clamped index stays in bounds), then merged
 #pragma unroll
-      for (int q = 0; q < kPerLane; ++q) r[q] = rec[min(b0 + 64 * q, nb - 1)];
+        for (int q = 0; q < PER; ++q) r[q] = rec[min(b0 + 64 * q, nb - 1)];
 #pragma unroll
-      for (int q = 0; q < kPerLane; ++q)
-        if (b0 + 64 * q < nb) t = t2_merge(t, t2_unpack(r[q]));
-    }
+        for (int q = 0; q < PER; ++q)
+          if (b0 + 64 * q < nb) t = t2_merge(t, t2_unpack(r[q]));
+      }
+    };
+    if (nb <= 64 * 4) fold(std::integral_constant<int, 4>{});
+    else fold(std::integral_constant<int, 16>{});
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) t = t2_merge(t, Top2{__shfl_xor(t.k1, m), __shfl_xor(t.k2, m)});
     if (lane == 0) put_top2<MODE, EPI>(p, row, t);
