@@ -839,8 +839,8 @@ __device__ __forceinline__ void put_top2(const Params &p, int row, const Top2 &t
 // The log-prob fold of rows row0 .. row0 + nrows - 1: one wave (kSlots lanes)
 // per row, so a row's records are loaded in one round up to 1024 blocks and
 // its latency is paid once, not once per 256 blocks.
-template <int MODE, int EPI>
-__device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nthreads) {
+template <int MODE, int EPI, int CH>
+__device__ void merge_rows_ch(const Params &p, int row0, int nrows, int tid, int nthreads) {
   static_assert(EPI == kLse || EPI == kLseInt, "top-2 folds use lmhead_merge_top2_kernel");
   using val_t = typename Arith<MODE>::val_t;
   const int slot = tid & (kSlots - 1);
@@ -849,23 +849,23 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
     const int row = row0 + g;
     const uint4 *rec = p.records + (int64_t)row * nb;
     // The row max (exact), then the sum of the rescaled block sums in slot
-    // order, then an xor butterfly over the slots.  kChunk records per slot
+    // order, then an xor butterfly over the slots.  CH records per slot
     // are in flight per round of loads (one memory latency per round).  When
-    // one round covers the row (nb <= kChunk * kSlots), its records stay in
+    // one round covers the row (nb <= CH * kSlots), its records stay in
     // registers for the sum; otherwise they are read again.  The row's own
     // inputs are loaded first, so their latency overlaps the records'.
     const int tgt = p.target[row];
     const int zt = p.zt[row];  // meaningful only for a target in range
-    const bool one_round = nb <= kChunk * kSlots;
+    const bool one_round = nb <= CH * kSlots;
     if constexpr (EPI == kLseInt) {
       const IntScale sc = int_row_scale(p.unit_m, p.unit_e, p.step_m[row], p.step_e[row]);
-      uint4 r[kChunk];
+      uint4 r[CH];
       int mx = INT_MIN;
-      for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
+      for (int b0 = slot; b0 < nb; b0 += CH * kSlots) {
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q) r[q] = rec[min(b0 + q * kSlots, nb - 1)];
+        for (int q = 0; q < CH; ++q) r[q] = rec[min(b0 + q * kSlots, nb - 1)];
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q) mx = (int)r[q].x > mx ? (int)r[q].x : mx;
+        for (int q = 0; q < CH; ++q) mx = (int)r[q].x > mx ? (int)r[q].x : mx;
       }
 #pragma unroll
       for (int m = 1; m < kSlots; m <<= 1) {
@@ -874,20 +874,20 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
       }
       // integer terms: the order does not matter
       uint64_t S = 0;
-      for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
+      for (int b0 = slot; b0 < nb; b0 += CH * kSlots) {
         if (!one_round) {
 #pragma unroll
-          for (int q = 0; q < kChunk; ++q) r[q] = rec[min(b0 + q * kSlots, nb - 1)];
+          for (int q = 0; q < CH; ++q) r[q] = rec[min(b0 + q * kSlots, nb - 1)];
         }
         // the chunk's rescale factors in lockstep (records past nb repeat the
         // last one and are left out of the exact sum)
-        uint64_t tq[kChunk];
-        uint32_t Rq[kChunk];
+        uint64_t tq[CH];
+        uint32_t Rq[CH];
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q) tq[q] = int_nats((uint32_t)mx - r[q].x, sc);
-        iexp_q30_n<kChunk>(tq, Rq);
+        for (int q = 0; q < CH; ++q) tq[q] = int_nats((uint32_t)mx - r[q].x, sc);
+        iexp_q30_n<CH>(tq, Rq);
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q) {
+        for (int q = 0; q < CH; ++q) {
           const uint64_t R = Rq[q];
           // rnd(S_b R, 30) with S_b < 2^38 split at bit 32: both products fit
           const uint64_t term = ((uint64_t)r[q].z * R << 2) + rnd64((uint64_t)r[q].y * R, kExpFrac);
@@ -912,13 +912,13 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
         sr = p.scale ? p.scale[row] : 1.0f;
         cr = sr * kLog2e;
       }
-      uint2 r[kChunk];
+      uint2 r[CH];
       val_t mx = lowest_of<val_t>();
-      for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
+      for (int b0 = slot; b0 < nb; b0 += CH * kSlots) {
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q) r[q] = *(const uint2 *)&rec[min(b0 + q * kSlots, nb - 1)];
+        for (int q = 0; q < CH; ++q) r[q] = *(const uint2 *)&rec[min(b0 + q * kSlots, nb - 1)];
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q) {
+        for (int q = 0; q < CH; ++q) {
           const val_t o = vfrom<val_t>((int)r[q].x);  // a repeated last block cannot change a max
           mx = o > mx ? o : mx;
         }
@@ -929,13 +929,13 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
         mx = o > mx ? o : mx;
       }
       float s = 0.0f;
-      for (int b0 = slot; b0 < nb; b0 += kChunk * kSlots) {
+      for (int b0 = slot; b0 < nb; b0 += CH * kSlots) {
         if (!one_round) {
 #pragma unroll
-          for (int q = 0; q < kChunk; ++q) r[q] = *(const uint2 *)&rec[min(b0 + q * kSlots, nb - 1)];
+          for (int q = 0; q < CH; ++q) r[q] = *(const uint2 *)&rec[min(b0 + q * kSlots, nb - 1)];
         }
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q) {
+        for (int q = 0; q < CH; ++q) {
           if (b0 + q * kSlots < nb) {
             float d;
             if constexpr (MODE == 0) d = __uint_as_float(r[q].x) - mx;
@@ -963,6 +963,15 @@ __device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nt
       }
     }
   }
+}
+
+// CH records per slot in flight: 4 when one round of them covers the row
+// (up to 256 blocks), else 16.  Each slot still adds its blocks in ascending
+// order, so CH changes no bit.
+template <int MODE, int EPI>
+__device__ void merge_rows(const Params &p, int row0, int nrows, int tid, int nthreads) {
+  if (p.nblocks <= 4 * kSlots) merge_rows_ch<MODE, EPI, 4>(p, row0, nrows, tid, nthreads);
+  else merge_rows_ch<MODE, EPI, kChunk>(p, row0, nrows, tid, nthreads);
 }
 
 // one block record (read by the fold kernel after the tile launch ends)
