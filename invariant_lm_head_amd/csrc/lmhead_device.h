@@ -855,7 +855,30 @@ __device__ void merge_rows_ch(const Params &p, int row0, int nrows, int tid, int
     // registers for the sum; otherwise they are read again.  The row's own
     // inputs are loaded first, so their latency overlaps the records'.
     const int tgt = p.target[row];
-    const int zt = p.zt[row];  // meaningful only for a target in range
+    int zt;  // the target's logit bits, meaningful only for a target in range
+    if constexpr (MODE == 1) {
+      // int8 head: the target's int32 logit, exact, from 16-byte pieces of
+      // x[row] and w[target] spread over the row's lanes (every partial sum is
+      // below 2^31 in magnitude, so any order gives the same integer)
+      int dot = 0;
+      if (tgt >= 0 && tgt < p.V) {
+        const char *xr = p.x + (int64_t)row * p.rowbytes;
+        const char *wr = p.w + (int64_t)tgt * p.rowbytes;
+#pragma unroll 4
+        for (int64_t off = 16 * slot; off < p.rowbytes; off += 16 * kSlots) {
+          const int4 a = *(const int4 *)(xr + off), c = *(const int4 *)(wr + off);
+          dot = __builtin_amdgcn_sdot4(a.x, c.x, dot, false);
+          dot = __builtin_amdgcn_sdot4(a.y, c.y, dot, false);
+          dot = __builtin_amdgcn_sdot4(a.z, c.z, dot, false);
+          dot = __builtin_amdgcn_sdot4(a.w, c.w, dot, false);
+        }
+      }
+#pragma unroll
+      for (int m = 1; m < kSlots; m <<= 1) dot += __shfl_xor(dot, m);
+      zt = dot;
+    } else {
+      zt = p.zt[row];  // the float head's target logit, as its tile computed it
+    }
     const bool one_round = nb <= CH * kSlots;
     if constexpr (EPI == kLseInt) {
       const IntScale sc = int_row_scale(p.unit_m, p.unit_e, p.step_m[row], p.step_e[row]);
@@ -1389,42 +1412,26 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
       int *xmax = (int *)smem;
       uint64_t *xsum = (uint64_t *)(smem + T::WAVES_M * 32 * T::WAVES_N * 4);
       const int xbase = wm * 32;
-      // the tile's row targets and logit scales, computed once per row and
-      // staged in LDS after the exchange areas (rows past B: target -1, scale 0)
+      // the tile's row logit scales, computed once per row and staged in LDS
+      // after the exchange areas (rows past B: scale 0).  The target's logit
+      // is not captured here: the fold computes it exactly from x and w.
       constexpr int TAB = (T::WAVES_M * 32 * T::WAVES_N * 12 + 15) / 16 * 16;
-      static_assert(TAB + T::BM * (int)(sizeof(IntScale) + 4) <= T::LDS, "row table");
+      static_assert(TAB + T::BM * (int)sizeof(IntScale) <= T::LDS, "row table");
       IntScale *tsc = (IntScale *)(smem + TAB);
-      int *ttg = (int *)(tsc + T::BM);
       for (int r = tid; r < T::BM; r += T::NT) {
         const int row = m0 + r;
         IntScale sr{0u, 0, 0};
-        int tr = -1;
-        if (row < p.B) {
-          sr = int_row_scale(p.unit_m, p.unit_e, p.step_m[row], p.step_e[row]);
-          tr = p.target[row];
-        }
+        if (row < p.B) sr = int_row_scale(p.unit_m, p.unit_e, p.step_m[row], p.step_e[row]);
         tsc[r] = sr;
-        ttg[r] = tr;
       }
       __syncthreads();
       static_for<0, T::WM>([&](auto mt_) __attribute__((always_inline)) {
         constexpr int mt = decltype(mt_)::value;
         const int lbase = wm * T::WM * 32 + mt * 32;  // first local row of this m-tile
-        // per row value: target and logit scale
-        int tgt[16];
+        // per row value: logit scale
         IntScale sc[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          tgt[v] = ttg[lbase + acc_row(v, h)];
-          sc[v] = tsc[lbase + acc_row(v, h)];
-        }
-#pragma unroll
-        for (int nt = 0; nt < T::WN; ++nt) {
-          const int col = wcol0 + nt * 32 + j;
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (col == tgt[v]) p.zt[m0 + lbase + acc_row(v, h)] = (int)acc[mt][nt][v];
-        }
+        for (int v = 0; v < 16; ++v) sc[v] = tsc[lbase + acc_row(v, h)];
         static_for<0, T::BPW>([&](auto b_) __attribute__((always_inline)) {
           constexpr int b = decltype(b_)::value;
           // block max (exact), in every lane
@@ -1513,8 +1520,8 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
       int *xmax = (int *)smem;
       float *xsum = (float *)(smem + T::WAVES_M * 32 * T::WAVES_N * 4);
       const int xbase = wm * 32;  // this wave row's slice of the exchange areas
-      // the tile's row targets and exp2 factors (log2(e) for bf16, s_r log2(e)
-      // for int8), staged in LDS once after the exchange areas
+      // the tile's row targets (float head) and exp2 factors (log2(e) for
+      // bf16, s_r log2(e) for int8), staged in LDS once after the exchange areas
       constexpr int TAB = T::WAVES_M * 32 * T::WAVES_N * (4 + 32 * 4);
       static_assert(TAB + T::BM * 8 <= T::LDS, "row table");
       int *ttg = (int *)(smem + TAB);
@@ -1523,7 +1530,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
         const int row = m0 + r;
         float c = kLog2e;
         if constexpr (MODE == 1) c = ((p.scale && row < p.B) ? p.scale[row] : 1.0f) * kLog2e;
-        ttg[r] = row < p.B ? p.target[row] : -1;
+        if constexpr (MODE == 0) ttg[r] = row < p.B ? p.target[row] : -1;
         tcr[r] = c;
       }
       __syncthreads();
@@ -1535,16 +1542,19 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
         float cr[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          tgt[v] = ttg[lbase + acc_row(v, h)];
+          tgt[v] = MODE == 0 ? ttg[lbase + acc_row(v, h)] : -1;
           cr[v] = tcr[lbase + acc_row(v, h)];
         }
-        // target logit capture
+        // target logit capture (the float head; the int8 head's fold computes
+        // the exact int32 logit itself)
+        if constexpr (MODE == 0) {
 #pragma unroll
-        for (int nt = 0; nt < T::WN; ++nt) {
-          const int col = wcol0 + nt * 32 + j;
+          for (int nt = 0; nt < T::WN; ++nt) {
+            const int col = wcol0 + nt * 32 + j;
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (col == tgt[v]) p.zt[m0 + lbase + acc_row(v, h)] = vbits(acc[mt][nt][v]);
+            for (int v = 0; v < 16; ++v)
+              if (col == tgt[v]) p.zt[m0 + lbase + acc_row(v, h)] = vbits(acc[mt][nt][v]);
+          }
         }
 #pragma unroll
         for (int b = 0; b < T::BPW; ++b) {
