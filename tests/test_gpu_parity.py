@@ -192,11 +192,14 @@ def test_int8_extremes_exact(o):
 @pytest.mark.parametrize("B,H,V", [(1, 64, 2), (2, 64, 3), (5, 128, 17), (17, 64, 129),
                                    (70, 192, 130), (300, 64, 1000), (1, 4096, 257),
                                    (5, 64, 70001), (40, 128, 70001), (48, 192, 1000),
-                                   (64, 256, 1000), (5, 64, 32768), (40, 64, 32769)])
+                                   (64, 256, 1000), (5, 64, 32768), (40, 64, 32769),
+                                   (3, 64, 131072), (3, 64, 131073)])
 def test_edge_shapes(o, mode, B, H, V):
     """Degenerate and ragged shapes through every entry point against the
     oracle.  V = 32768 and 32769 (256 and 257 blocks of 128) sit on either side
-    of the log-prob fold's switch from one round of record loads to two."""
+    of the folds' switch from 4 to 16 records per lane in flight; V = 131072
+    and 131073 (1024 and 1025 blocks) on either side of their switch from one
+    round of record loads to two."""
     rng = np.random.default_rng(B * 1000 + V)
     t = rng.integers(0, V, B).astype(np.int32)
     if mode == "bf16":
