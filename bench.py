@@ -35,6 +35,7 @@ from pathlib import Path
 import numpy as np
 
 ROOT = Path(__file__).resolve().parent
+DOCS = [ROOT / "README.md", ROOT / "DESIGN.md"]  # documents with generated tables
 sys.path.insert(0, str(ROOT))
 
 HBM_PEAK = 8.0e12           # bytes/s, MI355X HBM3E
@@ -304,10 +305,11 @@ def main():
     ap.add_argument("--summarize-trace", metavar="DB",
                     help="print the per-kernel durations of a rocprofv3 --kernel-trace database")
     ap.add_argument("--write-tables", action="store_true",
-                    help="regenerate the tables of README.md and DESIGN.md from results/ (no GPU)")
+                    help="regenerate the generated tables of the repository's documents from "
+                         "results/ and profiles/ (no GPU)")
     args = ap.parse_args()
     if args.write_tables:
-        write_tables(ROOT / "results", [ROOT / "README.md", ROOT / "DESIGN.md"])
+        write_tables(ROOT / "results", DOCS)
         return
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters))

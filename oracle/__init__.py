@@ -49,7 +49,7 @@ def build(force: bool = True) -> Path:
 
 def default_threads() -> int:
     """Worker threads when none are given: OMP_NUM_THREADS if set, else the
-    online CPUs, at most 16 (a GPU machine's CPU share)."""
+    online CPUs, at most 16."""
     env = os.environ.get("OMP_NUM_THREADS", "")
     n = int(env) if env.isdigit() and int(env) > 0 else (os.cpu_count() or 1)
     return max(1, min(n, 16))

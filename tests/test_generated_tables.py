@@ -1,5 +1,5 @@
-"""The figure tables of README.md are exactly what
-`python bench.py --write-tables` renders from the committed result files
+"""The generated figure tables of the repository's documents are exactly
+what `python bench.py --write-tables` renders from the committed result files
 (results/*.json) and the committed counter summary: no table is typed by hand
 or left stale ("batch-logprob-gap", "Tables": every reported number comes from
 a result file)."""
@@ -23,9 +23,18 @@ def tables():
     return t
 
 
-@pytest.mark.parametrize("doc", ["README.md", "DESIGN.md"])
-def test_generated_blocks_match_results(tables, doc):
-    blocks = BLOCK.findall((ROOT / doc).read_text())
+@pytest.fixture(scope="module")
+def docs():
+    spec = importlib.util.spec_from_file_location("bench_docs", ROOT / "bench.py")
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    return bench.DOCS
+
+
+@pytest.mark.parametrize("i", [0, 1])
+def test_generated_blocks_match_results(tables, docs, i):
+    doc = docs[i]
+    blocks = BLOCK.findall(doc.read_text())
     assert blocks, f"{doc} has no generated tables"
     for name, body in blocks:
         assert name in tables, f"{doc}: no renderer for table {name!r}"
