@@ -17,6 +17,11 @@
  *                     Integer-Only Arithmetic", sections "What if we don't use
  *                     floats at all?" and "DetLLM": int8 x int8 -> int32
  *                     matmul; integer sums are exact in any order.)
+ *   LMHEAD_MODE_BF16_PACKED  LMHEAD_MODE_BF16 with w in the packed layout that
+ *                     lmhead_pack_w writes.  Same arithmetic, same order: every
+ *                     output has the bits it has in LMHEAD_MODE_BF16 with the
+ *                     row-major w it was packed from.  Only where W is read
+ *                     from differs; small batches run faster from it.
  *
  * Batch invariance.  Every logit is reduced over k in one order fixed by H
  * alone (one MFMA shape, one accumulator; k ascending in MODE_BF16, and in
@@ -30,7 +35,8 @@
  * split reductions chosen by batch size break batch invariance.)
  *
  * Layout.  x is [B, H] row-major, w is [V, H] row-major (each vocabulary row
- * contiguous in k).  bf16 tensors are raw 16-bit patterns.  x, w and the
+ * contiguous in k), or packed (LMHEAD_MODE_BF16_PACKED, see lmhead_pack_w).
+ * bf16 tensors are raw 16-bit patterns.  x, w and the
  * workspace must be 16-byte aligned, every other array aligned to its element
  * size.  All data pointers are DEVICE pointers owned by the caller; the
  * library never allocates, frees or synchronises, and keeps no pointer after a
@@ -70,12 +76,16 @@ typedef enum {
   LMHEAD_E_VALUE = 8      /* a scalar argument is out of range (e.g. a NaN or negative tau) */
 } lmhead_status;
 
-typedef enum { LMHEAD_MODE_BF16 = 0, LMHEAD_MODE_INT8 = 1 } lmhead_mode;
+typedef enum {
+  LMHEAD_MODE_BF16 = 0,
+  LMHEAD_MODE_INT8 = 1,
+  LMHEAD_MODE_BF16_PACKED = 2
+} lmhead_mode;
 
 /* Rounding of the logits before they are stored or ranked.  LMHEAD_ROUND_BF16
  * is the ordinary 16-bit head (float32 accumulation, then round-to-nearest-even
  * to bf16), kept to compare decisions against the float32 head; it is valid
- * only in LMHEAD_MODE_BF16.  ("Greedy Decoding Has a Precision Clause":
+ * only in the bf16 modes.  ("Greedy Decoding Has a Precision Clause":
  * BF16-output head versus the FP32-recomputed head.) */
 typedef enum { LMHEAD_ROUND_F32 = 0, LMHEAD_ROUND_BF16 = 1 } lmhead_round;
 
@@ -86,8 +96,8 @@ typedef enum { LMHEAD_ROUND_F32 = 0, LMHEAD_ROUND_BF16 = 1 } lmhead_round;
 size_t lmhead_workspace_bytes(int mode, int64_t B, int64_t H, int64_t V);
 
 /* Full logits.  logits[b, v] = sum_k x[b, k] * w[v, k], stored row-major [B, V]
- * as float32 (MODE_BF16, ROUND_F32), bf16 bits (MODE_BF16, ROUND_BF16) or int32
- * (MODE_INT8, exact).  ("Greedy Decoding Has a Precision Clause", section
+ * as float32 (the bf16 modes, ROUND_F32), bf16 bits (the bf16 modes,
+ * ROUND_BF16) or int32 (MODE_INT8, exact).  ("Greedy Decoding Has a Precision Clause", section
  * "Token-ranking margins explain why numerical error sometimes matters": the
  * lm_head turns the final representation into one score per token.) */
 lmhead_status lmhead_logits(int mode, int round, const void *x, const void *w, int64_t B,
@@ -145,8 +155,8 @@ lmhead_status lmhead_logprob(int mode, const void *x, const void *w, int64_t B, 
  * a Precision Clause", section "Correct the vulnerable token decisions, not
  * every calculation": ordinary inference decides unless the top-2 logit margin
  * is below a calibrated threshold; such steps recompute the output projection
- * in FP32, and recomputing the two leading candidates sufficed).  MODE_BF16
- * only (LMHEAD_E_MODE otherwise).
+ * in FP32, and recomputing the two leading candidates sufficed).  The bf16
+ * modes only (LMHEAD_E_MODE otherwise).
  *   1. greedy top-2 of the bf16-output head, exactly as lmhead_greedy_top2 with
  *      LMHEAD_ROUND_BF16 (ids, bf16-rounded values, margin);
  *   2. every row whose margin is below tau recomputes the logits of its two
@@ -242,6 +252,26 @@ size_t lmhead_self_check_bytes(int mode, int64_t B, int64_t H, int64_t V);
 lmhead_status lmhead_self_check(int mode, const void *x, const void *w, int64_t B, int64_t H,
                                 int64_t V, void *scratch, size_t scratch_bytes,
                                 uint64_t *mismatches, void *stream);
+
+/* The packed layout of a bf16 vocabulary matrix, for LMHEAD_MODE_BF16_PACKED.
+ * A weight is packed once and then read by every call; packing changes where
+ * each byte sits, not any value or the order of any sum.  With R = 2 H bytes
+ * per row, C = 256 if R is a multiple of 256 (else 128), and rows in groups of
+ * 128, byte k of vocabulary row v is at byte
+ *     (v / 128) * 128 R + (k / C) * 128 C + (v % 128) * C + k % C
+ * (integer division): each group is stored chunk by chunk of C bytes, and a
+ * chunk row by row, so the contraction's pipeline stages read contiguous
+ * blocks.  The layout has ceil(V / 128) * 128 rows; the rows from V on are
+ * zero.  (The pages fix the arithmetic, not the storage of the weight; this
+ * layout is this library's own.)
+ *   lmhead_packed_w_bytes  its size in bytes (0 if H or V is not valid);
+ *   lmhead_pack_w          writes it from row-major bf16 w [V, H] into
+ *                          `packed` (device, 16-byte aligned, at least
+ *                          lmhead_packed_w_bytes(H, V) bytes, not overlapping
+ *                          w), asynchronously on `stream`.
+ * Shape rules and errors as for the other calls with B = 1. */
+size_t lmhead_packed_w_bytes(int64_t H, int64_t V);
+lmhead_status lmhead_pack_w(const void *w, int64_t H, int64_t V, void *packed, void *stream);
 
 /* Text of a status code, and of the last HIP error seen by this thread. */
 const char *lmhead_status_string(int status);

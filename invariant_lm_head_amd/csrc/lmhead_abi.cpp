@@ -24,14 +24,21 @@ constexpr int64_t kMaxVocab = (int64_t)1 << 30;  // V bound
 constexpr int64_t kMaxHidden = (int64_t)1 << 20; // H bound
 constexpr int64_t kInt8MaxHidden = 131071;       // H * 128^2 < 2^31
 
-int64_t row_bytes(int mode, int64_t H) { return mode == LMHEAD_MODE_BF16 ? 2 * H : H; }
+// the kernels' arithmetic (0 float head, 1 int8 head) and W's layout of a mode
+int arith_of(int mode) { return mode == LMHEAD_MODE_INT8 ? 1 : 0; }
+bool packed_of(int mode) { return mode == LMHEAD_MODE_BF16_PACKED; }
+int64_t row_bytes(int mode, int64_t H) { return mode == LMHEAD_MODE_INT8 ? H : 2 * H; }
+lmh::Plan plan_of(int mode, int64_t B, int64_t H, int64_t V) {
+  return lmh::plan_for(arith_of(mode), B, row_bytes(mode, H), V, packed_of(mode));
+}
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 lmhead_status check_common(int mode, int round, const void *x, const void *w, int64_t B,
                            int64_t H, int64_t V) {
-  if (mode != LMHEAD_MODE_BF16 && mode != LMHEAD_MODE_INT8) return LMHEAD_E_MODE;
+  if (mode != LMHEAD_MODE_BF16 && mode != LMHEAD_MODE_INT8 && mode != LMHEAD_MODE_BF16_PACKED)
+    return LMHEAD_E_MODE;
   if (round != LMHEAD_ROUND_F32 && round != LMHEAD_ROUND_BF16) return LMHEAD_E_MODE;
   if (mode == LMHEAD_MODE_INT8 && round != LMHEAD_ROUND_F32) return LMHEAD_E_MODE;
   if (!x || !w) return LMHEAD_E_NULL;
@@ -41,7 +48,7 @@ lmhead_status check_common(int mode, int round, const void *x, const void *w, in
   if (mode == LMHEAD_MODE_INT8 && H > kInt8MaxHidden) return LMHEAD_E_OVERFLOW;
   // the tile grid is one x dimension of at most 2^32 - 1 threads (256 or 512
   // per workgroup, by plan), which bounds B x V jointly
-  const lmh::Plan pl = lmh::plan_for(mode, B, row_bytes(mode, H), V);
+  const lmh::Plan pl = plan_of(mode, B, H, V);
   if ((uint64_t)pl.grid_m * (uint64_t)pl.grid_n * (uint64_t)pl.nt > 0xFFFFFFFFull)
     return LMHEAD_E_SHAPE;
   if (!aligned16(x) || !aligned16(w)) return LMHEAD_E_ALIGN;
@@ -60,7 +67,8 @@ lmh::Params base_params(int mode, const void *x, const void *w, int64_t B, int64
   memset(&p, 0, sizeof p);
   p.x = (const char *)x;
   p.w = (const char *)w;
-  p.rowbytes = mode == LMHEAD_MODE_BF16 ? 2 * H : H;
+  p.rowbytes = row_bytes(mode, H);
+  p.w_packed = packed_of(mode) ? 1 : 0;
   p.B = (int)B;
   p.V = (int)V;
   p.nblocks = (int)((V + lmh::kBlockCols - 1) / lmh::kBlockCols);
@@ -99,11 +107,11 @@ lmhead_status lmhead_logits(int mode, int round, const void *x, const void *w, i
   if (st != LMHEAD_OK) return st;
   if (!logits) return LMHEAD_E_NULL;
   if (((uintptr_t)logits & (round == LMHEAD_ROUND_BF16 ? 1u : 3u)) != 0) return LMHEAD_E_ALIGN;
-  const lmh::Plan plan = lmh::plan_for(mode, B, row_bytes(mode, H), V);
+  const lmh::Plan plan = plan_of(mode, B, H, V);
   lmh::Params p = base_params(mode, x, w, B, H, V, plan);
   p.round_bf16 = round == LMHEAD_ROUND_BF16;
   p.logits = logits;
-  return launched(lmh::launch(mode, lmh::kStore, plan, p, (hipStream_t)stream));
+  return launched(lmh::launch(arith_of(mode), lmh::kStore, plan, p, (hipStream_t)stream));
 }
 
 static lmhead_status bind_workspace(lmh::Params &p, void *ws, size_t ws_bytes, int64_t B,
@@ -130,7 +138,7 @@ lmhead_status greedy(int mode, int round, const void *x, const void *w, int64_t 
   if (!aligned4(top_id) || !aligned4(top_val) || !aligned4(margin) ||
       (top_raw && !aligned4(top_raw)) || (row_scale && !aligned4(row_scale)))
     return LMHEAD_E_ALIGN;
-  const lmh::Plan plan = lmh::plan_for(mode, B, row_bytes(mode, H), V);
+  const lmh::Plan plan = plan_of(mode, B, H, V);
   lmh::Params p = base_params(mode, x, w, B, H, V, plan);
   st = bind_workspace(p, ws, ws_bytes, B, V);
   if (st != LMHEAD_OK) return st;
@@ -142,7 +150,7 @@ lmhead_status greedy(int mode, int round, const void *x, const void *w, int64_t 
   p.top_raw = mode == LMHEAD_MODE_INT8 ? top_raw : nullptr;
   p.tau = tau;
   p.gated = gated;
-  return launched(lmh::launch(mode, lmh::kTop2, plan, p, (hipStream_t)stream));
+  return launched(lmh::launch(arith_of(mode), lmh::kTop2, plan, p, (hipStream_t)stream));
 }
 }  // namespace
 
@@ -177,14 +185,14 @@ lmhead_status lmhead_logprob(int mode, const void *x, const void *w, int64_t B, 
   if (!target || !logprob) return LMHEAD_E_NULL;
   if (!aligned4(target) || !aligned4(logprob) || (row_scale && !aligned4(row_scale)))
     return LMHEAD_E_ALIGN;
-  const lmh::Plan plan = lmh::plan_for(mode, B, row_bytes(mode, H), V);
+  const lmh::Plan plan = plan_of(mode, B, H, V);
   lmh::Params p = base_params(mode, x, w, B, H, V, plan);
   st = bind_workspace(p, ws, ws_bytes, B, V);
   if (st != LMHEAD_OK) return st;
   p.scale = mode == LMHEAD_MODE_INT8 ? row_scale : nullptr;
   p.target = target;
   p.logprob = logprob;
-  return launched(lmh::launch(mode, lmh::kLse, plan, p, (hipStream_t)stream));
+  return launched(lmh::launch(arith_of(mode), lmh::kLse, plan, p, (hipStream_t)stream));
 }
 
 lmhead_status lmhead_quantize_rows(const int32_t *x, int64_t B, int64_t H, int8_t *q,
@@ -207,7 +215,7 @@ lmhead_status lmhead_logprob_int(const void *x, const void *w, int64_t B, int64_
       ((uintptr_t)logprob_q & 7) != 0)
     return LMHEAD_E_ALIGN;
   if (unit_m <= 0) return LMHEAD_E_VALUE;
-  const lmh::Plan plan = lmh::plan_for(mode, B, row_bytes(mode, H), V);
+  const lmh::Plan plan = plan_of(mode, B, H, V);
   lmh::Params p = base_params(mode, x, w, B, H, V, plan);
   st = bind_workspace(p, ws, ws_bytes, B, V);
   if (st != LMHEAD_OK) return st;
@@ -217,7 +225,7 @@ lmhead_status lmhead_logprob_int(const void *x, const void *w, int64_t B, int64_
   p.step_m = step_m;
   p.step_e = step_e;
   p.logprob_q = logprob_q;
-  return launched(lmh::launch(mode, lmh::kLseInt, plan, p, (hipStream_t)stream));
+  return launched(lmh::launch(arith_of(mode), lmh::kLseInt, plan, p, (hipStream_t)stream));
 }
 
 lmhead_status lmhead_greedy_gated(int mode, const void *x, const void *w, int64_t B, int64_t H,
@@ -246,7 +254,7 @@ lmhead_status lmhead_sample_gumbel(int mode, const void *x, const void *w, int64
       (row_scale && !aligned4(row_scale)))
     return LMHEAD_E_ALIGN;
   if (!(temperature > 0.0f) || !(temperature <= 3.4e38f)) return LMHEAD_E_VALUE;
-  const lmh::Plan plan = lmh::plan_for(mode, B, row_bytes(mode, H), V);
+  const lmh::Plan plan = plan_of(mode, B, H, V);
   lmh::Params p = base_params(mode, x, w, B, H, V, plan);
   st = bind_workspace(p, ws, ws_bytes, B, V);
   if (st != LMHEAD_OK) return st;
@@ -257,7 +265,7 @@ lmhead_status lmhead_sample_gumbel(int mode, const void *x, const void *w, int64
   p.token = token;
   p.value = value;
   p.gap = gap;
-  return launched(lmh::launch(mode, lmh::kSample, plan, p, (hipStream_t)stream));
+  return launched(lmh::launch(arith_of(mode), lmh::kSample, plan, p, (hipStream_t)stream));
 }
 
 // scratch: [B, V] batch logits | [V] one-row logits | [B, V] reversed-batch logits |
@@ -312,6 +320,23 @@ lmhead_status lmhead_self_check(int mode, const void *x, const void *w, int64_t 
                                            sc + off[2] + 4 * (B - 1 - r) * V, V, mm, s))))
       return st;
   return LMHEAD_OK;
+}
+
+size_t lmhead_packed_w_bytes(int64_t H, int64_t V) {
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  if (check_common(LMHEAD_MODE_BF16_PACKED, LMHEAD_ROUND_F32, dummy, dummy, 1, H, V) != LMHEAD_OK)
+    return 0;
+  return (size_t)((V + lmh::kPackRows - 1) / lmh::kPackRows) * lmh::kPackRows *
+         (size_t)row_bytes(LMHEAD_MODE_BF16_PACKED, H);
+}
+
+lmhead_status lmhead_pack_w(const void *w, int64_t H, int64_t V, void *packed, void *stream) {
+  lmhead_status st = check_common(LMHEAD_MODE_BF16_PACKED, LMHEAD_ROUND_F32, w, w, 1, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (!packed) return LMHEAD_E_NULL;
+  if (!aligned16(packed)) return LMHEAD_E_ALIGN;
+  return launched(lmh::launch_pack_w(w, packed, V, row_bytes(LMHEAD_MODE_BF16_PACKED, H),
+                                     (hipStream_t)stream));
 }
 
 const char *lmhead_status_string(int status) {

@@ -752,7 +752,14 @@ __device__ void gate_rows(const Params &p, int row0, int nrows, int tid, int nth
     const int rb = s_rows[16 * b + min(j >> 1, n - 1)];
     const int cand = p.top_id[2 * rb + (j & 1)];
     const char *xr = p.x + (int64_t)ra * p.rowbytes + 16 * h;
-    const char *wr = p.w + (int64_t)cand * p.rowbytes + 16 * h;
+    // W row `cand`: byte kb at wr + kb (row-major), or at wr + packed(kb)
+    const int lc = pack_chunk_log2(p.rowbytes);
+    const char *wr = p.w_packed ? p.w + (int64_t)(cand / kPackRows) * kPackRows * p.rowbytes +
+                                      ((int64_t)(cand % kPackRows) << lc)
+                                : p.w + (int64_t)cand * p.rowbytes;
+    auto wpos = [&](int kb) -> int64_t {
+      return p.w_packed ? ((int64_t)(kb >> lc) << (7 + lc)) + (kb & ((1 << lc) - 1)) : kb;
+    };
     f32x16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
@@ -765,7 +772,7 @@ __device__ void gate_rows(const Params &p, int row0, int nrows, int tid, int nth
 #pragma unroll
       for (int k = 0; k < GK; ++k) {
         fa[k] = *(const i32x4 *)(xr + 32 * (k0 + k));
-        fb[k] = *(const i32x4 *)(wr + 32 * (k0 + k));
+        fb[k] = *(const i32x4 *)(wr + wpos(32 * (k0 + k) + 16 * h));
       }
       __builtin_amdgcn_sched_barrier(0);  // every load issued before the first MFMA waits
 #pragma unroll
@@ -1061,9 +1068,28 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
 #pragma unroll
   for (int i = 0; i < T::SPWX_MAX; ++i)
     xoff[i] = span_offset(min(wave + i * T::NW, T::XSPANS - 1), m0, p.B - 1);
+  // the packed W layout (float head): the same bytes of the tile's rows, at
+  // their packed offsets; tiles start on a row group (BN is a multiple of 128)
+  static_assert(T::BN % kPackRows == 0, "tiles start on a packed row group");
+  const bool wpk = MODE == 0 && p.w_packed;
+  const int lc = pack_chunk_log2(p.rowbytes);
+  auto span_offset_packed = [&](int span, int first, int last) -> unsigned {
+    const int off = span * 1024 + lane * 16;
+    const int row = min(first + off / T::BKB, last) - first;
+    const int kb = 16 * (((off % T::BKB) >> 4) ^ swz<T::BKB>(off / T::BKB));
+    return (unsigned)(row / kPackRows) * (unsigned)(kPackRows * p.rowbytes) +
+           (unsigned)(((kb >> lc) << (7 + lc)) + ((row % kPackRows) << lc) + (kb & ((1 << lc) - 1)));
+  };
 #pragma unroll
-  for (int i = 0; i < T::SPWW_MAX; ++i)
-    woff[i] = span_offset(min(wave + i * T::NW, T::WSPANS - 1), n0, p.V - 1);
+  for (int i = 0; i < T::SPWW_MAX; ++i) {
+    const int span = min(wave + i * T::NW, T::WSPANS - 1);
+    woff[i] = wpk ? span_offset_packed(span, n0, p.V - 1) : span_offset(span, n0, p.V - 1);
+  }
+  // W source of stage t: the stage's first byte of the tile's first row
+  auto wkoff = [&](int stage) -> int64_t {
+    const int64_t o = koff(stage);
+    return wpk ? ((o >> lc) << (7 + lc)) + (o & ((1 << lc) - 1)) : o;
+  };
   const unsigned lds0 = lds_addr(smem);
   auto issue_x = [&](int stage, int buf) {
     const char *base = xtile + koff(stage);
@@ -1076,7 +1102,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
     }
   };
   auto issue_w = [&](int stage, int buf) {
-    const char *base = wtile + koff(stage);
+    const char *base = wtile + wkoff(stage);
 #pragma unroll
     for (int i = 0; i < T::SPWW_MAX; ++i) {
       const int span = wave + i * T::NW;
@@ -1087,7 +1113,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   };
   // W stages s and s + 1 (those below nst), span by span
   auto issue_w_pair = [&](int s) {
-    const char *base0 = wtile + koff(s), *base1 = wtile + koff(s + 1 < nst ? s + 1 : s);
+    const char *base0 = wtile + wkoff(s), *base1 = wtile + wkoff(s + 1 < nst ? s + 1 : s);
     const unsigned buf0 = lds0 + T::WRING + (s % T::NSW) * T::WSTAGE;
     const unsigned buf1 = lds0 + T::WRING + ((s + 1) % T::NSW) * T::WSTAGE;
 #pragma unroll
@@ -1186,7 +1212,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   // W spans of one boundary, PER of them after each of the first k-steps
   constexpr int PER = (T::SPWW_MAX + T::STEPS - 2) / (T::STEPS - 1);
   auto issue_w_part = [&](int stage, int buf, int i0) {
-    const char *base = wtile + koff(stage);
+    const char *base = wtile + wkoff(stage);
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int i = i0 + q;

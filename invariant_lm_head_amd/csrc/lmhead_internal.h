@@ -13,6 +13,24 @@ enum Epilogue { kStore = 0, kTop2 = 1, kLse = 2, kSample = 3, kLseInt = 4 };
 // vocabulary columns; the block grid depends on V only.
 constexpr int kBlockCols = 128;
 
+// The packed layout of a bf16 vocabulary matrix (lmhead_pack_w): rows in
+// groups of kPackRows; within a group, the row bytes cut into chunks of C bytes
+// (256 where the row length allows it, else 128), stored chunk by chunk and,
+// within a chunk, row by row.  A pipeline stage of a 128-row tile then reads
+// whole contiguous 32 KB blocks instead of 128 pieces 4 KB apart.  Rows from V
+// up to the group's end are zero.
+constexpr int kPackRows = 128;
+__host__ __device__ constexpr int pack_chunk_log2(int64_t rowbytes) {
+  return rowbytes % 256 == 0 ? 8 : 7;
+}
+// byte offset of byte kb of row `row` (row-major: row * rowbytes + kb)
+__host__ __device__ inline int64_t w_packed_offset(int64_t row, int64_t kb, int64_t rowbytes) {
+  const int lc = pack_chunk_log2(rowbytes);
+  return (row / kPackRows) * kPackRows * rowbytes + ((kb >> lc) << (7 + lc)) +
+         ((row % kPackRows) << lc) + (kb & ((1 << lc) - 1));
+}
+static_assert(kPackRows == 1 << 7, "the offsets shift by log2(kPackRows)");
+
 // m = ceil(2^63 / d) for an exact division of n < 2^31 by 1 <= d <= 2^31 with
 // a multiply-high (div_exact in lmhead_device.h)
 constexpr uint64_t div_magic(uint64_t d) { return ((uint64_t)1 << 63) / d + (((uint64_t)1 << 63) % d != 0); }
@@ -30,6 +48,7 @@ struct Params {
   uint64_t div_group; // div_magic(kTileGroup * grid_n)
   uint64_t div_units; // div_magic(rowbytes / 256) (int8 k rotation; 1 if rowbytes < 256)
   int round_bf16;     // 1: round logits to bf16 before storing / ranking
+  int w_packed;       // 1: w is in the packed layout (bf16 head; w_packed_offset)
   void *logits;       // kStore output [B, V]
   const float *scale;     // int8 per-row scale (may be null)
   const int32_t *target;  // kLse targets [B]
@@ -66,7 +85,8 @@ struct Plan {
   int grid_m, grid_n;
 };
 
-Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V);
+// mode: 0 float head, 1 int8 head; w_packed: W in the packed layout
+Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V, bool w_packed);
 
 // Size of the static device workspace of lmhead_greedy_top2_noalloc.
 constexpr size_t kStaticWorkspaceBytes = (size_t)16 << 20;
@@ -93,5 +113,7 @@ hipError_t launch_compare(const void *a, const void *b, int64_t nwords,
                           unsigned long long *mismatches, hipStream_t s);
 hipError_t launch_reverse_rows(const void *src, void *dst, int64_t rows, int64_t rowbytes,
                                hipStream_t s);
+// Row-major W [V, rowbytes] to the packed layout (ceil(V / kPackRows) groups).
+hipError_t launch_pack_w(const void *w, void *out, int64_t V, int64_t rowbytes, hipStream_t s);
 
 }  // namespace lmh

@@ -88,6 +88,25 @@ __global__ void compare_words_kernel(const unsigned *a, const unsigned *b, int64
   if ((threadIdx.x & 63) == 0 && c) atomicAdd(mismatches, c);
 }
 
+// Row-major bf16 W [V, H] to the packed layout (w_packed_offset): one
+// 16-byte piece of the output per thread and step, read from its row; rows
+// from V to the end of the last group are written as zeros.
+__global__ __launch_bounds__(256) void pack_w_kernel(const char *w, char *out, int64_t V,
+                                                     int64_t rowbytes, int64_t n16) {
+  const int lc = pack_chunk_log2(rowbytes);
+  const int64_t group = kPackRows * rowbytes;
+  for (int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; u < n16;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t o = 16 * u;
+    const int64_t g = o / group, rem = o % group;
+    const int64_t c = rem >> (7 + lc), in = rem & ((kPackRows << lc) - 1);
+    const int64_t v = g * kPackRows + (in >> lc), k = (c << lc) + (in & ((1 << lc) - 1));
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (v < V) val = *(const uint4 *)(w + v * rowbytes + k);
+    *(uint4 *)(out + o) = val;
+  }
+}
+
 __global__ void reverse_rows_kernel(const char *src, char *dst, int64_t rows, int64_t rowbytes) {
   const int64_t total = rows * rowbytes;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
@@ -99,7 +118,7 @@ __global__ void reverse_rows_kernel(const char *src, char *dst, int64_t rows, in
 
 }  // namespace
 
-Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V) {
+Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V, bool w_packed) {
   Plan pl;
   const int bkb256 = rowbytes % 256 == 0 ? 256 : rowbytes % 128 == 0 ? 128 : 64;
   const int bkb128 = rowbytes % 128 == 0 ? 128 : 64;
@@ -125,7 +144,9 @@ Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V) {
     pl.variant = 5; pl.bm = V0w<128>::BM; pl.bn = V0w<128>::BN; pl.nt = V0w<128>::NT; pl.bkb = bkb128;
   } else if (B <= 32) {
     pl.variant = 0; pl.bm = V0<256>::BM; pl.bn = V0<256>::BN; pl.nt = V0<256>::NT; pl.bkb = bkb256;
-    if (mode == 0 && rowbytes % V0d::BKB == 0) pl.bkb = V0d::BKB;
+    // 512-byte stages help a row-major W stream; from the packed layout
+    // 256-byte stages with a 3-deep ring measured 1.4-1.9 us faster (batch 1-8)
+    if (mode == 0 && !w_packed && rowbytes % V0d::BKB == 0) pl.bkb = V0d::BKB;
   } else if (B <= 64 && wide) {
     pl.variant = 6; pl.bm = V1w<128>::BM; pl.bn = V1w<128>::BN; pl.nt = V1w<128>::NT; pl.bkb = bkb128;
   } else if (B <= 64) {
@@ -206,6 +227,15 @@ hipError_t launch_compare(const void *a, const void *b, int64_t nwords,
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(compare_words_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                      (const unsigned *)a, (const unsigned *)b, nwords, mismatches);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_w(const void *w, void *out, int64_t V, int64_t rowbytes, hipStream_t s) {
+  const int64_t n16 = (V + kPackRows - 1) / kPackRows * kPackRows * rowbytes / 16;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(pack_w_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const char *)w,
+                     (char *)out, V, rowbytes, n16);
   return hipGetLastError();
 }
 

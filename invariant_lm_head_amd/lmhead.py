@@ -21,7 +21,7 @@ import torch
 
 from . import _build
 
-MODE_BF16, MODE_INT8 = 0, 1
+MODE_BF16, MODE_INT8, MODE_BF16_PACKED = 0, 1, 2
 ROUND_F32, ROUND_BF16 = 0, 1
 
 _STATUS = {0: "LMHEAD_OK", 1: "LMHEAD_E_NULL", 2: "LMHEAD_E_SHAPE", 3: "LMHEAD_E_ALIGN",
@@ -46,6 +46,8 @@ SIGNATURES = {
                             _P, _P, _SZ, _P], _I),
     "lmhead_self_check_bytes": ([_I, _I64, _I64, _I64], _SZ),
     "lmhead_self_check": ([_I, _P, _P, _I64, _I64, _I64, _P, _SZ, _P, _P], _I),
+    "lmhead_packed_w_bytes": ([_I64, _I64], _SZ),
+    "lmhead_pack_w": ([_P, _I64, _I64, _P, _P], _I),
     "lmhead_status_string": ([_I], ctypes.c_char_p),
     "lmhead_last_error": ([], ctypes.c_char_p),
     "lmhead_source_digest": ([], ctypes.c_char_p),
@@ -141,15 +143,51 @@ def _check(fn: str, status: int):
         raise LMHeadError(fn, status, library())
 
 
-def _mode_of(x: torch.Tensor, w: torch.Tensor) -> int:
+class PackedW:
+    """A bf16 vocabulary matrix [V, H] in the library's packed layout (written
+    by pack_w, read by every call in MODE_BF16_PACKED).  `data` holds the
+    packed bytes; shape, dtype and device describe the matrix it came from."""
+
+    def __init__(self, data: torch.Tensor, V: int, H: int):
+        self.data, self.shape = data, torch.Size((V, H))
+        self.dtype, self.device, self.is_cuda = torch.bfloat16, data.device, data.is_cuda
+
+    def dim(self) -> int:
+        return 2
+
+    def is_contiguous(self) -> bool:
+        return True
+
+    def data_ptr(self) -> int:
+        return self.data.data_ptr()
+
+
+def pack_w(w: torch.Tensor) -> PackedW:
+    """Pack a contiguous bf16 device matrix [V, H] once for MODE_BF16_PACKED
+    calls (lmhead_pack_w): every output keeps the bits of the row-major call."""
+    if w.dtype != torch.bfloat16 or w.dim() != 2 or not w.is_cuda or not w.is_contiguous():
+        raise ValueError("w must be a contiguous 2-D bfloat16 device tensor")
+    V, H = w.shape
+    nbytes = int(library().lmhead_packed_w_bytes(H, V))
+    if nbytes == 0:
+        raise ValueError(f"no packed layout for w of shape {tuple(w.shape)}")
+    data = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    st = library().lmhead_pack_w(_ptr(w), H, V, _ptr(data), _stream(w.device))
+    _check("lmhead_pack_w", st)
+    return PackedW(data, V, H)
+
+
+def _mode_of(x: torch.Tensor, w) -> int:
+    if x.dtype == torch.bfloat16 and isinstance(w, PackedW):
+        return MODE_BF16_PACKED
     if x.dtype == torch.bfloat16 and w.dtype == torch.bfloat16:
         return MODE_BF16
-    if x.dtype == torch.int8 and w.dtype == torch.int8:
+    if x.dtype == torch.int8 and w.dtype == torch.int8 and not isinstance(w, PackedW):
         return MODE_INT8
     raise TypeError(f"x and w must both be bfloat16 or both int8, got {x.dtype}, {w.dtype}")
 
 
-def _dims(x: torch.Tensor, w: torch.Tensor, checked: bool = True):
+def _dims(x: torch.Tensor, w, checked: bool = True):
     if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
         raise ValueError(f"x must be [B, H] and w [V, H], got {tuple(x.shape)}, {tuple(w.shape)}")
     if not (x.is_cuda and w.is_cuda and x.is_contiguous() and w.is_contiguous()):

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(lmhead.SIGNATURES)
@@ -73,9 +73,10 @@ def test_workspace_bytes_layout(lib):
         want = up(4 * B) + 16 * B * ((V + 127) // 128)
         assert lib.lmhead_workspace_bytes(0, B, H, V) == want
         assert lib.lmhead_workspace_bytes(1, B, H, V) == want
+        assert lib.lmhead_workspace_bytes(2, B, H, V) == want     # packed W: same workspace
     assert lib.lmhead_workspace_bytes(0, 0, 2048, 32000) == 0
     assert lib.lmhead_workspace_bytes(0, 1, 100, 32000) == 0
-    assert lib.lmhead_workspace_bytes(2, 1, 2048, 32000) == 0
+    assert lib.lmhead_workspace_bytes(3, 1, 2048, 32000) == 0
     # B and V each within bounds but together beyond one launch grid (2^32 threads)
     assert lib.lmhead_workspace_bytes(0, 1 << 24, 64, 151936) == 0
     assert lib.lmhead_workspace_bytes(0, 1 << 24, 64, 32000) > 0      # 2^32 - 2^24 threads: fits
@@ -88,8 +89,13 @@ def logits_status(lib, mode=0, rnd=0, x=A, w=A, B=4, H=64, V=1000, out=A2):
 
 
 def test_logits_validation(lib):
-    assert logits_status(lib, mode=2) == E_MODE
+    assert logits_status(lib, mode=3) == E_MODE
+    assert logits_status(lib, mode=-1) == E_MODE
     assert logits_status(lib, rnd=2) == E_MODE
+    assert logits_status(lib, mode=2, x=None) == E_NULL         # packed W: a bf16 mode
+    assert logits_status(lib, mode=2, rnd=1, out=None) == E_NULL
+    assert logits_status(lib, mode=2, w=MIS) == E_ALIGN
+    assert logits_status(lib, mode=2, H=96) == E_SHAPE
     assert logits_status(lib, mode=1, rnd=1) == E_MODE          # bf16 rounding needs bf16 mode
     assert logits_status(lib, x=None) == E_NULL
     assert logits_status(lib, w=None) == E_NULL
@@ -179,7 +185,8 @@ def test_sample_validation(lib):
         return lib.lmhead_sample_gumbel(mode, x, w, B, H, V, T, scale, seed, pos, tok, val, gap,
                                         ws, nws, S)
 
-    assert call(mode=2) == E_MODE
+    assert call(mode=3) == E_MODE
+    assert call(mode=2, seed=None) == E_NULL
     assert call(seed=None) == E_NULL
     assert call(pos=None) == E_NULL
     assert call(tok=None) == E_NULL
@@ -193,6 +200,26 @@ def test_sample_validation(lib):
     assert call(nws=ws_need - 1) == E_WORKSPACE
     assert call(V=1) == E_SHAPE
     assert call(mode=1, H=1 << 17) == E_OVERFLOW
+
+
+def test_packed_w_layout_size_and_validation(lib):
+    """lmhead_packed_w_bytes: ceil(V / 128) groups of 128 rows of 2H bytes; no
+    int8 bound on H (a bf16 layout).  lmhead_pack_w refuses what the other calls
+    refuse, before anything is queued."""
+    for H, V in [(2048, 32000), (64, 2), (64, 129), (4096, 151936), (131072, 1000)]:
+        assert lib.lmhead_packed_w_bytes(H, V) == (V + 127) // 128 * 128 * 2 * H, (H, V)
+    for H, V in [(100, 1000), (0, 1000), (64, 1), (64, (1 << 30) + 1), ((1 << 20) + 64, 10)]:
+        assert lib.lmhead_packed_w_bytes(H, V) == 0, (H, V)
+
+    def call(w=A, H=64, V=1000, out=A2):
+        return lib.lmhead_pack_w(w, H, V, out, S)
+
+    assert call(w=None) == E_NULL
+    assert call(out=None) == E_NULL
+    assert call(w=MIS) == E_ALIGN
+    assert call(out=MIS) == E_ALIGN
+    assert call(H=96) == E_SHAPE
+    assert call(V=1) == E_SHAPE
 
 
 def test_quantize_validation(lib):

@@ -56,3 +56,49 @@ def test_udiv_small_quotient():
         den = (2 << 30) + f
         n, d = 2 * (f << 30) + den, 2 * den
         assert udiv_small_quotient(n, d) == n // d
+
+
+# ---------------------------------------------- packed W addresses of the tile
+def swz(bkb, row):
+    if bkb == 64:
+        return (row >> 2) & 3
+    if bkb == 128:
+        return (row >> 1) & 7
+    return row & 15
+
+
+def packed_offset(v, k, R):
+    """The header's formula for byte k of row v in the packed layout."""
+    C = 256 if R % 256 == 0 else 128
+    return (v // 128) * 128 * R + (k // C) * 128 * C + (v % 128) * C + k % C
+
+
+def test_tile_packed_w_addresses():
+    """The float head's tile kernel splits each packed W address into a
+    per-lane part (fixed for the launch) and a per-stage part; emulated here
+    for every tile width, stage width and row length the float plans use, with
+    rows past V re-reading row V - 1: every lane of every stage must read the
+    byte the row-major tile reads, at its packed position."""
+    for R in (128, 384, 512, 1536, 4096):
+        lc = 8 if R % 256 == 0 else 7
+        for BN in (128, 256):
+            for BKB in (64, 128, 256, 512):
+                if R % BKB:
+                    continue
+                nst, spans = R // BKB, BN * BKB // 1024
+                for n0, V in ((0, 10 ** 6), (BN, BN + 77), (3 * BN, 3 * BN + 129)):
+                    for span in range(spans):
+                        for lane in range(64):
+                            off = span * 1024 + lane * 16
+                            row = min(n0 + off // BKB, V - 1) - n0
+                            kb = 16 * (((off % BKB) >> 4) ^ swz(BKB, off // BKB))
+                            woff = (row // 128) * (128 * R) + (((kb >> lc) << (7 + lc)) +
+                                                               ((row % 128) << lc) +
+                                                               (kb & ((1 << lc) - 1)))
+                            assert woff < 2 ** 32
+                            for s in range(nst):
+                                o = s * BKB
+                                wk = ((o >> lc) << (7 + lc)) + (o & ((1 << lc) - 1))
+                                got = n0 * R + wk + woff
+                                assert got == packed_offset(n0 + row, o + kb, R), \
+                                    (R, BN, BKB, n0, span, lane, s)
