@@ -8,7 +8,10 @@ seeded.  One step = one greedy top-2 call (float32 head, logits never
 stored) at each batch size 1, 8, 64, 256 and 512: 841 rows.  value = rows /
 second over the K timed steps.  Inputs are resident in HBM before timing; four
 copies of W (524 MB, more than the 256 MB Infinity Cache) rotate from call to
-call, so W is read from HBM, not from the cache.
+call, so W is read from HBM, not from the cache.  W is packed once, before
+timing, into the library's packed layout (lmhead_pack_w: the same bytes in
+another order, every output bit the same as with the row-major W); the
+row-major W's times are reported beside it (per_batch_row_major).
 
 Printed as ONE JSON line on stdout, with:
   roofline      the dominant call (the largest batch: its tile kernel plus the
@@ -17,6 +20,7 @@ Printed as ONE JSON line on stdout, with:
                 committed rocprofv3 counter summary (null once the kernel
                 sources differ from the ones it was taken on);
   per_batch     every batch size: us per call, rows/s, GB/s, TFLOP/s, roofline;
+  per_batch_row_major  the same calls reading the row-major W;
   cpu_baseline  the float64 CPU oracle timed on this host on a bounded sample;
   other         the other workloads (log-prob scoring at H = 4096, V = 151936;
                 int8 head at H = 4096, V = 128256; near-tie stress; full logits).
@@ -43,6 +47,7 @@ MFMA_PEAK = {"bf16": 2.5e15, "int8": 5.0e15}   # dense, per second
 METRIC = "LM-head rows/s + % of HBM/MFMA roofline, V=32000 H=2048, batch 1..512"
 SWEEP = (1, 8, 64, 256, 512)
 NCOPIES = 4
+PACKED = 2                  # LMHEAD_MODE_BF16_PACKED
 
 
 def log(*a):
@@ -343,9 +348,10 @@ def main():
     d = synth.make_inputs("tinyllama")
     x = bf16(d["x"])
     ws_ = [bf16(d["w"]) for _ in range(NCOPIES)]
+    wp_ = [lmhead.pack_w(w) for w in ws_]   # once, before anything is timed
     torch.cuda.synchronize()
 
-    callers = {B: Caller(torch, lmhead, [x[:B].contiguous()] * NCOPIES, ws_, B, H, V)
+    callers = {B: Caller(torch, lmhead, [x[:B].contiguous()] * NCOPIES, wp_, B, H, V, mode=PACKED)
                for B in SWEEP}
 
     # ---- the timed steps (whole sweep per step)
@@ -376,7 +382,7 @@ def main():
     per_batch = []
     for B in SWEEP:
         t = time_calls(torch, callers[B], 200)
-        warm = Caller(torch, lmhead, [x[:B].contiguous()], ws_[:1], B, H, V)
+        warm = Caller(torch, lmhead, [x[:B].contiguous()], wp_[:1], B, H, V, mode=PACKED)
         tw = time_calls(torch, warm, 200)
         rf = roofline(B, H, V, t)
         per_batch.append({"batch": B, "us_per_call": t * 1e6, "rows_per_s": B / t,
@@ -391,7 +397,8 @@ def main():
     rf = dict(dom["roofline"])
     traffic = traffic_from_profile(f"greedy_tinyllama_b{dom['batch']}")
     rf["traffic"] = traffic
-    rf["kernel"] = f"one greedy top-2 call at batch {dom['batch']} (tile kernel + fold kernel)"
+    rf["kernel"] = (f"one greedy top-2 call at batch {dom['batch']} (tile kernel + fold kernel), "
+                    "packed W")
 
     out = {
         "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1,
@@ -401,7 +408,8 @@ def main():
         "config": {"workload": "TinyLlama-shaped head H=2048 V=32000, fused greedy top-2 "
                                "(float32 head), one call per batch 1,8,64,256,512",
                    "H": H, "V": V, "batches": list(SWEEP), "rows_per_step": rows,
-                   "w_copies_rotated": NCOPIES, "parallelism": "single GPU"},
+                   "w_copies_rotated": NCOPIES, "w_layout": "packed once (lmhead_pack_w)",
+                   "parallelism": "single GPU"},
         "roofline": rf,
         "per_batch": per_batch,
         "source_digest": source_digest(),
@@ -409,6 +417,17 @@ def main():
 
     # ---- other workloads (reported, not in value)
     if not args.no_extras:
+        # the same sweep's calls reading the row-major W (bits identical)
+        out["per_batch_row_major"] = []
+        for B in SWEEP:
+            c = Caller(torch, lmhead, [x[:B].contiguous()] * NCOPIES, ws_, B, H, V)
+            t = time_calls(torch, c, 200)
+            rfr = roofline(B, H, V, t)
+            out["per_batch_row_major"].append({
+                "batch": B, "us_per_call": t * 1e6, "rows_per_s": B / t,
+                "roofline": {k: rfr[k] for k in ("bound", "achieved", "peak", "unit", "frac")}})
+            log(f"row-major W, B={B:4d}: {t * 1e6:8.2f} us")
+        del c, wp_
         out["other"] = extras(torch, lmhead, synth, bf16, x, ws_, d)
         out["output_digests"] = output_digests(torch, lmhead, synth, bf16, dev)
     del callers
@@ -424,7 +443,7 @@ def counters_run(torch, lmhead, synth, dev):
     """Launch sequence for the rocprofv3 --pmc runs (one counter set per run):
     3 copies of 512 MiB (read 512 MiB + write 512 MiB each: the calibration of
     the HBM byte counters), then 5 greedy top-2 calls at each batch 1, 256 and
-    512 of the H=2048, V=32000 head (four rotating W copies), then 5 greedy
+    512 of the H=2048, V=32000 head (four rotating packed W copies), then 5 greedy
     top-2 calls of the int8 head H=4096, V=128256 at batch 512."""
     src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -439,9 +458,10 @@ def counters_run(torch, lmhead, synth, dev):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
     x = bf16(d["x"])
-    w = [bf16(d["w"]) for _ in range(NCOPIES)]
+    w = [lmhead.pack_w(bf16(d["w"])) for _ in range(NCOPIES)]   # as the timed sweep reads W
+    torch.cuda.synchronize()
     for B in (1, 256, 512):
-        c = Caller(torch, lmhead, [x[:B].contiguous()] * NCOPIES, w, B, 2048, 32000)
+        c = Caller(torch, lmhead, [x[:B].contiguous()] * NCOPIES, w, B, 2048, 32000, mode=PACKED)
         for _ in range(5):
             c()
         torch.cuda.synchronize()
@@ -462,7 +482,7 @@ def counters_run(torch, lmhead, synth, dev):
 # Kernels of the launch sequence of --counters, by (template arguments, mode,
 # epilogue, threads in the grid): the workload each one belongs to.
 COUNTER_CONFIGS = [
-    ("Tile<32, 128, 1, 4, 512, 2, 2, false, false>, 0, 1>", 64000, "tinyllama greedy, batch 1, tile kernel"),
+    ("Tile<32, 128, 1, 4, 256, 2, 3, false, false>, 0, 1>", 64000, "tinyllama greedy, batch 1, tile kernel"),
     ("lmhead_merge_top2_kernel<0, 1>", 256, "tinyllama greedy, batch 1, fold kernel"),
     ("Tile<256, 128, 4, 2, 128, 2, 4, false, false>, 0, 1>", 128000, "tinyllama greedy, batch 256, tile kernel"),
     ("lmhead_merge_top2_kernel<0, 1>", 16384, "tinyllama greedy, batch 256, fold kernel"),
@@ -616,13 +636,17 @@ def render_tables(results: Path) -> dict:
     (results/bench_full.json) and the GPU tests' parity files."""
     b = json.loads((results / "bench_full.json").read_text())
     t = {}
-    rows = ["| batch | us / call (W from HBM) | rows/s | roofline | us / call (W in the Infinity Cache) |",
-            "|---|---|---|---|---|"]
+    rows = ["| batch | us / call (packed W from HBM) | rows/s | roofline | "
+            "us / call (row-major W from HBM) | us / call (packed W in the Infinity Cache) |",
+            "|---|---|---|---|---|---|"]
+    rm = {r["batch"]: r for r in b.get("per_batch_row_major", [])}
     for r in b["per_batch"]:
+        rmaj = f"{rm[r['batch']]['us_per_call']:.2f}" if r["batch"] in rm else ""
         rows.append(f"| {r['batch']} | {r['us_per_call']:.2f} | {r['rows_per_s'] / 1e6:.3f} M | "
-                    f"{_fmt_roof(r['roofline'])} | {r['us_per_call_warm_mall']:.2f} |")
+                    f"{_fmt_roof(r['roofline'])} | {rmaj} | {r['us_per_call_warm_mall']:.2f} |")
     rows.append(f"| sweep step (841 rows) | {b['ms_per_step'] * 1e3:.1f} | "
-                f"{b['value'] / 1e6:.3f} M | dominant call: {_fmt_roof(b['roofline'])} | |")
+                f"{b['value'] / 1e6:.3f} M | dominant call: {_fmt_roof(b['roofline'])} | "
+                f"{sum(r['us_per_call'] for r in rm.values()):.1f} (sum of the calls) | |")
     t["per_batch"] = "\n".join(rows)
     o = b.get("other", {})
     names = {
@@ -632,6 +656,8 @@ def render_tables(results: Path) -> dict:
         "logprob_16384x151936x4096": "log-prob scoring, 4096 x 151936, 16384 rows",
         "greedy_4096x151936_b1": "greedy, 4096 x 151936 (1.24 GB of W), batch 1",
         "greedy_4096x151936_b64": "greedy, 4096 x 151936, batch 64",
+        "greedy_4096x151936_packed_b1": "greedy, 4096 x 151936, packed W, batch 1",
+        "greedy_4096x151936_packed_b64": "greedy, 4096 x 151936, packed W, batch 64",
         "int8_b1": "int8 greedy, 4096 x 128256, batch 1",
         "int8_b8": "int8 greedy, batch 8",
         "int8_b64": "int8 greedy, batch 64",
@@ -871,7 +897,16 @@ def extras(torch, lmhead, synth, bf16, x, w_copies, d):
         res[key] = {"us_per_call": tt * 1e6, "rows_per_s": B / tt, "roofline": roofline(B, Hl, Vl, tt)}
         log(f"greedy 4096x151936 B={B}: {tt * 1e6:.1f} us, "
             f"{res[key]['roofline']['bound']} {100 * res[key]['roofline']['frac']:.1f}%")
-    del c, xl, wl_, tl
+    # the same with W packed once (lmhead_pack_w)
+    wlp = lmhead.pack_w(wl_)
+    for B in (1, 64):
+        c = Caller(torch, lmhead, [xl[:B].contiguous()], [wlp], B, Hl, Vl, mode=PACKED)
+        tt = time_calls(torch, c, 30)
+        key = f"greedy_4096x151936_packed_b{B}"
+        res[key] = {"us_per_call": tt * 1e6, "rows_per_s": B / tt, "roofline": roofline(B, Hl, Vl, tt)}
+        log(f"greedy 4096x151936 packed W B={B}: {tt * 1e6:.1f} us, "
+            f"{res[key]['roofline']['bound']} {100 * res[key]['roofline']['frac']:.1f}%")
+    del c, xl, wl_, wlp, tl
     torch.cuda.empty_cache()
 
     # int8 head, 4096 x 128256, batch 1 .. 512
