@@ -1730,6 +1730,7 @@ __global__ __launch_bounds__(256) void lmhead_merge_top2_kernel(Params p) {
 //      512-column grid fits one round of the CUs
 //   9: 128 x 256 in place of 2 when ceil(V / 256) >= 256; 10: 128 x 512 for
 //      the int8 head where 7 and 8 apply
+//   11: 1 with an unpaired W ring, for packed W
 template <int BKB> using V0w = Tile<32, 256, 1, 4, BKB, 2, 3>;
 template <int BKB> using V1w = Tile<64, 256, 2, 2, BKB, 2, 3>;
 // int8 head, large vocabularies: 512-column tiles with rings of equal depth
@@ -1752,6 +1753,12 @@ using V0d = Tile<32, 128, 1, 4, 512, 2, 2>;
 // us against 34.2-35.0 us with a 3-deep spread W ring; the same pairing in
 // V3 was 4.5 us slower at batch 256 (its loads are limited by issue, not HBM).
 template <int BKB> using V1 = Tile<64, 128, 2, 2, BKB, 2, 4, true>;
+// V1 reading packed W (float head): every stage is already a contiguous block,
+// so the W ring is spread over the k-steps, 3 deep, unpaired.  Measured on
+// MI355X (TinyLlama head, packed W from HBM): batch 33 and 64 in 27.1 us against
+// 28.7 us with the paired ring (row-major W keeps the paired ring: 30.4 against
+// 31.1 us unpaired).
+template <int BKB> using V1p = Tile<64, 128, 2, 2, BKB, 2, 3>;
 template <int BKB> using V2 = Tile<128, 128, 2, 2, BKB, 2, 4>;
 // batches 65-128 at large vocabularies (ceil(V / 256) >= 256): 256-column
 // tiles (and 512-column ones for the int8 head where their grid fits one

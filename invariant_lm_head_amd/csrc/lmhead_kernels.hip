@@ -151,6 +151,7 @@ Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V, bool w_packed) {
     pl.variant = 6; pl.bm = V1w<128>::BM; pl.bn = V1w<128>::BN; pl.nt = V1w<128>::NT; pl.bkb = bkb128;
   } else if (B <= 64) {
     pl.variant = 1; pl.bm = V1<256>::BM; pl.bn = V1<256>::BN; pl.nt = V1<256>::NT; pl.bkb = bkb256;
+    if (mode == 0 && w_packed) pl.variant = 11;  // same tile, W ring unpaired
   } else if (B <= 128 && wide512) {
     pl.variant = 10; pl.bm = V2x<128>::BM; pl.bn = V2x<128>::BN; pl.nt = V2x<128>::NT; pl.bkb = bkb128;
   } else if (B <= 128 && (V + 255) / 256 >= kCUs) {
