@@ -23,7 +23,9 @@ Printed as ONE JSON line on stdout, with:
   per_batch_row_major  the same calls reading the row-major W;
   cpu_baseline  the float64 CPU oracle timed on this host on a bounded sample;
   other         the other workloads (log-prob scoring at H = 4096, V = 151936;
-                int8 head at H = 4096, V = 128256; near-tie stress; full logits).
+                int8 head at H = 4096, V = 128256; near-tie stress; full logits);
+                the float head's read packed W like the sweep, the int8 head's
+                row-major W.
 """
 from __future__ import annotations
 
@@ -427,8 +429,9 @@ def main():
                 "batch": B, "us_per_call": t * 1e6, "rows_per_s": B / t,
                 "roofline": {k: rfr[k] for k in ("bound", "achieved", "peak", "unit", "frac")}})
             log(f"row-major W, B={B:4d}: {t * 1e6:8.2f} us")
-        del c, wp_
-        out["other"] = extras(torch, lmhead, synth, bf16, x, ws_, d)
+        del c
+        out["other"] = extras(torch, lmhead, synth, bf16, x, wp_, d)
+        del wp_
         out["output_digests"] = output_digests(torch, lmhead, synth, bf16, dev)
     del callers
     if not args.no_cpu:
@@ -654,8 +657,8 @@ def render_tables(results: Path) -> dict:
         "tinyllama_logits_b512": "float32 logits stored, 2048 x 32000, batch 512",
         "neartie_4096": "near-tie set, 2048 x 32000, 4096 rows",
         "logprob_16384x151936x4096": "log-prob scoring, 4096 x 151936, 16384 rows",
-        "greedy_4096x151936_b1": "greedy, 4096 x 151936 (1.24 GB of W), batch 1",
-        "greedy_4096x151936_b64": "greedy, 4096 x 151936, batch 64",
+        "greedy_4096x151936_b1": "greedy, 4096 x 151936 (1.24 GB of W), row-major W, batch 1",
+        "greedy_4096x151936_b64": "greedy, 4096 x 151936, row-major W, batch 64",
         "greedy_4096x151936_packed_b1": "greedy, 4096 x 151936, packed W, batch 1",
         "greedy_4096x151936_packed_b64": "greedy, 4096 x 151936, packed W, batch 64",
         "int8_b1": "int8 greedy, 4096 x 128256, batch 1",
@@ -807,16 +810,21 @@ def write_tables(results: Path, docs) -> None:
 
 
 def extras(torch, lmhead, synth, bf16, x, w_copies, d):
+    """The other workloads.  w_copies: the TinyLlama head's W copies, packed;
+    the float head's workloads read packed W like the sweep (the 4096 x 151936
+    head both ways), the int8 head row-major W."""
     H, V = 2048, 32000
+    P2 = PACKED
     res = {}
     B = 512
     t = torch.from_numpy(d["target"][:B]).to(x.device)
-    c = Caller(torch, lmhead, [x[:B].contiguous()] * NCOPIES, w_copies, B, H, V, kind="logprob",
-               target=t)
+    c = Caller(torch, lmhead, [x[:B].contiguous()] * NCOPIES, w_copies, B, H, V, mode=P2,
+               kind="logprob", target=t)
     tt = time_calls(torch, c, 100)
     res["tinyllama_logprob_b512"] = {"us_per_call": tt * 1e6, "rows_per_s": B / tt,
                                      "roofline": roofline(B, H, V, tt, out_bytes_per_row=8)}
-    c = Caller(torch, lmhead, [x[:B].contiguous()] * NCOPIES, w_copies, B, H, V, kind="logits")
+    c = Caller(torch, lmhead, [x[:B].contiguous()] * NCOPIES, w_copies, B, H, V, mode=P2,
+               kind="logits")
     tt = time_calls(torch, c, 100)
     res["tinyllama_logits_b512"] = {"us_per_call": tt * 1e6, "rows_per_s": B / tt,
                                     "roofline": roofline(B, H, V, tt, out_bytes_per_row=4 * V)}
@@ -841,8 +849,8 @@ def extras(torch, lmhead, synth, bf16, x, w_copies, d):
     # margin-gated float32 recompute (tau = 1e-3) against the plain bf16-output head
     for B in (1, 512):
         xb = [x[:B].contiguous()] * NCOPIES
-        plain = Caller(torch, lmhead, xb, w_copies, B, H, V, round_bf16=1)
-        gated = Caller(torch, lmhead, xb, w_copies, B, H, V, kind="gated", tau=1e-3)
+        plain = Caller(torch, lmhead, xb, w_copies, B, H, V, mode=P2, round_bf16=1)
+        gated = Caller(torch, lmhead, xb, w_copies, B, H, V, mode=P2, kind="gated", tau=1e-3)
         tp, tg = time_calls(torch, plain, 100), time_calls(torch, gated, 100)
         rate = float(gated.keep[3].float().mean().item())
         res[f"gated_tau1e-3_b{B}"] = {"us_per_call": tg * 1e6, "us_bf16_head": tp * 1e6,
@@ -853,8 +861,8 @@ def extras(torch, lmhead, synth, bf16, x, w_copies, d):
     # seeded Gumbel-max sampling (T = 1) against the float32 greedy head
     for B in (1, 512):
         xb = [x[:B].contiguous()] * NCOPIES
-        greedy = Caller(torch, lmhead, xb, w_copies, B, H, V)
-        samp = Caller(torch, lmhead, xb, w_copies, B, H, V, kind="sample", tau=1.0)
+        greedy = Caller(torch, lmhead, xb, w_copies, B, H, V, mode=P2)
+        samp = Caller(torch, lmhead, xb, w_copies, B, H, V, mode=P2, kind="sample", tau=1.0)
         tgr, tsa = time_calls(torch, greedy, 100), time_calls(torch, samp, 100)
         res[f"sample_gumbel_b{B}"] = {"us_per_call": tsa * 1e6, "us_greedy": tgr * 1e6,
                                       "overhead": tsa / tgr - 1.0, "rows_per_s": B / tsa}
@@ -863,12 +871,12 @@ def extras(torch, lmhead, synth, bf16, x, w_copies, d):
 
     # near-tie stress, 4096 rows
     nt = synth.make_inputs("neartie")
-    xn, wn = bf16(nt["x"]), bf16(nt["w"])
-    c = Caller(torch, lmhead, [xn], [wn], 4096, H, V)
+    xn, wn = bf16(nt["x"]), lmhead.pack_w(bf16(nt["w"]))
+    c = Caller(torch, lmhead, [xn], [wn], 4096, H, V, mode=P2)
     tt = time_calls(torch, c, 30)
     res["neartie_4096"] = {"us_per_call": tt * 1e6, "rows_per_s": 4096 / tt,
                            "roofline": roofline(4096, H, V, tt)}
-    c = Caller(torch, lmhead, [xn], [wn], 4096, H, V, kind="gated", tau=1e-3)
+    c = Caller(torch, lmhead, [xn], [wn], 4096, H, V, mode=P2, kind="gated", tau=1e-3)
     tg = time_calls(torch, c, 30)
     res["neartie_4096_gated_tau1e-3"] = {"us_per_call": tg * 1e6,
                                          "gate_rate": float(c.keep[3].float().mean().item())}
@@ -881,7 +889,8 @@ def extras(torch, lmhead, synth, bf16, x, w_copies, d):
     xl, wl_ = bf16(lp["x"]), bf16(lp["w"])
     tl = torch.from_numpy(lp["target"]).to(x.device)
     del lp
-    c = Caller(torch, lmhead, [xl], [wl_], Bl, Hl, Vl, kind="logprob", target=tl)
+    wlp = lmhead.pack_w(wl_)   # kept alive while its callers run
+    c = Caller(torch, lmhead, [xl], [wlp], Bl, Hl, Vl, mode=P2, kind="logprob", target=tl)
     tt = time_calls(torch, c, 5, warmup=1)
     res["logprob_16384x151936x4096"] = {"ms_per_call": tt * 1e3, "rows_per_s": Bl / tt,
                                         "roofline": roofline(Bl, Hl, Vl, tt, out_bytes_per_row=8),
@@ -898,7 +907,6 @@ def extras(torch, lmhead, synth, bf16, x, w_copies, d):
         log(f"greedy 4096x151936 B={B}: {tt * 1e6:.1f} us, "
             f"{res[key]['roofline']['bound']} {100 * res[key]['roofline']['frac']:.1f}%")
     # the same with W packed once (lmhead_pack_w)
-    wlp = lmhead.pack_w(wl_)
     for B in (1, 64):
         c = Caller(torch, lmhead, [xl[:B].contiguous()], [wlp], B, Hl, Vl, mode=PACKED)
         tt = time_calls(torch, c, 30)
