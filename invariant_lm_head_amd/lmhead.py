@@ -5,8 +5,8 @@ PyTorch provides device memory and the current stream.  There is no CPU or
 PyTorch fallback: if the library cannot be loaded, every call raises.
 
 Before the first call on a device the binding runs the library's device
-self-check (lmhead_self_check) in both arithmetic modes on a fixed synthetic
-batch: every row's logits alone, in the batch and in the reversed batch must
+self-check (lmhead_self_check) in both arithmetic modes, and from the packed
+bf16 layout, on a fixed synthetic batch: every row's logits alone, in the batch and in the reversed batch must
 have the same bits, or every call on that device raises SelfCheckError
 ("12 Exactness", section 12.8: a load-time self-check of the row property on
 the device).  Set LMHEAD_SELF_CHECK=0 to skip it.
@@ -100,7 +100,8 @@ class SelfCheckError(RuntimeError):
 
 
 _self_checked: dict = {}
-SELF_CHECK_SHAPES = ((MODE_BF16, 300, 128, 2000), (MODE_INT8, 300, 128, 2000))
+SELF_CHECK_SHAPES = ((MODE_BF16, 300, 128, 2000), (MODE_INT8, 300, 128, 2000),
+                     (MODE_BF16_PACKED, 300, 128, 2000))
 
 
 def self_check_enabled() -> bool:
@@ -109,9 +110,10 @@ def self_check_enabled() -> bool:
 
 
 def ensure_self_check(device) -> dict:
-    """Run the device self-check once per device (both modes, 300 rows: the
-    batch spans two 256-row tiles, each row alone runs the 32-row tile) and
-    raise SelfCheckError if any logit's bits differ.  Returns {mode:
+    """Run the device self-check once per device (both arithmetic modes and
+    the packed bf16 layout, 300 rows: the batch spans two 256-row tiles, each
+    row alone runs the 32-row tile) and raise SelfCheckError if any logit's
+    bits differ.  Returns {mode:
     mismatches} (empty when the check is switched off)."""
     dev = torch.device(device)
     key = dev.index if dev.index is not None else torch.cuda.current_device()
@@ -123,14 +125,15 @@ def ensure_self_check(device) -> dict:
         res = {}
         g = torch.Generator().manual_seed(12)
         for mode, B, H, V in SELF_CHECK_SHAPES:
-            if mode == MODE_BF16:
-                x = torch.randn((B, H), generator=g).to(torch.bfloat16)
-                w = (0.05 * torch.randn((V, H), generator=g)).to(torch.bfloat16)
-            else:
+            if mode == MODE_INT8:
                 x = torch.randint(-127, 128, (B, H), generator=g, dtype=torch.int8)
                 w = torch.randint(-127, 128, (V, H), generator=g, dtype=torch.int8)
+            else:
+                x = torch.randn((B, H), generator=g).to(torch.bfloat16)
+                w = (0.05 * torch.randn((V, H), generator=g)).to(torch.bfloat16)
             with torch.cuda.device(dev):
-                res[mode] = self_check(x.to(dev), w.to(dev))
+                wd = w.to(dev)
+                res[mode] = self_check(x.to(dev), pack_w(wd) if mode == MODE_BF16_PACKED else wd)
         _self_checked[key] = res
     if any(res.values()):
         raise SelfCheckError(f"device self-check on {dev}: logits whose bits depend on the "

@@ -342,11 +342,12 @@ def test_self_check_reports_no_mismatch(tl, i8):
 
 
 def test_load_time_self_check_ran(tl):
-    """The binding ran the device self-check in both modes before the first
-    call on this device, and found no logit whose bits depend on the batch."""
+    """The binding ran the device self-check in both modes and from the packed
+    bf16 layout before the first call on this device, and found no logit whose
+    bits depend on the batch."""
     lmhead.greedy_top2(tl["gx"][:2].contiguous(), tl["gw"])
     res = lmhead.ensure_self_check(DEV)
-    assert res == {lmhead.MODE_BF16: 0, lmhead.MODE_INT8: 0}
+    assert res == {lmhead.MODE_BF16: 0, lmhead.MODE_INT8: 0, lmhead.MODE_BF16_PACKED: 0}
 
 
 def test_bad_arguments_raise_before_launch(tl):
