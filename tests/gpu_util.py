@@ -118,7 +118,9 @@ def row_digests(z) -> list:
 
 # ------------------------------------------------------- result files
 def results_dir() -> Path:
-    d = Path(os.environ.get("LMHEAD_RESULTS_DIR", ROOT / "gpurun_out" / "results"))
+    """Where the GPU tests write their result files: results/ (the committed
+    ones), or LMHEAD_RESULTS_DIR."""
+    d = Path(os.environ.get("LMHEAD_RESULTS_DIR", ROOT / "results"))
     d.mkdir(parents=True, exist_ok=True)
     return d
 
