@@ -67,9 +67,10 @@ def _same(a, b, what):
 
 
 # (H, V): row bytes 4096 (the float head's 512-byte stages when row-major),
-# 384 (128-byte chunks), 1536, and a vocabulary wide enough for the 128 x 256
-# and 256 x 256 tiles at batches 65-128 and 129-256
-SHAPES = [(2048, 32000), (192, 1000), (768, 1000), (128, 70001)]
+# 384 (128-byte chunks), 1536, 128 (one chunk per row) with a ragged last
+# group, and a vocabulary wide enough for the 128 x 256 and 256 x 256 tiles at
+# batches 65-128 and 129-256
+SHAPES = [(2048, 32000), (192, 1000), (768, 1000), (64, 1001), (128, 70001)]
 BATCHES = [1, 7, 33, 64, 65, 129, 200, 257, 300]
 
 
