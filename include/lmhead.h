@@ -255,12 +255,13 @@ lmhead_status lmhead_self_check(int mode, const void *x, const void *w, int64_t 
 
 /* The packed layout of a bf16 vocabulary matrix, for LMHEAD_MODE_BF16_PACKED.
  * A weight is packed once and then read by every call; packing changes where
- * each byte sits, not any value or the order of any sum.  With R = 2 H bytes
- * per row, C = 256 if R is a multiple of 256 (else 128), and rows in groups of
- * 128, byte k of vocabulary row v is at byte
- *     (v / 128) * 128 R + (k / C) * 128 C + (v % 128) * C + k % C
- * (integer division): each group is stored chunk by chunk of C bytes, and a
- * chunk row by row, so the contraction's pipeline stages read contiguous
+ * each byte sits, not any value or the order of any sum.  W is cut into blocks
+ * of 128 rows x 128 bytes; each block is stored row by row (16 KB, contiguous),
+ * the blocks of a group of 128 rows one after another in k order, and the
+ * groups in order.  With R = 2 H bytes per row, byte k of vocabulary row v is
+ * at byte
+ *     (v / 128) * 128 R + (k / 128) * 16384 + (v % 128) * 128 + k % 128
+ * (integer division), so the contraction's pipeline stages read contiguous
  * blocks.  The layout has ceil(V / 128) * 128 rows; the rows from V on are
  * zero.  (The pages fix the arithmetic, not the storage of the weight; this
  * layout is this library's own.)

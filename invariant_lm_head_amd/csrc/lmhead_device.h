@@ -752,13 +752,10 @@ __device__ void gate_rows(const Params &p, int row0, int nrows, int tid, int nth
     const int rb = s_rows[16 * b + min(j >> 1, n - 1)];
     const int cand = p.top_id[2 * rb + (j & 1)];
     const char *xr = p.x + (int64_t)ra * p.rowbytes + 16 * h;
-    // W row `cand`: byte kb at wr + kb (row-major), or at wr + packed(kb)
-    const int lc = pack_chunk_log2(p.rowbytes);
-    const char *wr = p.w_packed ? p.w + (int64_t)(cand / kPackRows) * kPackRows * p.rowbytes +
-                                      ((int64_t)(cand % kPackRows) << lc)
-                                : p.w + (int64_t)cand * p.rowbytes;
-    auto wpos = [&](int kb) -> int64_t {
-      return p.w_packed ? ((int64_t)(kb >> lc) << (7 + lc)) + (kb & ((1 << lc) - 1)) : kb;
+    // byte kb of W row `cand`, row-major or packed
+    auto wat = [&](int kb) -> const char * {
+      return p.w + (p.w_packed ? w_packed_offset(cand, kb, p.rowbytes)
+                               : (int64_t)cand * p.rowbytes + kb);
     };
     f32x16 acc;
 #pragma unroll
@@ -772,7 +769,7 @@ __device__ void gate_rows(const Params &p, int row0, int nrows, int tid, int nth
 #pragma unroll
       for (int k = 0; k < GK; ++k) {
         fa[k] = *(const i32x4 *)(xr + 32 * (k0 + k));
-        fb[k] = *(const i32x4 *)(wr + wpos(32 * (k0 + k) + 16 * h));
+        fb[k] = *(const i32x4 *)wat(32 * (k0 + k) + 16 * h);
       }
       __builtin_amdgcn_sched_barrier(0);  // every load issued before the first MFMA waits
 #pragma unroll
@@ -1071,14 +1068,15 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   // the packed W layout (float head): the same bytes of the tile's rows, at
   // their packed offsets; tiles start on a row group (BN is a multiple of 128)
   static_assert(T::BN % kPackRows == 0, "tiles start on a packed row group");
+  static_assert(T::BKB % kPackBytes == 0 || kPackBytes % T::BKB == 0, "stages and blocks nest");
   const bool wpk = MODE == 0 && p.w_packed;
-  const int lc = pack_chunk_log2(p.rowbytes);
+  constexpr int kBlock = kPackRows * kPackBytes;
   auto span_offset_packed = [&](int span, int first, int last) -> unsigned {
     const int off = span * 1024 + lane * 16;
     const int row = min(first + off / T::BKB, last) - first;
     const int kb = 16 * (((off % T::BKB) >> 4) ^ swz<T::BKB>(off / T::BKB));
     return (unsigned)(row / kPackRows) * (unsigned)(kPackRows * p.rowbytes) +
-           (unsigned)(((kb >> lc) << (7 + lc)) + ((row % kPackRows) << lc) + (kb & ((1 << lc) - 1)));
+           (unsigned)((kb / kPackBytes) * kBlock + (row % kPackRows) * kPackBytes + kb % kPackBytes);
   };
 #pragma unroll
   for (int i = 0; i < T::SPWW_MAX; ++i) {
@@ -1088,7 +1086,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   // W source of stage t: the stage's first byte of the tile's first row
   auto wkoff = [&](int stage) -> int64_t {
     const int64_t o = koff(stage);
-    return wpk ? ((o >> lc) << (7 + lc)) + (o & ((1 << lc) - 1)) : o;
+    return wpk ? (o / kPackBytes) * kBlock + o % kPackBytes : o;
   };
   const unsigned lds0 = lds_addr(smem);
   auto issue_x = [&](int stage, int buf) {

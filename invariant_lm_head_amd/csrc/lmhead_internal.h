@@ -13,23 +13,18 @@ enum Epilogue { kStore = 0, kTop2 = 1, kLse = 2, kSample = 3, kLseInt = 4 };
 // vocabulary columns; the block grid depends on V only.
 constexpr int kBlockCols = 128;
 
-// The packed layout of a bf16 vocabulary matrix (lmhead_pack_w): rows in
-// groups of kPackRows; within a group, the row bytes cut into chunks of C bytes
-// (256 where the row length allows it, else 128), stored chunk by chunk and,
-// within a chunk, row by row.  A pipeline stage of a 128-row tile then reads
-// whole contiguous 32 KB blocks instead of 128 pieces 4 KB apart.  Rows from V
-// up to the group's end are zero.
-constexpr int kPackRows = 128;
-__host__ __device__ constexpr int pack_chunk_log2(int64_t rowbytes) {
-  return rowbytes % 256 == 0 ? 8 : 7;
-}
+// The packed layout of a bf16 vocabulary matrix (lmhead_pack_w): W cut into
+// blocks of kPackRows rows x kPackBytes bytes, each block contiguous (row by
+// row), the blocks of a row group in k order, row groups in order.  A pipeline
+// stage of a 128-row tile (128 bytes of each row, or a multiple) then reads
+// whole contiguous 16 KB blocks instead of 128 pieces a row apart.  Rows from
+// V up to the group's end are zero.
+constexpr int kPackRows = 128, kPackBytes = 128;
 // byte offset of byte kb of row `row` (row-major: row * rowbytes + kb)
 __host__ __device__ inline int64_t w_packed_offset(int64_t row, int64_t kb, int64_t rowbytes) {
-  const int lc = pack_chunk_log2(rowbytes);
-  return (row / kPackRows) * kPackRows * rowbytes + ((kb >> lc) << (7 + lc)) +
-         ((row % kPackRows) << lc) + (kb & ((1 << lc) - 1));
+  return (row / kPackRows) * kPackRows * rowbytes + (kb / kPackBytes) * (kPackRows * kPackBytes) +
+         (row % kPackRows) * kPackBytes + kb % kPackBytes;
 }
-static_assert(kPackRows == 1 << 7, "the offsets shift by log2(kPackRows)");
 
 // m = ceil(2^63 / d) for an exact division of n < 2^31 by 1 <= d <= 2^31 with
 // a multiply-high (div_exact in lmhead_device.h)

@@ -93,14 +93,14 @@ __global__ void compare_words_kernel(const unsigned *a, const unsigned *b, int64
 // from V to the end of the last group are written as zeros.
 __global__ __launch_bounds__(256) void pack_w_kernel(const char *w, char *out, int64_t V,
                                                      int64_t rowbytes, int64_t n16) {
-  const int lc = pack_chunk_log2(rowbytes);
+  constexpr int64_t kBlock = kPackRows * kPackBytes;  // bytes of one block
   const int64_t group = kPackRows * rowbytes;
   for (int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; u < n16;
        u += (int64_t)gridDim.x * blockDim.x) {
     const int64_t o = 16 * u;
     const int64_t g = o / group, rem = o % group;
-    const int64_t c = rem >> (7 + lc), in = rem & ((kPackRows << lc) - 1);
-    const int64_t v = g * kPackRows + (in >> lc), k = (c << lc) + (in & ((1 << lc) - 1));
+    const int64_t c = rem / kBlock, in = rem % kBlock;
+    const int64_t v = g * kPackRows + in / kPackBytes, k = c * kPackBytes + in % kPackBytes;
     uint4 val = make_uint4(0u, 0u, 0u, 0u);
     if (v < V) val = *(const uint4 *)(w + v * rowbytes + k);
     *(uint4 *)(out + o) = val;

@@ -2,7 +2,7 @@
 GPU, through the C-ABI.  Packing moves bytes and changes no arithmetic, so:
 
 - the packed bytes equal the layout's formula in the header, applied here in
-  numpy (rows past V zero), for both chunk widths (256 and 128 bytes);
+  numpy (rows past V zero);
 - every entry point with the packed W returns the bits it returns with the
   row-major W, at batch sizes that run every tile plan of the float head
   (including the gated head's float32 recompute, which reads W rows itself);
@@ -22,12 +22,12 @@ pytestmark = pytest.mark.gpu
 
 
 def packed_reference(wb: np.ndarray) -> np.ndarray:
-    """The header's formula: byte k of row v at (v / 128) 128 R + (k / C) 128 C
-    + (v % 128) C + k % C, R = 2H, C = 256 if R % 256 == 0 else 128; rows from
-    V to the end of the last group of 128 are zero."""
+    """The header's formula: byte k of row v at (v / 128) 128 R + (k / 128)
+    16384 + (v % 128) 128 + k % 128, R = 2H; rows from V to the end of the last
+    group of 128 are zero."""
     V, H = wb.shape
     R = 2 * H
-    C = 256 if R % 256 == 0 else 128
+    C = 128
     src = np.ascontiguousarray(wb, dtype=np.uint16).view(np.uint8).reshape(V, R)
     out = np.zeros((V + 127) // 128 * 128 * R, dtype=np.uint8)
     v = np.arange(V, dtype=np.int64)[:, None]
@@ -43,7 +43,8 @@ def bf16_w(rng, V, H, scale=0.1):
 
 @pytest.mark.parametrize("V,H", [(1000, 64), (130, 192), (3000, 2048), (257, 256), (2, 64)])
 def test_pack_layout(V, H):
-    """R = 128 and 384 bytes take 128-byte chunks; 4096 and 512 take 256."""
+    """Row lengths of one block (128 bytes), three (384), 32 (4096) and four
+    (512), and ragged last groups."""
     rng = np.random.default_rng(V + H)
     wb = bf16_w(rng, V, H)
     pw = lmhead.pack_w(gpu_bf16(wb))
@@ -67,7 +68,7 @@ def _same(a, b, what):
 
 
 # (H, V): row bytes 4096 (the float head's 512-byte stages when row-major),
-# 384 (128-byte chunks), 1536, 128 (one chunk per row) with a ragged last
+# 384 (128-byte stages), 1536, 128 (one block per row) with a ragged last
 # group, and a vocabulary wide enough for the 128 x 256 and 256 x 256 tiles at
 # batches 65-128 and 129-256
 SHAPES = [(2048, 32000), (192, 1000), (768, 1000), (64, 1001), (128, 70001)]

@@ -69,8 +69,7 @@ def swz(bkb, row):
 
 def packed_offset(v, k, R):
     """The header's formula for byte k of row v in the packed layout."""
-    C = 256 if R % 256 == 0 else 128
-    return (v // 128) * 128 * R + (k // C) * 128 * C + (v % 128) * C + k % C
+    return (v // 128) * 128 * R + (k // 128) * 16384 + (v % 128) * 128 + k % 128
 
 
 def test_tile_packed_w_addresses():
@@ -80,7 +79,6 @@ def test_tile_packed_w_addresses():
     rows past V re-reading row V - 1: every lane of every stage must read the
     byte the row-major tile reads, at its packed position."""
     for R in (128, 384, 512, 1536, 4096):
-        lc = 8 if R % 256 == 0 else 7
         for BN in (128, 256):
             for BKB in (64, 128, 256, 512):
                 if R % BKB:
@@ -92,13 +90,12 @@ def test_tile_packed_w_addresses():
                             off = span * 1024 + lane * 16
                             row = min(n0 + off // BKB, V - 1) - n0
                             kb = 16 * (((off % BKB) >> 4) ^ swz(BKB, off // BKB))
-                            woff = (row // 128) * (128 * R) + (((kb >> lc) << (7 + lc)) +
-                                                               ((row % 128) << lc) +
-                                                               (kb & ((1 << lc) - 1)))
+                            woff = (row // 128) * (128 * R) + ((kb // 128) * 16384 +
+                                                               (row % 128) * 128 + kb % 128)
                             assert woff < 2 ** 32
                             for s in range(nst):
                                 o = s * BKB
-                                wk = ((o >> lc) << (7 + lc)) + (o & ((1 << lc) - 1))
+                                wk = (o // 128) * 16384 + o % 128
                                 got = n0 * R + wk + woff
                                 assert got == packed_offset(n0 + row, o + kb, R), \
                                     (R, BN, BKB, n0, span, lane, s)
