@@ -652,6 +652,39 @@ def render_tables(results: Path) -> dict:
                 f"{sum(r['us_per_call'] for r in rm.values()):.1f} (sum of the calls) | |")
     t["per_batch"] = "\n".join(rows)
     o = b.get("other", {})
+    # the performance targets of this head on MI355X (70% of the HBM roofline
+    # where W's stream bounds a call, 50% of MFMA peak at large batches)
+    # against this run
+    pb = {r["batch"]: r for r in b["per_batch"]}
+    rows = ["| workload | target | measured | met |", "|---|---|---|---|"]
+
+    def tgt(label, want, got, ok):
+        rows.append(f"| {label} | {want} | {got} | {'yes' if ok else 'no'} |")
+
+    if 1 in pb:
+        u = pb[1]["us_per_call"]
+        tgt("greedy 2048 x 32000, batch 1", "<= 23.4 us (70% of HBM)",
+            f"{u:.2f} us ({_fmt_roof(pb[1]['roofline'])})", u <= 23.4)
+    for B, lim in ((256, 26.7), (512, 53.3)):
+        if B in pb:
+            u = pb[B]["us_per_call"]
+            tgt(f"greedy 2048 x 32000, batch {B}", f"<= {lim} us (50% of MFMA)",
+                f"{u:.2f} us ({100 * 2 * B * 32000 * 2048 / (u * 1e-6) / 2.5e15:.1f}% of MFMA)",
+                u <= lim)
+    if "logprob_16384x151936x4096" in o:
+        r = o["logprob_16384x151936x4096"]
+        tgt("log-prob scoring 4096 x 151936, 16384 rows", "<= 16.2 ms (50% of MFMA)",
+            f"{r['ms_per_call']:.2f} ms ({_fmt_roof(r['roofline'])})", r["ms_per_call"] <= 16.2)
+    if "int8_b1" in o:
+        r = o["int8_b1"]
+        tgt("int8 greedy 4096 x 128256, batch 1", "<= 93.8 us (70% of HBM)",
+            f"{r['us_per_call']:.1f} us ({_fmt_roof(r['roofline'])})", r["us_per_call"] <= 93.8)
+    if "int8_b512" in o:
+        r = o["int8_b512"]
+        tgt("int8 greedy 4096 x 128256, batch 512", ">= 2.4 M rows/s (50% of MFMA)",
+            f"{r['rows_per_s'] / 1e6:.2f} M rows/s ({_fmt_roof(r['roofline'])})",
+            r["rows_per_s"] >= 2.4e6)
+    t["targets"] = "\n".join(rows)
     names = {
         "tinyllama_logprob_b512": "log-prob, 2048 x 32000, batch 512",
         "tinyllama_logits_b512": "float32 logits stored, 2048 x 32000, batch 512",
