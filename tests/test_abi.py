@@ -307,3 +307,22 @@ def test_self_check_switch(monkeypatch):
         assert lmhead.self_check_enabled() is on
     monkeypatch.delenv("LMHEAD_SELF_CHECK")
     assert lmhead.self_check_enabled()
+
+
+def test_abi_from_plain_c(tmp_path):
+    """tests/abi_c_check.c, built as C99 with gcc against the library: the
+    header is valid C and the validation paths answer from C (no GPU)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    root = HEADER.parents[1]
+    exe = tmp_path / "abi_c_check"
+    lib_dir = _build.LIBRARY.parent
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    f"-I{root / 'include'}", str(root / "tests" / "abi_c_check.c"),
+                    f"-L{lib_dir}", "-llmhead", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)],
+                   check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
