@@ -1389,6 +1389,40 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
 #pragma unroll
           for (int b = 0; b < T::BPW; ++b) {
             const int col0 = wcol0 + b * T::NTB * 32 + j;  // this lane's first column of the block
+            if (p.B - m0 == 1) {
+              // one live row in the tile (batch 1, or a last row tile of one
+              // row): its row 0, value 0 of the lanes with h = 0 in the first
+              // 32-row tile of wave row 0.  Only that row is ranked, by a
+              // butterfly over the 32 column lanes; the pairings j^16, j^15,
+              // j^7, j^2, j^1 are independent bit masks, so every lane ends
+              // with the exact top-2 of all 32 (the same keys the
+              // reduce-scatter below would merge)
+              if (wm == 0 && mt == 0) {
+                val_t z[T::NTB];
+#pragma unroll
+                for (int k = 0; k < T::NTB; ++k) {
+                  val_t zz = acc[mt][b * T::NTB + k][0];
+                  if constexpr (MODE == 0 && decltype(round)::value) zz = bf16_round(zz);
+                  z[k] = col0 + 32 * k < p.V ? zz : lowest_of<val_t>();
+                }
+                Top2 r = lane_top2<T::NTB>(z, ~(unsigned)col0);
+                r = combine(r, perm<kX16>(r));
+                r = combine(r, perm<kMirror>(r));
+                r = combine(r, perm<kHalfMirror>(r));
+                r = combine(r, perm<kQuadX2>(r));
+                r = combine(r, perm<kQuadX1>(r));
+                if (lane == 0) {
+                  if constexpr (T::PARTS == 1) {
+                    const int blk = wcol0 / kBlockCols + b;
+                    if (blk < p.nblocks)
+                      put_record(&p.records[(int64_t)m0 * p.nblocks + blk], t2_pack(r));
+                  } else {
+                    xch[wn] = t2_pack(r);  // row 0 of the exchange
+                  }
+                }
+              }
+              continue;
+            }
             Top2 t[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
