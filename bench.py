@@ -784,6 +784,10 @@ def render_tables(results: Path) -> dict:
     if "logits_batches_1_to_512" in inv:
         rows.append(f"| bitwise invariance: logits, top-2, log-prob at every batch 1..512 | "
                     f"{inv['logits_batches_1_to_512']['rows_compared']} rows x 32000 logits | identical |")
+    if "packed_greedy_batches_1_to_512" in inv:
+        rows.append(f"| bitwise invariance, packed W: top-2 at every batch 1..512 against the "
+                    f"row-major batch-512 call, both rankings | "
+                    f"{inv['packed_greedy_batches_1_to_512']['rows_compared']} rows x 2 | identical |")
     t["parity"] = "\n".join(rows)
     bv = par.get("batch_variance")
     if bv:

@@ -43,6 +43,21 @@ def test_greedy_and_logprob_bits_equal_for_every_batch_size(tl):
     record("invariance", "greedy_logprob_batches_1_to_512", {"batches": len(SIZES) + 1})
 
 
+def test_packed_w_greedy_bits_equal_for_every_batch_size(tl):
+    """The packed W layout (lmhead_pack_w), batches 1..512, against the
+    row-major batch-512 call: top-2 ids, values and margin, bit for bit, with
+    both rankings (float32 logits and the bf16-output head)."""
+    pw = lmhead.pack_w(tl["gw"])
+    for round_bf16 in (False, True):
+        g512 = lmhead.greedy_top2(tl["gx"], tl["gw"], round_bf16=round_bf16)
+        for B in SIZES + [512]:
+            g = lmhead.greedy_top2(tl["gx"][:B].contiguous(), pw, round_bf16=round_bf16)
+            for a, b in zip(g[:3], g512[:3]):
+                assert torch.equal(bits(a), bits(b[:B])), (B, round_bf16)
+    record("invariance", "packed_greedy_batches_1_to_512", {"batches": len(SIZES) + 1,
+                                                            "rows_compared": sum(SIZES) + 512})
+
+
 def test_row_position_and_neighbours_do_not_matter(tl):
     """A permuted batch (every row at another position with other neighbours)
     and one row repeated B times give the same bits per row."""
