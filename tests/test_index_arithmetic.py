@@ -99,3 +99,41 @@ def test_tile_packed_w_addresses():
                                 got = n0 * R + wk + woff
                                 assert got == packed_offset(n0 + row, o + kb, R), \
                                     (R, BN, BKB, n0, span, lane, s)
+
+
+# ------------------------------------------------- workgroup -> tile mapping
+K_TILE_GROUP = 8  # row tiles walked per vocabulary tile
+
+
+def tile_of(bid, G, grid_m, grid_n, w_packed):
+    """The tile kernel's map from workgroup id to (row tile, vocabulary tile),
+    with its multiply-high divisions."""
+    per = G >> 3
+    if grid_m == 1 and w_packed:
+        nb = bid
+    elif bid < (per << 3):
+        nb = (bid & 7) * per + (bid >> 3)
+    else:
+        nb = bid
+    in_group = K_TILE_GROUP * grid_n
+    group = div_exact(nb, div_magic(in_group))
+    first_m = group * K_TILE_GROUP
+    gsz = min(grid_m - first_m, K_TILE_GROUP)
+    rem = nb - group * in_group
+    tn = div_exact(rem, div_magic(gsz))
+    return first_m + (rem - tn * gsz), tn
+
+
+def test_tile_map_is_a_bijection():
+    """Every grid the plans launch (any row tile count, vocabulary tile counts
+    around the multiples of 8, both W layouts): each tile is computed by
+    exactly one workgroup."""
+    grid_ns = sorted({1, 2, 7, 8, 9, 63, 125, 126, 250, 251, 256, 257, 501, 1002} |
+                     {8 * k + r for k in (15, 31) for r in range(8)})
+    for grid_m in (1, 2, 3, 7, 8, 9, 16, 17):
+        for grid_n in grid_ns:
+            G = grid_m * grid_n
+            for w_packed in (False, True):
+                tiles = {tile_of(b, G, grid_m, grid_n, w_packed) for b in range(G)}
+                assert len(tiles) == G, (grid_m, grid_n, w_packed)
+                assert all(0 <= tm < grid_m and 0 <= tn < grid_n for tm, tn in tiles)
