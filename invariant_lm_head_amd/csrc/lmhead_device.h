@@ -1021,16 +1021,17 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   // ---- workgroup -> tile, XCD-aware: consecutive workgroups are dealt to the 8
   // XCDs in turn, so renumber them XCD-major, then walk GROUP_M row tiles per
   // vocabulary tile so neighbours on one XCD share X and W tiles in its L2.
-  // A grid of one row tile shares no W tile; from the packed layout it keeps
-  // the plain order (workgroup b, vocabulary tile b), which streamed W
-  // 0.2-0.65 us faster per call at batches 1-128 (row-major W: the XCD-major
-  // order, 0.03-0.45 us faster).
+  // A grid of one row tile of up to 128 rows shares no W tile; from the
+  // packed layout it keeps the plain order (workgroup b, vocabulary tile b),
+  // which streamed W 0.2-0.65 us faster per call at batches 1-128 (row-major
+  // W, and the 256-row tile of batches 129-256: the XCD-major order, 0.03-0.45
+  // and about 0.3 us faster).
   int tm, tn;
   {
     const int G = gridDim.x, bid = blockIdx.x, per = G >> 3;
-    const int nb = p.grid_m == 1 && p.w_packed ? bid
-                   : bid < (per << 3)          ? (bid & 7) * per + (bid >> 3)
-                                               : bid;
+    const int nb = T::BM <= 128 && p.grid_m == 1 && p.w_packed ? bid
+                   : bid < (per << 3)                          ? (bid & 7) * per + (bid >> 3)
+                                                               : bid;
     constexpr int GROUP_M = kTileGroup;
     const int in_group = GROUP_M * p.grid_n;
     const int group = (int)div_exact((uint32_t)nb, p.div_group);  // nb / in_group

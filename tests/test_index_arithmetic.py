@@ -105,11 +105,11 @@ def test_tile_packed_w_addresses():
 K_TILE_GROUP = 8  # row tiles walked per vocabulary tile
 
 
-def tile_of(bid, G, grid_m, grid_n, w_packed):
+def tile_of(bid, G, grid_m, grid_n, w_packed, bm=128):
     """The tile kernel's map from workgroup id to (row tile, vocabulary tile),
-    with its multiply-high divisions."""
+    with its multiply-high divisions (bm: rows per tile)."""
     per = G >> 3
-    if grid_m == 1 and w_packed:
+    if bm <= 128 and grid_m == 1 and w_packed:
         nb = bid
     elif bid < (per << 3):
         nb = (bid & 7) * per + (bid >> 3)
@@ -133,7 +133,7 @@ def test_tile_map_is_a_bijection():
     for grid_m in (1, 2, 3, 7, 8, 9, 16, 17):
         for grid_n in grid_ns:
             G = grid_m * grid_n
-            for w_packed in (False, True):
-                tiles = {tile_of(b, G, grid_m, grid_n, w_packed) for b in range(G)}
-                assert len(tiles) == G, (grid_m, grid_n, w_packed)
+            for w_packed, bm in ((False, 128), (True, 128), (True, 256)):
+                tiles = {tile_of(b, G, grid_m, grid_n, w_packed, bm) for b in range(G)}
+                assert len(tiles) == G, (grid_m, grid_n, w_packed, bm)
                 assert all(0 <= tm < grid_m and 0 <= tn < grid_n for tm, tn in tiles)
