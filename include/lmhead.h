@@ -257,14 +257,16 @@ lmhead_status lmhead_self_check(int mode, const void *x, const void *w, int64_t 
  * A weight is packed once and then read by every call; packing changes where
  * each byte sits, not any value or the order of any sum.  W is cut into blocks
  * of 128 rows x 128 bytes; each block is stored row by row (16 KB, contiguous),
- * the blocks of a group of 128 rows one after another in k order, and the
- * groups in order.  With R = 2 H bytes per row, byte k of vocabulary row v is
- * at byte
- *     (v / 128) * 128 R + (k / 128) * 16384 + (v % 128) * 128 + k % 128
+ * the blocks of a group of 128 rows one after another in k order followed by
+ * one unused 16 KB block (zeros), and the groups in order.  With R = 2 H bytes
+ * per row, byte k of vocabulary row v is at byte
+ *     (v / 128) * (128 R + 16384) + (k / 128) * 16384 + (v % 128) * 128 + k % 128
  * (integer division), so the contraction's pipeline stages read contiguous
- * blocks.  The layout has ceil(V / 128) * 128 rows; the rows from V on are
- * zero.  (The pages fix the arithmetic, not the storage of the weight; this
- * layout is this library's own.)
+ * blocks, and the unused block keeps the groups from all starting at one
+ * offset modulo a large power of two.  The layout has ceil(V / 128) groups,
+ * ceil(V / 128) * (128 R + 16384) bytes; the rows from V on are zero.  (The
+ * pages fix the arithmetic, not the storage of the weight; this layout is
+ * this library's own.)
  *   lmhead_packed_w_bytes  its size in bytes (0 if H or V is not valid);
  *   lmhead_pack_w          writes it from row-major bf16 w [V, H] into
  *                          `packed` (device, 16-byte aligned, at least

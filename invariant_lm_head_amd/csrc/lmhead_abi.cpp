@@ -326,8 +326,8 @@ size_t lmhead_packed_w_bytes(int64_t H, int64_t V) {
   static const char dummy[16] __attribute__((aligned(16))) = {0};
   if (check_common(LMHEAD_MODE_BF16_PACKED, LMHEAD_ROUND_F32, dummy, dummy, 1, H, V) != LMHEAD_OK)
     return 0;
-  return (size_t)((V + lmh::kPackRows - 1) / lmh::kPackRows) * lmh::kPackRows *
-         (size_t)row_bytes(LMHEAD_MODE_BF16_PACKED, H);
+  return (size_t)((V + lmh::kPackRows - 1) / lmh::kPackRows) *
+         (size_t)lmh::packed_group_bytes(row_bytes(LMHEAD_MODE_BF16_PACKED, H));
 }
 
 lmhead_status lmhead_pack_w(const void *w, int64_t H, int64_t V, void *packed, void *stream) {

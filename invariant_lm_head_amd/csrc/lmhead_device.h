@@ -1049,8 +1049,10 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   // ---- per-lane 32-bit source offset (from the tile's first row) of each 1 KB
   // LDS span this wave fills every stage; rows past B / V re-read the last row
   // (their results are masked in the epilogue)
+  const bool wpk = MODE == 0 && p.w_packed;  // W in the packed layout (float head)
   const char *xtile = p.x + (int64_t)m0 * p.rowbytes;
-  const char *wtile = p.w + (int64_t)n0 * p.rowbytes;
+  const char *wtile =
+      p.w + (wpk ? (int64_t)(n0 / kPackRows) * packed_group_bytes(p.rowbytes) : (int64_t)n0 * p.rowbytes);
   // stage t holds bytes [koff(t), koff(t) + BKB) of every row: the k order of
   // this tile's columns (a tile never straddles a rotation group, and the
   // rotation is a whole number of stages)
@@ -1076,14 +1078,12 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   // their packed offsets; tiles start on a row group (BN is a multiple of 128)
   static_assert(T::BN % kPackRows == 0, "tiles start on a packed row group");
   static_assert(T::BKB % kPackBytes == 0 || kPackBytes % T::BKB == 0, "stages and blocks nest");
-  const bool wpk = MODE == 0 && p.w_packed;
-  constexpr int kBlock = kPackRows * kPackBytes;
   auto span_offset_packed = [&](int span, int first, int last) -> unsigned {
     const int off = span * 1024 + lane * 16;
     const int row = min(first + off / T::BKB, last) - first;
     const int kb = 16 * (((off % T::BKB) >> 4) ^ swz<T::BKB>(off / T::BKB));
-    return (unsigned)(row / kPackRows) * (unsigned)(kPackRows * p.rowbytes) +
-           (unsigned)((kb / kPackBytes) * kBlock + (row % kPackRows) * kPackBytes + kb % kPackBytes);
+    return (unsigned)(row / kPackRows) * (unsigned)packed_group_bytes(p.rowbytes) +
+           (unsigned)((kb / kPackBytes) * kPackBlock + (row % kPackRows) * kPackBytes + kb % kPackBytes);
   };
 #pragma unroll
   for (int i = 0; i < T::SPWW_MAX; ++i) {
@@ -1093,7 +1093,7 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
   // W source of stage t: the stage's first byte of the tile's first row
   auto wkoff = [&](int stage) -> int64_t {
     const int64_t o = koff(stage);
-    return wpk ? (o / kPackBytes) * kBlock + o % kPackBytes : o;
+    return wpk ? (o / kPackBytes) * kPackBlock + o % kPackBytes : o;
   };
   const unsigned lds0 = lds_addr(smem);
   auto issue_x = [&](int stage, int buf) {

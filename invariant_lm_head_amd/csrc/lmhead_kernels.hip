@@ -90,19 +90,19 @@ __global__ void compare_words_kernel(const unsigned *a, const unsigned *b, int64
 
 // Row-major bf16 W [V, H] to the packed layout (w_packed_offset): one
 // 16-byte piece of the output per thread and step, read from its row; rows
-// from V to the end of the last group are written as zeros.
+// from V to the end of the last group and each group's unused block are
+// written as zeros.
 __global__ __launch_bounds__(256) void pack_w_kernel(const char *w, char *out, int64_t V,
                                                      int64_t rowbytes, int64_t n16) {
-  constexpr int64_t kBlock = kPackRows * kPackBytes;  // bytes of one block
-  const int64_t group = kPackRows * rowbytes;
+  const int64_t group = packed_group_bytes(rowbytes), data = kPackRows * rowbytes;
   for (int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; u < n16;
        u += (int64_t)gridDim.x * blockDim.x) {
     const int64_t o = 16 * u;
     const int64_t g = o / group, rem = o % group;
-    const int64_t c = rem / kBlock, in = rem % kBlock;
+    const int64_t c = rem / kPackBlock, in = rem % kPackBlock;
     const int64_t v = g * kPackRows + in / kPackBytes, k = c * kPackBytes + in % kPackBytes;
     uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (v < V) val = *(const uint4 *)(w + v * rowbytes + k);
+    if (rem < data && v < V) val = *(const uint4 *)(w + v * rowbytes + k);
     *(uint4 *)(out + o) = val;
   }
 }
@@ -232,7 +232,7 @@ hipError_t launch_compare(const void *a, const void *b, int64_t nwords,
 }
 
 hipError_t launch_pack_w(const void *w, void *out, int64_t V, int64_t rowbytes, hipStream_t s) {
-  const int64_t n16 = (V + kPackRows - 1) / kPackRows * kPackRows * rowbytes / 16;
+  const int64_t n16 = (V + kPackRows - 1) / kPackRows * packed_group_bytes(rowbytes) / 16;
   int64_t blocks = (n16 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(pack_w_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const char *)w,

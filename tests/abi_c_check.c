@@ -18,7 +18,7 @@
 int main(void) {
   const void *a = (const void *)(uintptr_t)0x10000; /* aligned, never dereferenced */
   void *out = (void *)(uintptr_t)0x20000;
-  CHECK(lmhead_packed_w_bytes(2048, 32000) == (size_t)250 * 128 * 4096);
+  CHECK(lmhead_packed_w_bytes(2048, 32000) == (size_t)250 * (128 * 4096 + 16384));
   CHECK(lmhead_packed_w_bytes(100, 32000) == 0);
   CHECK(lmhead_workspace_bytes(LMHEAD_MODE_BF16, 512, 2048, 32000) ==
         lmhead_workspace_bytes(LMHEAD_MODE_BF16_PACKED, 512, 2048, 32000));

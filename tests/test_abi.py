@@ -203,11 +203,11 @@ def test_sample_validation(lib):
 
 
 def test_packed_w_layout_size_and_validation(lib):
-    """lmhead_packed_w_bytes: ceil(V / 128) groups of 128 rows of 2H bytes; no
-    int8 bound on H (a bf16 layout).  lmhead_pack_w refuses what the other calls
-    refuse, before anything is queued."""
+    """lmhead_packed_w_bytes: ceil(V / 128) groups of 128 rows of 2H bytes and
+    one unused 16 KB block; no int8 bound on H (a bf16 layout).  lmhead_pack_w
+    refuses what the other calls refuse, before anything is queued."""
     for H, V in [(2048, 32000), (64, 2), (64, 129), (4096, 151936), (131072, 1000)]:
-        assert lib.lmhead_packed_w_bytes(H, V) == (V + 127) // 128 * 128 * 2 * H, (H, V)
+        assert lib.lmhead_packed_w_bytes(H, V) == (V + 127) // 128 * (128 * 2 * H + 16384), (H, V)
     for H, V in [(100, 1000), (0, 1000), (64, 1), (64, (1 << 30) + 1), ((1 << 20) + 64, 10)]:
         assert lib.lmhead_packed_w_bytes(H, V) == 0, (H, V)
 

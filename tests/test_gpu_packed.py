@@ -22,17 +22,18 @@ pytestmark = pytest.mark.gpu
 
 
 def packed_reference(wb: np.ndarray) -> np.ndarray:
-    """The header's formula: byte k of row v at (v / 128) 128 R + (k / 128)
-    16384 + (v % 128) 128 + k % 128, R = 2H; rows from V to the end of the last
-    group of 128 are zero."""
+    """The header's formula: byte k of row v at (v / 128) (128 R + 16384) +
+    (k / 128) 16384 + (v % 128) 128 + k % 128, R = 2H; rows from V to the end
+    of the last group of 128 and each group's unused last block are zero."""
     V, H = wb.shape
     R = 2 * H
     C = 128
+    group = 128 * R + 128 * C
     src = np.ascontiguousarray(wb, dtype=np.uint16).view(np.uint8).reshape(V, R)
-    out = np.zeros((V + 127) // 128 * 128 * R, dtype=np.uint8)
+    out = np.zeros((V + 127) // 128 * group, dtype=np.uint8)
     v = np.arange(V, dtype=np.int64)[:, None]
     k = np.arange(R, dtype=np.int64)[None, :]
-    off = (v // 128) * 128 * R + (k // C) * 128 * C + (v % 128) * C + k % C
+    off = (v // 128) * group + (k // C) * 128 * C + (v % 128) * C + k % C
     out[off] = src
     return out
 

@@ -69,7 +69,12 @@ def swz(bkb, row):
 
 def packed_offset(v, k, R):
     """The header's formula for byte k of row v in the packed layout."""
-    return (v // 128) * 128 * R + (k // 128) * 16384 + (v % 128) * 128 + k % 128
+    return (v // 128) * (128 * R + 16384) + (k // 128) * 16384 + (v % 128) * 128 + k % 128
+
+
+def packed_bytes(V, R):
+    """The header's size of the packed layout."""
+    return (V + 127) // 128 * (128 * R + 16384)
 
 
 def test_tile_packed_w_addresses():
@@ -90,15 +95,16 @@ def test_tile_packed_w_addresses():
                             off = span * 1024 + lane * 16
                             row = min(n0 + off // BKB, V - 1) - n0
                             kb = 16 * (((off % BKB) >> 4) ^ swz(BKB, off // BKB))
-                            woff = (row // 128) * (128 * R) + ((kb // 128) * 16384 +
-                                                               (row % 128) * 128 + kb % 128)
+                            woff = (row // 128) * (128 * R + 16384) + (
+                                (kb // 128) * 16384 + (row % 128) * 128 + kb % 128)
                             assert woff < 2 ** 32
                             for s in range(nst):
                                 o = s * BKB
                                 wk = (o // 128) * 16384 + o % 128
-                                got = n0 * R + wk + woff
+                                got = (n0 // 128) * (128 * R + 16384) + wk + woff
                                 assert got == packed_offset(n0 + row, o + kb, R), \
                                     (R, BN, BKB, n0, span, lane, s)
+                                assert got + 16 <= packed_bytes(V, R)
 
 
 # ------------------------------------------------- workgroup -> tile mapping
