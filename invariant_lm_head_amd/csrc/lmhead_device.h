@@ -1396,37 +1396,62 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
 #pragma unroll
           for (int b = 0; b < T::BPW; ++b) {
             const int col0 = wcol0 + b * T::NTB * 32 + j;  // this lane's first column of the block
-            if (p.B - m0 == 1) {
-              // one live row in the tile (batch 1, or a last row tile of one
-              // row): its row 0, value 0 of the lanes with h = 0 in the first
-              // 32-row tile of wave row 0.  Only that row is ranked, by a
-              // butterfly over the 32 column lanes; the pairings j^16, j^15,
-              // j^7, j^2, j^1 are independent bit masks, so every lane ends
-              // with the exact top-2 of all 32 (the same keys the
-              // reduce-scatter below would merge)
-              if (wm == 0 && mt == 0) {
-                val_t z[T::NTB];
+            if (p.B - m0 <= 8) {
+              // at most 8 live rows in the tile (batches 1-8, or a last row
+              // tile that short): rows 0-7, row 4 h + v in values v = 0..3 of
+              // the first 32-row tile of wave row 0 (one row: value 0 of the
+              // lanes with h = 0).  Only those values are ranked.  Four
+              // values: two halving steps (j^16, then j^15) leave lane j value
+              // u = 2 b4 + b3, and full merges on j^7, j^2, j^1, which keep
+              // bits 4 and 3, finish it; one value: full merges on all five
+              // pairings.  The five masks are independent, so each lane merges
+              // every other lane once: the records are the ones the
+              // reduce-scatter below would write (a set's top-2 is unique).
+              auto rank_rows = [&](auto nv_) {
+                constexpr int NV = decltype(nv_)::value;
+                Top2 a[NV];
 #pragma unroll
-                for (int k = 0; k < T::NTB; ++k) {
-                  val_t zz = acc[mt][b * T::NTB + k][0];
-                  if constexpr (MODE == 0 && decltype(round)::value) zz = bf16_round(zz);
-                  z[k] = col0 + 32 * k < p.V ? zz : lowest_of<val_t>();
+                for (int v = 0; v < NV; ++v) {
+                  val_t z[T::NTB];
+#pragma unroll
+                  for (int k = 0; k < T::NTB; ++k) {
+                    val_t zz = acc[mt][b * T::NTB + k][v];
+                    if constexpr (MODE == 0 && decltype(round)::value) zz = bf16_round(zz);
+                    z[k] = col0 + 32 * k < p.V ? zz : lowest_of<val_t>();
+                  }
+                  a[v] = lane_top2<T::NTB>(z, ~(unsigned)col0);
                 }
-                Top2 r = lane_top2<T::NTB>(z, ~(unsigned)col0);
-                r = combine(r, perm<kX16>(r));
-                r = combine(r, perm<kMirror>(r));
-                r = combine(r, perm<kHalfMirror>(r));
+                if constexpr (NV == 4) {
+                  const bool lo16 = (j & 16) == 0;
+#pragma unroll
+                  for (int i = 0; i < 2; ++i) {
+                    const Top2 send = pick(lo16, a[i + 2], a[i]);
+                    a[i] = combine(pick(lo16, a[i], a[i + 2]), perm<kX16>(send));
+                  }
+                  const bool lo8 = (j & 8) == 0;
+                  a[0] = combine(pick(lo8, a[0], a[1]), perm<kMirror>(pick(lo8, a[1], a[0])));
+                } else {
+                  a[0] = combine(a[0], perm<kX16>(a[0]));
+                  a[0] = combine(a[0], perm<kMirror>(a[0]));
+                }
+                Top2 r = combine(a[0], perm<kHalfMirror>(a[0]));
                 r = combine(r, perm<kQuadX2>(r));
                 r = combine(r, perm<kQuadX1>(r));
-                if (lane == 0) {
+                const int lr = NV == 4 ? 4 * h + 2 * ((j >> 4) & 1) + ((j >> 3) & 1) : 0;
+                const bool writer = NV == 4 ? (j & 7) == 0 : lane == 0;
+                if (writer && m0 + lr < p.B) {
                   if constexpr (T::PARTS == 1) {
                     const int blk = wcol0 / kBlockCols + b;
                     if (blk < p.nblocks)
-                      put_record(&p.records[(int64_t)m0 * p.nblocks + blk], t2_pack(r));
+                      put_record(&p.records[(int64_t)(m0 + lr) * p.nblocks + blk], t2_pack(r));
                   } else {
-                    xch[wn] = t2_pack(r);  // row 0 of the exchange
+                    xch[lr * T::WAVES_N + wn] = t2_pack(r);
                   }
                 }
+              };
+              if (wm == 0 && mt == 0) {
+                if (p.B - m0 == 1) rank_rows(std::integral_constant<int, 1>{});
+                else rank_rows(std::integral_constant<int, 4>{});
               }
               continue;
             }
