@@ -1396,20 +1396,21 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
 #pragma unroll
           for (int b = 0; b < T::BPW; ++b) {
             const int col0 = wcol0 + b * T::NTB * 32 + j;  // this lane's first column of the block
-            if (p.B - m0 <= 8) {
-              // at most 8 live rows in the tile (batches 1-8, or a last row
-              // tile that short): rows 0-7, row 4 h + v in values v = 0..3 of
-              // the first 32-row tile of wave row 0 (one row: value 0 of the
-              // lanes with h = 0).  Only those values are ranked.  Four
-              // values: two halving steps (j^16, then j^15) leave lane j value
-              // u = 2 b4 + b3, and full merges on j^7, j^2, j^1, which keep
-              // bits 4 and 3, finish it; one value: full merges on all five
-              // pairings.  The five masks are independent, so each lane merges
-              // every other lane once: the records are the ones the
-              // reduce-scatter below would write (a set's top-2 is unique).
+            if (p.B - m0 <= 16) {
+              // at most 16 live rows in the tile (batches 1-16, or a last row
+              // tile that short): rows 0-15 sit in values v = 0..7 of the first
+              // 32-row tile of wave row 0 (row acc_row(v, h)); rows 0-7 in
+              // values 0-3, row 0 in value 0 of the lanes with h = 0.  Only the
+              // NV values that hold live rows are ranked: the reduce-scatter's
+              // halving steps over NV values (j^16, j^15, j^7 in turn; each
+              // keeps the bits the earlier ones used), then full merges on the
+              // remaining pairings.  The five masks are independent, so each
+              // lane merges every other lane once, and a set's top-2 is
+              // unique: the records are the ones the full reduce-scatter below
+              // writes.
               auto rank_rows = [&](auto nv_) {
                 constexpr int NV = decltype(nv_)::value;
-                Top2 a[NV];
+                Top2 a[16];
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
                   val_t z[T::NTB];
@@ -1421,24 +1422,20 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
                   }
                   a[v] = lane_top2<T::NTB>(z, ~(unsigned)col0);
                 }
-                if constexpr (NV == 4) {
-                  const bool lo16 = (j & 16) == 0;
-#pragma unroll
-                  for (int i = 0; i < 2; ++i) {
-                    const Top2 send = pick(lo16, a[i + 2], a[i]);
-                    a[i] = combine(pick(lo16, a[i], a[i + 2]), perm<kX16>(send));
-                  }
-                  const bool lo8 = (j & 8) == 0;
-                  a[0] = combine(pick(lo8, a[0], a[1]), perm<kMirror>(pick(lo8, a[1], a[0])));
-                } else {
-                  a[0] = combine(a[0], perm<kX16>(a[0]));
-                  a[0] = combine(a[0], perm<kMirror>(a[0]));
-                }
-                Top2 r = combine(a[0], perm<kHalfMirror>(a[0]));
-                r = combine(r, perm<kQuadX2>(r));
+                if constexpr (NV >= 4) rs_step<kX16, NV>(a, j);
+                else a[0] = combine(a[0], perm<kX16>(a[0]));
+                if constexpr (NV >= 4) rs_step<kMirror, NV / 2>(a, j);
+                else a[0] = combine(a[0], perm<kMirror>(a[0]));
+                if constexpr (NV >= 8) rs_step<kHalfMirror, NV / 4>(a, j);
+                else a[0] = combine(a[0], perm<kHalfMirror>(a[0]));
+                Top2 r = combine(a[0], perm<kQuadX2>(a[0]));
                 r = combine(r, perm<kQuadX1>(r));
-                const int lr = NV == 4 ? 4 * h + 2 * ((j >> 4) & 1) + ((j >> 3) & 1) : 0;
-                const bool writer = NV == 4 ? (j & 7) == 0 : lane == 0;
+                // the value this lane ends with, and one writer per row
+                const int u = NV == 8 ? 4 * ((j >> 4) & 1) + 2 * ((j >> 3) & 1) + ((j >> 2) & 1)
+                              : NV == 4 ? 2 * ((j >> 4) & 1) + ((j >> 3) & 1)
+                                        : 0;
+                const int lr = acc_row(u, h);
+                const bool writer = (j & (32 / NV - 1)) == 0 && (NV > 1 || h == 0);
                 if (writer && m0 + lr < p.B) {
                   if constexpr (T::PARTS == 1) {
                     const int blk = wcol0 / kBlockCols + b;
@@ -1451,7 +1448,8 @@ __global__ __launch_bounds__(T::NT) void lmhead_tile_kernel(Params p) {
               };
               if (wm == 0 && mt == 0) {
                 if (p.B - m0 == 1) rank_rows(std::integral_constant<int, 1>{});
-                else rank_rows(std::integral_constant<int, 4>{});
+                else if (p.B - m0 <= 8) rank_rows(std::integral_constant<int, 4>{});
+                else rank_rows(std::integral_constant<int, 8>{});
               }
               continue;
             }

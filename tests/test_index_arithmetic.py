@@ -143,3 +143,66 @@ def test_tile_map_is_a_bijection():
                 tiles = {tile_of(b, G, grid_m, grid_n, w_packed, bm) for b in range(G)}
                 assert len(tiles) == G, (grid_m, grid_n, w_packed, bm)
                 assert all(0 <= tm < grid_m and 0 <= tn < grid_n for tm, tn in tiles)
+
+
+# ------------------------------------- top-2 of a tile with few live rows
+# Lane pairings of the 32 column lanes of a wave half (ds_swizzle and DPP row
+# permutations) and the lane bit each halving step keeps.
+PAIR = {"x16": 16, "mirror": 15, "half_mirror": 7, "quad2": 2, "quad1": 1}
+KEEP = {"x16": 16, "mirror": 8, "half_mirror": 4}
+
+
+def _merge(a, b):
+    s = sorted(set(a) | set(b), reverse=True)
+    return (s[0], s[1])
+
+
+def _halve(a, p, r):
+    out = [list(x) for x in a]
+    for j in range(32):
+        q = j ^ PAIR[p]
+        lo, qlo = (j & KEEP[p]) == 0, (q & KEEP[p]) == 0
+        for i in range(r // 2):
+            mine = a[j][i] if lo else a[j][i + r // 2]
+            theirs = a[q][i + r // 2] if qlo else a[q][i]
+            out[j][i] = _merge(mine, theirs)
+    return out
+
+
+def _full(a, p):
+    return [[_merge(a[j][0], a[j ^ PAIR[p]][0])] + a[j][1:] for j in range(32)]
+
+
+def acc_row(v, h):
+    return 8 * (v >> 2) + 4 * h + (v & 3)
+
+
+def test_few_live_rows_top2_lane_steps():
+    """The top-2 epilogue of a tile with at most 16 live rows ranks NV = 1, 4
+    or 8 accumulator values per lane: halving steps on j^16, j^15, j^7 (as
+    many as NV needs), full merges on the rest of j^16, j^15, j^7, j^2, j^1.
+    Emulated on random distinct keys: each writer lane (one per live row)
+    must hold the brute-force top-2 of its row over all 32 column lanes, and
+    the writers must cover exactly the rows of those values."""
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        for nv in (1, 4, 8):
+            for h in (0, 1):
+                keys = rng.choice(10 ** 9, size=(32, 16, 2), replace=False)
+                a = [[tuple(sorted(map(int, keys[j, v]), reverse=True)) for v in range(16)]
+                     for j in range(32)]
+                steps = ["x16", "mirror", "half_mirror"]
+                halvings = {1: 0, 4: 2, 8: 3}[nv]
+                for s, p in enumerate(steps):
+                    a = _halve(a, p, nv >> s) if s < halvings else _full(a, p)
+                a = _full(_full(a, "quad2"), "quad1")
+                rows = {}
+                for j in range(32):
+                    u = ((4 * ((j >> 4) & 1) + 2 * ((j >> 3) & 1) + ((j >> 2) & 1)) if nv == 8
+                         else (2 * ((j >> 4) & 1) + ((j >> 3) & 1)) if nv == 4 else 0)
+                    if (j & (32 // nv - 1)) == 0 and (nv > 1 or h == 0):
+                        want = sorted({int(k) for k in keys[:, u].ravel()}, reverse=True)[:2]
+                        assert a[j][0] == tuple(want), (trial, nv, h, j)
+                        rows[acc_row(u, h)] = j
+                expect = {acc_row(v, h) for v in range(nv)} if (nv > 1 or h == 0) else set()
+                assert set(rows) == expect, (nv, h)
