@@ -784,6 +784,10 @@ def render_tables(results: Path) -> dict:
     if "logits_batches_1_to_512" in inv:
         rows.append(f"| bitwise invariance: logits, top-2, log-prob at every batch 1..512 | "
                     f"{inv['logits_batches_1_to_512']['rows_compared']} rows x 32000 logits | identical |")
+    if "int8_greedy_batches_1_to_512_vs_oracle" in inv:
+        rows.append(f"| int8 greedy at every batch 1..512 against the oracle's stored rows | "
+                    f"{inv['int8_greedy_batches_1_to_512_vs_oracle']['rows_compared']} rows | "
+                    f"bit-exact |")
     if "packed_greedy_batches_1_to_512" in inv:
         rows.append(f"| bitwise invariance, packed W: top-2 at every batch 1..512 against the "
                     f"row-major batch-512 call, both rankings | "

@@ -113,3 +113,19 @@ def test_int8_logit_hash_identical_across_batches(i8):
     assert digests(lmhead.logits(x[:1].contiguous(), w)) == ref[:1]
     assert digests(lmhead.logits(x[:64].contiguous(), w))[:8] == ref
     assert digests(lmhead.logits(x[:8].flip(0).contiguous(), w))[::-1] == ref
+
+
+def test_int8_greedy_every_batch_size_against_oracle(i8):
+    """The int8 head at every batch 1..512 (every plan, every short last row
+    tile): ids, exact raw values, scaled values and margins bit for bit equal
+    to the oracle's stored outputs for those rows."""
+    g = i8["golden"]
+    for B in range(1, 513):
+        ids, vals, margin, raw = lmhead.greedy_top2(i8["gx"][:B].contiguous(), i8["gw"],
+                                                    row_scale=i8["gs"][:B].contiguous())
+        assert np.array_equal(host(ids), g["ids"][:B]), B
+        assert np.array_equal(host(raw).astype(np.int64), g["raw"][:B]), B
+        assert np.array_equal(host(vals).view(np.int32), g["vals"][:B].view(np.int32)), B
+        assert np.array_equal(host(margin).view(np.int32), g["margin"][:B].view(np.int32)), B
+    record("invariance", "int8_greedy_batches_1_to_512_vs_oracle",
+           {"batches": 512, "rows_compared": 512 * 513 // 2})
