@@ -1,7 +1,8 @@
 """The entry point that allocates nothing (lmhead_greedy_top2_noalloc, through
 the C-ABI) against lmhead_greedy_top2 with a caller workspace: bitwise equal
-outputs on two calls in a row, the second with a smaller input, in both
-modes; a shape beyond the static workspace is refused."""
+outputs on two calls in a row, the second with a smaller input, in every
+mode (bf16, bf16 from packed W, int8); a shape beyond the static workspace is
+refused."""
 import ctypes
 
 import numpy as np
@@ -54,6 +55,12 @@ def test_noalloc_matches_workspace_entry_point():
         xb = x[:B].contiguous()
         got = _noalloc(lib, 0, xb, w, B, H, V, round_bf16=rnd)
         _same(got, _with_workspace(xb, w, round_bf16=bool(rnd)))
+    # the packed W layout (mode 2): batch 257 (a one-row last tile), then 3
+    pw = lmhead.pack_w(w)
+    for B in (257, 3):
+        xb = x[:B].contiguous()
+        got = _noalloc(lib, lmhead.MODE_BF16_PACKED, xb, pw.data, B, H, V)
+        _same(got, _with_workspace(xb, pw))
     # int8 head (4096 x 128256 would need 4 MB at batch 512; a smaller vocabulary
     # keeps the test short): batch 64, then 3
     rng = np.random.default_rng(31)
