@@ -271,7 +271,8 @@ lmhead_status lmhead_self_check(int mode, const void *x, const void *w, int64_t 
  *   lmhead_pack_w          writes it from row-major bf16 w [V, H] into
  *                          `packed` (device, 16-byte aligned, at least
  *                          lmhead_packed_w_bytes(H, V) bytes, not overlapping
- *                          w), asynchronously on `stream`.
+ *                          w: LMHEAD_E_VALUE if the two ranges meet),
+ *                          asynchronously on `stream`.
  * Shape rules and errors as for the other calls with B = 1. */
 size_t lmhead_packed_w_bytes(int64_t H, int64_t V);
 lmhead_status lmhead_pack_w(const void *w, int64_t H, int64_t V, void *packed, void *stream);

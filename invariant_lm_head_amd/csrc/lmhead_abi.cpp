@@ -335,6 +335,10 @@ lmhead_status lmhead_pack_w(const void *w, int64_t H, int64_t V, void *packed, v
   if (st != LMHEAD_OK) return st;
   if (!packed) return LMHEAD_E_NULL;
   if (!aligned16(packed)) return LMHEAD_E_ALIGN;
+  // the layout is written while w is read: the two ranges must not meet
+  const uintptr_t w0 = (uintptr_t)w, w1 = w0 + (uintptr_t)V * (uintptr_t)row_bytes(LMHEAD_MODE_BF16_PACKED, H);
+  const uintptr_t p0 = (uintptr_t)packed, p1 = p0 + (uintptr_t)lmhead_packed_w_bytes(H, V);
+  if (p0 < w1 && w0 < p1) return LMHEAD_E_VALUE;
   return launched(lmh::launch_pack_w(w, packed, V, row_bytes(LMHEAD_MODE_BF16_PACKED, H),
                                      (hipStream_t)stream));
 }

@@ -205,7 +205,8 @@ def test_sample_validation(lib):
 def test_packed_w_layout_size_and_validation(lib):
     """lmhead_packed_w_bytes: ceil(V / 128) groups of 128 rows of 2H bytes and
     one unused 16 KB block; no int8 bound on H (a bf16 layout).  lmhead_pack_w
-    refuses what the other calls refuse, before anything is queued."""
+    refuses what the other calls refuse, and a destination whose range meets
+    w's, before anything is queued."""
     for H, V in [(2048, 32000), (64, 2), (64, 129), (4096, 151936), (131072, 1000)]:
         assert lib.lmhead_packed_w_bytes(H, V) == (V + 127) // 128 * (128 * 2 * H + 16384), (H, V)
     for H, V in [(100, 1000), (0, 1000), (64, 1), (64, (1 << 30) + 1), ((1 << 20) + 64, 10)]:
@@ -220,6 +221,12 @@ def test_packed_w_layout_size_and_validation(lib):
     assert call(out=MIS) == E_ALIGN
     assert call(H=96) == E_SHAPE
     assert call(V=1) == E_SHAPE
+    # packing in place, or into a range that meets w's, is refused
+    w0 = 0x100000
+    nw = 1000 * 2 * 64
+    assert call(w=ctypes.c_void_p(w0), out=ctypes.c_void_p(w0)) == E_VALUE
+    assert call(w=ctypes.c_void_p(w0), out=ctypes.c_void_p(w0 + nw - 16)) == E_VALUE
+    assert call(w=ctypes.c_void_p(w0 + 16), out=ctypes.c_void_p(w0)) == E_VALUE
 
 
 def test_quantize_validation(lib):
