@@ -1793,6 +1793,7 @@ __global__ __launch_bounds__(256) void lmhead_merge_top2_kernel(Params p) {
 //   9: 128 x 256 in place of 2 when ceil(V / 256) >= 256; 10: 128 x 512 for
 //      the int8 head where 7 and 8 apply
 //   11: 1 with an unpaired W ring, for packed W
+//   12: 2 with 256-byte stages, for packed W
 template <int BKB> using V0w = Tile<32, 256, 1, 4, BKB, 2, 3>;
 template <int BKB> using V1w = Tile<64, 256, 2, 2, BKB, 2, 3>;
 // int8 head, large vocabularies: 512-column tiles with rings of equal depth
@@ -1822,6 +1823,12 @@ template <int BKB> using V1 = Tile<64, 128, 2, 2, BKB, 2, 4, true>;
 // 31.1 us unpaired).
 template <int BKB> using V1p = Tile<64, 128, 2, 2, BKB, 2, 3>;
 template <int BKB> using V2 = Tile<128, 128, 2, 2, BKB, 2, 4>;
+// V2 reading packed W (float head): 256-byte stages, so each stage reads two
+// adjacent blocks (32 KB contiguous), with a 3-deep W ring (2 x 32 KB + 3 x
+// 32 KB of LDS).  Measured on MI355X (TinyLlama head, packed W from HBM, two
+// boxes): batch 65 / 100 / 128 in 29.51 / 29.92 / 30.58 us against 29.66 /
+// 30.33 / 31.03 us, and 30.34 / 30.86 / 31.20 us against 31.36 / 31.69 / 32.10 us.
+using V2p = Tile<128, 128, 2, 2, 256, 2, 3>;
 // batches 65-128 at large vocabularies (ceil(V / 256) >= 256): 256-column
 // tiles (and 512-column ones for the int8 head where their grid fits one
 // round of the CUs) halve or quarter the X re-reads and the rounds.  Measured

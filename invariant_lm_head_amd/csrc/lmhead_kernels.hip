@@ -158,6 +158,7 @@ Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V, bool w_packed) {
     pl.variant = 9; pl.bm = V2w<128>::BM; pl.bn = V2w<128>::BN; pl.nt = V2w<128>::NT; pl.bkb = bkb128;
   } else if (B <= 128) {
     pl.variant = 2; pl.bm = V2<128>::BM; pl.bn = V2<128>::BN; pl.nt = V2<128>::NT; pl.bkb = bkb128;
+    if (mode == 0 && w_packed && rowbytes % V2p::BKB == 0) { pl.variant = 12; pl.bkb = V2p::BKB; }
   } else if (B <= 256 && (V + 255) / 256 < kCUs) {
     // 256-column tiles would leave CUs idle: 256 x 128.  Where they fill the
     // CUs (V >= 65281) the 256 x 256 tile below reads X half as often; measured

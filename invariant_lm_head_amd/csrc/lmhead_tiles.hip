@@ -82,6 +82,9 @@ hipError_t launch_epi(const Plan &plan, const Params &p, hipStream_t s) {
         return launch_tile<V1p<128>, MODE, EPI>(p, s);
       }
       return hipErrorInvalidValue;  // packed W: float head only
+    case 12:
+      if constexpr (MODE == 0) return launch_tile<V2p, MODE, EPI>(p, s);
+      return hipErrorInvalidValue;  // packed W: float head only
     case 9:
       if (plan.bkb == 128) return launch_tile<V2w<128>, MODE, EPI>(p, s);
       return launch_tile<V2w<64>, MODE, EPI>(p, s);
