@@ -1792,7 +1792,7 @@ __global__ __launch_bounds__(256) void lmhead_merge_top2_kernel(Params p) {
 //      512-column grid fits one round of the CUs
 //   9: 128 x 256 in place of 2 when ceil(V / 256) >= 256; 10: 128 x 512 for
 //      the int8 head where 7 and 8 apply
-//   11: 1 with an unpaired W ring, for packed W
+//   11: 1 with eight waves and an unpaired W ring, for packed W
 //   12: 2 with 256-byte stages, for packed W
 template <int BKB> using V0w = Tile<32, 256, 1, 4, BKB, 2, 3>;
 template <int BKB> using V1w = Tile<64, 256, 2, 2, BKB, 2, 3>;
@@ -1820,8 +1820,11 @@ template <int BKB> using V1 = Tile<64, 128, 2, 2, BKB, 2, 4, true>;
 // so the W ring is spread over the k-steps, 3 deep, unpaired.  Measured on
 // MI355X (TinyLlama head, packed W from HBM): batch 33 and 64 in 27.1 us against
 // 28.7 us with the paired ring (row-major W keeps the paired ring: 30.4 against
-// 31.1 us unpaired).
-template <int BKB> using V1p = Tile<64, 128, 2, 2, BKB, 2, 3>;
+// 31.1 us unpaired).  Eight waves of 32 x 32 (two per SIMD) rather than four
+// of 32 x 64: batch 33 / 48 / 64 in 27.07 / 26.60 / 26.36 us against 27.25 /
+// 27.67 / 27.92 us, and 26.37 / 26.30 / 26.29 us against 26.69 / 28.10 / 28.28
+// us on a second box (the 128 x 128 tile with eight waves was 1-2 us slower).
+template <int BKB> using V1p = Tile<64, 128, 2, 4, BKB, 2, 3>;
 template <int BKB> using V2 = Tile<128, 128, 2, 2, BKB, 2, 4>;
 // V2 reading packed W (float head): 256-byte stages, so each stage reads two
 // adjacent blocks (32 KB contiguous), with a 3-deep W ring (2 x 32 KB + 3 x

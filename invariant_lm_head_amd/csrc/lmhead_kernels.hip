@@ -151,14 +151,14 @@ Plan plan_for(int mode, int64_t B, int64_t rowbytes, int64_t V, bool w_packed) {
     pl.variant = 6; pl.bm = V1w<128>::BM; pl.bn = V1w<128>::BN; pl.nt = V1w<128>::NT; pl.bkb = bkb128;
   } else if (B <= 64) {
     pl.variant = 1; pl.bm = V1<256>::BM; pl.bn = V1<256>::BN; pl.nt = V1<256>::NT; pl.bkb = bkb256;
-    if (mode == 0 && w_packed) pl.variant = 11;  // same tile, W ring unpaired
+    if (mode == 0 && w_packed) { pl.variant = 11; pl.nt = V1p<256>::NT; }  // same tile, 8 waves, W ring unpaired
   } else if (B <= 128 && wide512) {
     pl.variant = 10; pl.bm = V2x<128>::BM; pl.bn = V2x<128>::BN; pl.nt = V2x<128>::NT; pl.bkb = bkb128;
   } else if (B <= 128 && (V + 255) / 256 >= kCUs) {
     pl.variant = 9; pl.bm = V2w<128>::BM; pl.bn = V2w<128>::BN; pl.nt = V2w<128>::NT; pl.bkb = bkb128;
   } else if (B <= 128) {
     pl.variant = 2; pl.bm = V2<128>::BM; pl.bn = V2<128>::BN; pl.nt = V2<128>::NT; pl.bkb = bkb128;
-    if (mode == 0 && w_packed && rowbytes % V2p::BKB == 0) { pl.variant = 12; pl.bkb = V2p::BKB; }
+    if (mode == 0 && w_packed && rowbytes % V2p::BKB == 0) { pl.variant = 12; pl.nt = V2p::NT; pl.bkb = V2p::BKB; }
   } else if (B <= 256 && (V + 255) / 256 < kCUs) {
     // 256-column tiles would leave CUs idle: 256 x 128.  Where they fill the
     // CUs (V >= 65281) the 256 x 256 tile below reads X half as often; measured
