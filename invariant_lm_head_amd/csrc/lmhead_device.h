@@ -1815,7 +1815,10 @@ using V0d = Tile<32, 128, 1, 4, 512, 2, 2>;
 // Measured on MI355X (TinyLlama head, W from HBM): batch 33 and 64 in 33.1-33.8
 // us against 34.2-35.0 us with a 3-deep spread W ring; the same pairing in
 // V3 was 4.5 us slower at batch 256 (its loads are limited by issue, not HBM).
-template <int BKB> using V1 = Tile<64, 128, 2, 2, BKB, 2, 4, true>;
+// Eight waves of 32 x 32 (two per SIMD) rather than four of 32 x 64: batch
+// 33 / 48 / 64 in 29.64 / 29.58 / 29.66 us against 30.06 / 30.11 / 29.95 us,
+// and 30.38 / 30.49 / 30.43 us against 30.49 / 30.64 / 30.51 us on a second box.
+template <int BKB> using V1 = Tile<64, 128, 2, 4, BKB, 2, 4, true>;
 // V1 reading packed W (float head): every stage is already a contiguous block,
 // so the W ring is spread over the k-steps, 3 deep, unpaired.  Measured on
 // MI355X (TinyLlama head, packed W from HBM): batch 33 and 64 in 27.1 us against
